@@ -1,0 +1,192 @@
+/*
+ * ss1.h -- C ABI of the SS1 (Sketch Structured Transform) forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (source: "SS1: Accelerating Inference with Fast and Expressive
+ * Sketch Structured Transform", summary page, section "Approach"; and the SS1
+ * author abstract): a linear layer whose neurons share parameters randomly but
+ * only inside their own weight vector, through hash functions coalesced along
+ * K and along N.  The layer first sketches its input down by the compression
+ * factor c using additions and subtractions only, then multiplies the sketch
+ * by the compressed weight W_c, so it does c times fewer FLOPs than the dense
+ * layer it replaces.
+ *
+ * Concretely (readings of the page's wording, fixed here):
+ *   J  = K / BK input chunks of BK consecutive inputs, Jc = J / c, Kc = K / c,
+ *   G  = N / BN neuron groups of BN consecutive neurons (n belongs to n / BN).
+ *   Plan of group g: hash[g][j] in [0, Jc) and sign[g][j] in {-1, +1}; it is
+ *   balanced: every compressed chunk t receives exactly c input chunks.
+ *   Sketch:  z_g[m][t*BK + u] = sum over j with hash[g][j] == t of
+ *                               sign[g][j] * x[m][j*BK + u]
+ *   Output:  y[m][n] = sum over k' < Kc of z_{n/BN}[m][k'] * W_c[n][k']
+ *
+ * Layouts: every matrix is dense row-major with rows packed (row stride =
+ * cols).  x is [M][K], W_c is [N][Kc] (one row per neuron, like a dense
+ * layer's [out][in] weight), y is [M][N].  hash/sign are [G][J]; the inverse
+ * index idx/isign is [G][Jc][c].
+ *
+ * Precision: float32 layers compute the sketch and the contraction in float32
+ * (fused multiply-add, no reduced-precision matrix format).  bf16 layers sum
+ * each sketch value in float32 over its sources in ascending chunk order,
+ * round it to bf16 (nearest, ties to even), contract on bf16 matrix cores with
+ * float32 accumulation, and round y to bf16 (nearest, ties to even).
+ *
+ * Ownership and threading: the caller owns every buffer.  The device entry
+ * points do not allocate, free or cache anything and keep no global state;
+ * they enqueue work on the caller's HIP stream and return without waiting.
+ * They are safe to call from several threads at once.
+ *
+ * Errors: every call returns an ss1_status.  All argument checks (null
+ * pointers, shapes, dtypes, alignment) happen on the host before any HIP call,
+ * so a failing check enqueues nothing.  A failed launch returns SS1_ERR_HIP;
+ * faults during execution surface at the caller's next synchronisation.
+ */
+#ifndef SS1_H
+#define SS1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SS1_OK = 0,
+    SS1_ERR_NULL = 1,      /* a required pointer is NULL                          */
+    SS1_ERR_SHAPE = 2,     /* sizes inconsistent, non-dividing or out of range   */
+    SS1_ERR_DTYPE = 3,     /* unknown dtype, or x / W_c / y dtypes differ         */
+    SS1_ERR_PLAN = 4,      /* host plan arrays fail validation (range, sign, balance) */
+    SS1_ERR_ALIGN = 5,     /* a device pointer is not aligned as documented       */
+    SS1_ERR_HIP = 6,       /* a HIP launch or runtime call failed                 */
+    SS1_ERR_ALGO = 7       /* the requested kernel cannot run this shape          */
+} ss1_status;
+
+typedef enum { SS1_F32 = 0, SS1_BF16 = 1 } ss1_dtype;
+
+/* Kernel choice for ss1_forward_algo / ss1_forward_idx_algo. */
+typedef enum {
+    SS1_ALGO_AUTO = 0,     /* what ss1_forward picks                                  */
+    SS1_ALGO_FUSED = 1,    /* bf16: sketch tile built in LDS, then MFMA (M of any size) */
+    SS1_ALGO_SMALLM = 2,   /* bf16: decode shapes, M <= 16, W_c streamed once          */
+    SS1_ALGO_GENERIC = 3   /* any dtype and chunking: LDS-tiled FMA kernel             */
+} ss1_algo;
+
+/* A dense row-major matrix in device memory (rows packed). */
+typedef struct {
+    void* data;
+    int32_t dtype;         /* ss1_dtype */
+    int32_t reserved;      /* must be 0 */
+    int64_t rows;
+    int64_t cols;
+} ss1_tensor;
+
+/* Largest number of input chunks J = K/BK per group the device kernels take
+   (their plan is staged in LDS). */
+#define SS1_MAX_CHUNKS 4096
+/* Largest compression factor. */
+#define SS1_MAX_C 64
+
+/* Library version, "major.minor.patch". */
+const char* ss1_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* ss1_status_string(ss1_status s);
+
+/*
+ * ss1_plan -- HOST.  Seeded balanced chunk hash and +-1 signs for every group
+ * (the random, within-neuron, K- and N-coalesced parameter sharing of the SS1
+ * summary page, "Approach"; the generator itself is this library's choice):
+ *   SplitMix64 (Steele, Lea, Flood 2014) seeded with `seed`; for g = 0..G-1 in
+ *   order: Fisher-Yates shuffle of [0, J) (i from J-1 down to 1, swap i with
+ *   next() % (i+1)); the chunk at shuffled position p gets hash p / c; then one
+ *   draw per chunk j = 0..J-1, sign = -1 when its top bit is set, else +1.
+ * Outputs: caller-owned host arrays hash[G*J] (int32) and sign[G*J] (int8),
+ * row-major [G][J].  Deterministic in (seed, K, N, c, BK, BN).
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE (K % BK, (K/BK) % c, N % BN, non-positive
+ * sizes, c > SS1_MAX_C, J > SS1_MAX_CHUNKS).
+ */
+ss1_status ss1_plan(uint64_t seed, int64_t K, int64_t N, int32_t c, int32_t BK, int32_t BN,
+                    int32_t* hash, int8_t* sign);
+
+/*
+ * ss1_plan_index -- HOST.  Validates a plan (0 <= hash < Jc, sign = +-1, and
+ * exactly c input chunks per compressed chunk in every group) and writes its
+ * inverse: idx[g][t][0..c-1] are the input chunks of compressed chunk t of
+ * group g in ascending order, isign[g][t][r] = sign[g][idx[g][t][r]].
+ * Inputs hash[G*J], sign[G*J]; outputs idx[G*Jc*c], isign[G*Jc*c]; all host,
+ * caller-owned.  Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_PLAN (outputs are
+ * then unspecified).
+ */
+ss1_status ss1_plan_index(const int32_t* hash, const int8_t* sign, int64_t K, int64_t N,
+                          int32_t c, int32_t BK, int32_t BN, int32_t* idx, int8_t* isign);
+
+/*
+ * ss1_forward -- DEVICE, asynchronous on `stream` (a hipStream_t; NULL means
+ * the default stream).  y = SS1(x) for one layer: the input sketch by the
+ * plan's signed chunk additions followed by the contraction with W_c (SS1
+ * summary page, "Approach").
+ *   x   : [M][K]  (rows = M >= 0, cols = K),  dtype F32 or BF16
+ *   W_c : [N][K/c], same dtype as x
+ *   hash, sign : DEVICE arrays [G][J] as written by ss1_plan (int32 / int8)
+ *   y   : [M][N], same dtype as x; written, never read
+ * Requirements: K % BK == 0, (K/BK) % c == 0, N % BN == 0, 1 <= c <= SS1_MAX_C,
+ * J <= SS1_MAX_CHUNKS; BK % 8 == 0 for BF16 and BK % 4 == 0 for F32; x, W_c and
+ * y 16-byte aligned; hash 4-byte aligned.  M == 0 enqueues nothing.
+ * The plan must be balanced (as ss1_plan makes it and ss1_plan_index checks);
+ * the kernels never read or write outside the buffers whatever the plan
+ * holds, but y is unspecified for a plan that is not balanced.
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (all before
+ * any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_forward(const ss1_tensor* x, const ss1_tensor* W_c,
+                       const int32_t* hash, const int8_t* sign,
+                       int32_t c, int32_t BK, int32_t BN,
+                       ss1_tensor* y, void* stream);
+
+/*
+ * ss1_forward_idx -- as ss1_forward, but the plan is given as its inverse
+ * index (DEVICE arrays idx [G][Jc][c] int32 and isign [G][Jc][c] int8, as
+ * written by ss1_plan_index), which the kernels read directly.  idx must be
+ * 4-byte aligned.  Entries outside [0, J) are treated as absent sources.
+ */
+ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
+                           const int32_t* idx, const int8_t* isign,
+                           int32_t c, int32_t BK, int32_t BN,
+                           ss1_tensor* y, void* stream);
+
+/*
+ * ss1_forward_algo / ss1_forward_idx_algo -- as ss1_forward / ss1_forward_idx
+ * with an explicit kernel choice (ss1_algo).  Returns SS1_ERR_ALGO, before any
+ * HIP call, when that kernel cannot run the given dtype or shape:
+ *   FUSED  : BF16, BK % 32 == 0, BN in {32, 64, 128}
+ *   SMALLM : BF16, M <= 16, BK % 32 == 0, BN % 16 == 0
+ *   GENERIC: any valid call
+ */
+ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
+                            const int32_t* hash, const int8_t* sign,
+                            int32_t c, int32_t BK, int32_t BN,
+                            ss1_tensor* y, int32_t algo, void* stream);
+ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
+                                const int32_t* idx, const int8_t* isign,
+                                int32_t c, int32_t BK, int32_t BN,
+                                ss1_tensor* y, int32_t algo, void* stream);
+
+/*
+ * ss1_sketch -- DEVICE, asynchronous.  The standalone input sketch (the first
+ * of the two steps on the SS1 summary page, "Approach") for every group:
+ *   z[g][m][k'] for g < G = N/BN, m < M, k' < Kc, written as a [G*M][Kc]
+ *   row-major matrix (z->rows = G*M, z->cols = K/c).
+ * x is F32 or BF16; z is F32 (the float32 sum itself) or BF16 (that sum
+ * rounded to nearest, ties to even).  F32 x requires F32 z.  hash/sign as for
+ * ss1_forward; same alignment rules.
+ */
+ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* sign,
+                      int32_t c, int32_t BK, int32_t BN, int64_t N,
+                      ss1_tensor* z, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS1_H */

@@ -1,0 +1,20 @@
+"""CPU oracle for the SS1 forward (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package; the product path never does.
+"""
+from .ss1_oracle import (  # noqa: F401
+    SplitMix64,
+    bf16_bits_to_f64,
+    check_plan,
+    dense_expand,
+    dims,
+    flops,
+    forward,
+    forward_mirror,
+    identity_plan,
+    plan,
+    plan_index,
+    sketch,
+    sketch_rounded,
+)

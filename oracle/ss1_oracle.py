@@ -1,0 +1,305 @@
+"""Plain CPU oracle for the Sketch Structured Transform (SS1) linear-layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (the HIP library and its Python binding) never touches it, and it
+shares no code with that path: not the plan generator, not the bf16 decoding,
+not the index construction.  Random numbers the method draws (the hash and the
+signs) come from SplitMix64, a published counter-based generator that this
+module implements on its own from its definition.
+
+What it computes, and where that is stated
+------------------------------------------
+Sources (page titles; no code exists on any of them):
+
+* "SS1: Accelerating Inference with Fast and Expressive Sketch Structured
+  Transform" (atlas.scime.ai summary page), section *Approach*: parameter
+  sharing is confined to each neuron's own weight vector; hash functions that
+  are coalesced along K and along N make the layer first sketch its input down
+  by the compression factor with additions and subtractions only, and then
+  multiply that sketch by the compressed weight, so FLOPs drop by the factor.
+* The SS1 author abstract (taxoreview abstract list for that author group):
+  the operator shares parameters randomly but in a structured way to cut
+  computation; dense pre-trained layers can be projected onto it.
+* CountSketch (Charikar, Chen and Farach-Colton 2002, entry 29 of the reference
+  list on the "Deja Vu: Contextual Sparsity" page): a sketch that adds each
+  coordinate, with a random sign, into one random bucket.
+
+Readings where the pages are silent (each is listed in the design doc):
+
+* K-coalescing: inputs are cut into J = K/BK chunks of BK consecutive
+  coordinates; input chunk j of neuron group g lands in compressed chunk
+  hash[g][j], keeping its offset u inside the chunk.
+* N-coalescing: BN consecutive neurons (group g = n // BN) share one hash and
+  one sign vector; groups are independent.
+* Signs: one +-1 per (group, input chunk); no scaling by 1/sqrt(c); no bias.
+* Balanced hash: every compressed chunk receives exactly c input chunks.  The
+  oracle's forward accepts any hash in range (balanced or not); only the plan
+  generator promises balance.
+* Plan generator: SplitMix64, Fisher-Yates with plain modulo, then one sign bit
+  per chunk (top bit of a draw), all per group in group order.
+* Precision: everything in float64; bf16 inputs are widened exactly.
+
+Nothing here is blocked, fused or reordered beyond the definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_MASK64 = (1 << 64) - 1
+_GOLDEN_GAMMA = 0x9E3779B97F4A7C15
+
+
+class SplitMix64:
+    """SplitMix64 (Steele, Lea and Flood, OOPSLA 2014, "Fast splittable
+    pseudorandom number generators"), as published by its authors: the state
+    advances by the golden-ratio gamma and each output is the state passed
+    through a 64-bit xor-shift-multiply finaliser.  Python integers, masked to
+    64 bits, so every step is exact."""
+
+    def __init__(self, seed: int):
+        self.state = int(seed) & _MASK64
+
+    def next(self) -> int:
+        self.state = (self.state + _GOLDEN_GAMMA) & _MASK64
+        z = self.state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        return z ^ (z >> 31)
+
+
+def dims(K: int, N: int, c: int, BK: int, BN: int) -> dict:
+    """Derived sizes: J input chunks, Jc compressed chunks, Kc compressed width,
+    G neuron groups.  Raises ValueError when the chunking does not divide."""
+    if min(K, N, c, BK, BN) <= 0:
+        raise ValueError("K, N, c, BK, BN must be positive")
+    if K % BK:
+        raise ValueError("K must be a multiple of BK")
+    J = K // BK
+    if J % c:
+        raise ValueError("the number of input chunks K/BK must be a multiple of c")
+    if N % BN:
+        raise ValueError("N must be a multiple of BN")
+    Jc = J // c
+    return {"J": J, "Jc": Jc, "Kc": Jc * BK, "G": N // BN}
+
+
+def plan(seed: int, K: int, N: int, c: int, BK: int, BN: int):
+    """Seeded balanced chunk hash and +-1 signs, one pair of vectors per group.
+
+    Group by group, in order: shuffle the J chunk ids with Fisher-Yates (for
+    i = J-1 down to 1, swap position i with position ``draw % (i+1)``); the
+    shuffled list is cut into Jc consecutive runs of c and run t becomes the
+    source set of compressed chunk t.  Then draw one value per input chunk,
+    in chunk order, and use its top bit as the sign (1 -> -1).
+
+    Returns ``hash`` int32 [G][J] with values in [0, Jc) and ``sign`` int8
+    [G][J] with values +-1."""
+    d = dims(K, N, c, BK, BN)
+    J, G = d["J"], d["G"]
+    rng = SplitMix64(seed)
+    hash_ = np.empty((G, J), dtype=np.int32)
+    sign = np.empty((G, J), dtype=np.int8)
+    for g in range(G):
+        order = list(range(J))
+        for i in range(J - 1, 0, -1):
+            k = rng.next() % (i + 1)
+            order[i], order[k] = order[k], order[i]
+        for p in range(J):
+            hash_[g, order[p]] = p // c
+        for j in range(J):
+            sign[g, j] = -1 if (rng.next() >> 63) else 1
+    return hash_, sign
+
+
+def identity_plan(K: int, N: int, BK: int, BN: int):
+    """The c = 1 plan that maps every chunk to itself with sign +1, under which
+    SS1 must reduce to a dense linear layer (the zero-compression end of the
+    parameter-sharing family)."""
+    d = dims(K, N, 1, BK, BN)
+    J, G = d["J"], d["G"]
+    hash_ = np.tile(np.arange(J, dtype=np.int32), (G, 1))
+    sign = np.ones((G, J), dtype=np.int8)
+    return hash_, sign
+
+
+def check_plan(hash_, sign, K: int, N: int, c: int, BK: int, BN: int, balanced: bool = True):
+    """Validate a plan: shapes, 0 <= hash < Jc, sign in {-1, +1}, and (when
+    ``balanced``) exactly c input chunks per compressed chunk in every group.
+    Raises ValueError naming the first violation."""
+    d = dims(K, N, c, BK, BN)
+    J, Jc, G = d["J"], d["Jc"], d["G"]
+    hash_ = np.asarray(hash_)
+    sign = np.asarray(sign)
+    if hash_.shape != (G, J) or sign.shape != (G, J):
+        raise ValueError(f"plan arrays must have shape {(G, J)}")
+    for g in range(G):
+        counts = [0] * Jc
+        for j in range(J):
+            t = int(hash_[g, j])
+            if not 0 <= t < Jc:
+                raise ValueError(f"hash[{g}][{j}] = {t} outside [0, {Jc})")
+            if int(sign[g, j]) not in (-1, 1):
+                raise ValueError(f"sign[{g}][{j}] = {int(sign[g, j])} is not +-1")
+            counts[t] += 1
+        if balanced:
+            for t in range(Jc):
+                if counts[t] != c:
+                    raise ValueError(f"group {g}: compressed chunk {t} receives {counts[t]} chunks, not {c}")
+
+
+def plan_index(hash_, sign, K: int, N: int, c: int, BK: int, BN: int):
+    """Inverse of a balanced plan: ``idx[g][t]`` lists the c input chunks that
+    land in compressed chunk t of group g, in ascending order, and
+    ``isign[g][t][r]`` is the sign of ``idx[g][t][r]``.  int32 and int8 arrays
+    of shape [G][Jc][c]."""
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=True)
+    d = dims(K, N, c, BK, BN)
+    J, Jc, G = d["J"], d["Jc"], d["G"]
+    idx = np.empty((G, Jc, c), dtype=np.int32)
+    isign = np.empty((G, Jc, c), dtype=np.int8)
+    for g in range(G):
+        fill = [0] * Jc
+        for j in range(J):  # ascending j gives ascending sources per slot
+            t = int(hash_[g, j])
+            idx[g, t, fill[t]] = j
+            isign[g, t, fill[t]] = sign[g, j]
+            fill[t] += 1
+    return idx, isign
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) exactly: a bf16 value is the float32
+    whose top 16 bits are the pattern and whose low 16 bits are zero."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def sketch(x, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+    """Per-group chunk sketch of the input rows, in float64.
+
+    For every group g a fresh [M][Kc] accumulator starts at zero; walking the
+    input chunks j in ascending order, chunk j of every row, times sign[g][j],
+    is added into compressed chunk hash[g][j] at the same offsets.  Returns
+    z with shape [G][M][Kc].  Accepts any in-range hash (balance not needed)."""
+    d = dims(K, N, c, BK, BN)
+    J, Kc, G = d["J"], d["Kc"], d["G"]
+    x = np.asarray(x, dtype=np.float64)
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError(f"x must have shape [M][{K}]")
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
+    M = x.shape[0]
+    z = np.zeros((G, M, Kc), dtype=np.float64)
+    for g in range(G):
+        for j in range(J):
+            t = int(hash_[g, j])
+            s = float(sign[g, j])
+            z[g, :, t * BK:(t + 1) * BK] += s * x[:, j * BK:(j + 1) * BK]
+    return z
+
+
+def forward(x, Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+    """SS1 forward in float64: sketch the input (as in :func:`sketch`), then
+    multiply group g's sketch by its BN rows of the compressed weight,
+    ``y[:, g*BN:(g+1)*BN] = z_g @ Wc[g*BN:(g+1)*BN, :].T``.
+
+    ``x`` is [M][K], ``Wc`` is [N][Kc] (row-major, one row per neuron, like a
+    dense linear layer's [out][in] weight).  Returns y, [M][N] float64."""
+    d = dims(K, N, c, BK, BN)
+    Kc, G = d["Kc"], d["G"]
+    Wc = np.asarray(Wc, dtype=np.float64)
+    if Wc.shape != (N, Kc):
+        raise ValueError(f"Wc must have shape {(N, Kc)}")
+    z = sketch(x, hash_, sign, K, N, c, BK, BN)
+    M = z.shape[1]
+    y = np.empty((M, N), dtype=np.float64)
+    for g in range(G):
+        y[:, g * BN:(g + 1) * BN] = z[g] @ Wc[g * BN:(g + 1) * BN, :].T
+    return y
+
+
+def dense_expand(Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+    """The dense [N][K] weight that SS1's parameter sharing stands for: entry
+    (n, j*BK + u) is sign[g][j] * Wc[n, hash[g][j]*BK + u] with g = n // BN.
+    By linearity ``x @ dense_expand(...).T`` equals :func:`forward`."""
+    d = dims(K, N, c, BK, BN)
+    J, Kc, G = d["J"], d["Kc"], d["G"]
+    Wc = np.asarray(Wc, dtype=np.float64)
+    if Wc.shape != (N, Kc):
+        raise ValueError(f"Wc must have shape {(N, Kc)}")
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
+    W = np.empty((N, K), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * BN, (g + 1) * BN)
+        for j in range(J):
+            t = int(hash_[g, j])
+            W[rows, j * BK:(j + 1) * BK] = float(sign[g, j]) * Wc[rows, t * BK:(t + 1) * BK]
+    return W
+
+
+def sketch_rounded(x, hash_, sign, K: int, N: int, c: int, BK: int, BN: int,
+                   to_bf16: bool) -> np.ndarray:
+    """Diagnostic "mirror" sketch: the same sum as :func:`sketch`, but taken in
+    float32 over the sources of each compressed chunk in ascending chunk order
+    (starting from the first signed source), then, when ``to_bf16``, rounded
+    to the nearest bf16 value with ties to even.  A GPU path that keeps its
+    sketch in float32 and rounds it to bf16 once should reproduce this bit for
+    bit for c <= 2 and closely otherwise.  Returns float64 values of the
+    rounded sketch, [G][M][Kc]."""
+    d = dims(K, N, c, BK, BN)
+    J, Jc, Kc, G = d["J"], d["Jc"], d["Kc"], d["G"]
+    x32 = np.asarray(x, dtype=np.float32)
+    M = x32.shape[0]
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
+    z = np.zeros((G, M, Kc), dtype=np.float64)
+    for g in range(G):
+        acc = [None] * Jc
+        for j in range(J):
+            t = int(hash_[g, j])
+            term = np.float32(sign[g, j]) * x32[:, j * BK:(j + 1) * BK]
+            acc[t] = term if acc[t] is None else (acc[t] + term).astype(np.float32)
+        for t in range(Jc):
+            if acc[t] is None:
+                continue
+            v = acc[t]
+            if to_bf16:
+                v = _round_f32_to_bf16(v)
+            z[g, :, t * BK:(t + 1) * BK] = v.astype(np.float64)
+    return z
+
+
+def _round_f32_to_bf16(v) -> np.ndarray:
+    """Round float32 values to bf16 precision (8 significant bits), nearest,
+    ties to even, computed on the float64 value with frexp/ldexp so that no
+    bit trick is shared with any other code.  Finite inputs only."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)              # v = m * 2**e, 0.5 <= |m| < 1
+    scaled = np.ldexp(m, 8)         # 8 significant bits left of the point
+    r = np.round(scaled)            # numpy rounds half to even
+    return np.ldexp(r, e - 8).astype(np.float32)
+
+
+def forward_mirror(x, Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int,
+                   sketch_bf16: bool) -> np.ndarray:
+    """Diagnostic forward using :func:`sketch_rounded` (float32 sketch, then
+    optionally bf16) followed by the same float64 contraction as
+    :func:`forward`.  Used for a tighter check than the plain tolerance."""
+    d = dims(K, N, c, BK, BN)
+    Kc, G = d["Kc"], d["G"]
+    Wc = np.asarray(Wc, dtype=np.float64)
+    if Wc.shape != (N, Kc):
+        raise ValueError(f"Wc must have shape {(N, Kc)}")
+    z = sketch_rounded(x, hash_, sign, K, N, c, BK, BN, sketch_bf16)
+    M = z.shape[1]
+    y = np.empty((M, N), dtype=np.float64)
+    for g in range(G):
+        y[:, g * BN:(g + 1) * BN] = z[g] @ Wc[g * BN:(g + 1) * BN, :].T
+    return y
+
+
+def flops(M: int, K: int, N: int, c: int) -> dict:
+    """Work of one forward: the compressed contraction does 2*M*N*K/c FLOPs
+    (the reduction by c the method claims); the dense layer it replaces does
+    2*M*N*K.  Sketch additions are counted apart: each of the G groups adds
+    M*K/c*(c-1) values."""
+    return {"compressed": 2 * M * N * K // c, "dense_equiv": 2 * M * N * K}

@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself:
+published generator values, brute-force expansion into the equivalent dense
+weight, the c = 1 identity case against a library matmul, the Kronecker
+(CountSketch-matrix) form, the textbook CountSketch scatter, and invariants of
+the plan.  CPU only."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from ss1_inputs import bf16_bits_to_f32, draw, f32_to_bf16_bits
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _kat():
+    out, seed = {}, None
+    with open(os.path.join(GOLDEN, "splitmix64_kat.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("seed"):
+                seed = int(line.split()[1])
+                out[seed] = []
+            else:
+                out[seed].append(int(line))
+    return out
+
+
+def test_splitmix64_known_answers():
+    for seed, vals in _kat().items():
+        r = oracle.SplitMix64(seed)
+        assert [r.next() for _ in vals] == vals
+
+
+# ----------------------------------------------------------------- plan pins
+SHAPES = [  # K, N, c, BK, BN
+    (256, 256, 2, 32, 32),
+    (48, 12, 3, 4, 3),
+    (48, 8, 4, 2, 2),
+    (16, 4, 1, 2, 1),
+    (96, 6, 8, 1, 6),
+]
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", SHAPES)
+def test_plan_balanced_and_signed(K, N, c, BK, BN):
+    h, s = oracle.plan(7, K, N, c, BK, BN)
+    d = oracle.dims(K, N, c, BK, BN)
+    assert h.shape == (d["G"], d["J"]) and s.shape == (d["G"], d["J"])
+    assert h.dtype == np.int32 and s.dtype == np.int8
+    for g in range(d["G"]):
+        counts = np.bincount(h[g], minlength=d["Jc"])
+        assert counts.tolist() == [c] * d["Jc"]
+    assert set(np.unique(s).tolist()) <= {-1, 1}
+
+
+def test_plan_deterministic_and_seed_dependent():
+    a = oracle.plan(11, 512, 128, 2, 16, 32)
+    b = oracle.plan(11, 512, 128, 2, 16, 32)
+    c = oracle.plan(12, 512, 128, 2, 16, 32)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    assert not np.array_equal(a[0], c[0])
+    # groups draw different hashes from one stream
+    assert not np.array_equal(a[0][0], a[0][1])
+
+
+def test_plan_shuffle_reaches_every_pairing_uniformly():
+    # J = 4 chunks, c = 2: the shuffle has 24 orders mapping onto 3 pairings of
+    # the chunks ({01,23}, {02,13}, {03,12}), each hit by 8 orders.  A shuffle
+    # that only reaches cyclic orders (a swap range of i instead of i+1) or is
+    # otherwise biased shows up as a skewed count.
+    counts = {}
+    orders = set()
+    n = 3000
+    for seed in range(n):
+        h, s = oracle.plan(seed, 4, 1, 2, 1, 1)
+        orders.add(tuple(h[0].tolist()))
+        key = frozenset(frozenset(np.flatnonzero(h[0] == t).tolist()) for t in range(2))
+        counts[key] = counts.get(key, 0) + 1
+    assert len(counts) == 3
+    for v in counts.values():
+        assert abs(v - n / 3) < 5 * np.sqrt(n * (1 / 3) * (2 / 3))
+    # all 6 assignments of chunks to compressed slots 0/1 appear
+    assert len(orders) == 6
+
+
+def test_plan_signs_fair():
+    _, s = oracle.plan(5, 4096, 256, 2, 1, 1)
+    frac = float(np.mean(s == -1))
+    assert abs(frac - 0.5) < 0.01
+
+
+def test_identity_plan():
+    h, s = oracle.identity_plan(64, 8, 8, 4)
+    assert (h == np.arange(8)).all() and (s == 1).all()
+    oracle.check_plan(h, s, 64, 8, 1, 8, 4)
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", SHAPES)
+def test_plan_index_partitions_chunks(K, N, c, BK, BN):
+    h, s = oracle.plan(3, K, N, c, BK, BN)
+    idx, isign = oracle.plan_index(h, s, K, N, c, BK, BN)
+    d = oracle.dims(K, N, c, BK, BN)
+    for g in range(d["G"]):
+        flat = idx[g].reshape(-1)
+        assert sorted(flat.tolist()) == list(range(d["J"]))
+        for t in range(d["Jc"]):
+            assert list(idx[g, t]) == sorted(idx[g, t])
+            for r in range(c):
+                j = idx[g, t, r]
+                assert h[g, j] == t and isign[g, t, r] == s[g, j]
+
+
+def test_check_plan_rejects_bad_plans():
+    K, N, c, BK, BN = 64, 8, 2, 8, 4
+    h, s = oracle.plan(1, K, N, c, BK, BN)
+    bad = h.copy(); bad[0, 0] = 4  # out of range (Jc = 4)
+    with pytest.raises(ValueError):
+        oracle.check_plan(bad, s, K, N, c, BK, BN)
+    bad = h.copy(); bad[1, 0] = bad[1, 1] if bad[1, 0] != bad[1, 1] else (bad[1, 1] + 1) % 4
+    with pytest.raises(ValueError):
+        oracle.plan_index(bad, s, K, N, c, BK, BN)  # unbalanced
+    oracle.check_plan(bad, s, K, N, c, BK, BN, balanced=False)
+    bs = s.copy(); bs[0, 3] = 0
+    with pytest.raises(ValueError):
+        oracle.check_plan(h, bs, K, N, c, BK, BN)
+    with pytest.raises(ValueError):
+        oracle.dims(60, 8, 2, 8, 4)  # K % BK
+    with pytest.raises(ValueError):
+        oracle.dims(48, 8, 4, 8, 4)  # J % c
+    with pytest.raises(ValueError):
+        oracle.dims(64, 10, 2, 8, 4)  # N % BN
+
+
+# -------------------------------------------------------------- forward pins
+def _brute_dense(Wc, h, s, K, N, BK, BN):
+    """Equivalent dense weight written out element by element from the
+    parameter-sharing view: weight (n, k) of neuron n is the compressed weight
+    its group's hash points at, times the chunk's sign."""
+    W = [[0.0] * K for _ in range(N)]
+    for n in range(N):
+        g = n // BN
+        for k in range(K):
+            j, u = divmod(k, BK)
+            W[n][k] = float(s[g][j]) * float(Wc[n][h[g][j] * BK + u])
+    return W
+
+
+def _naive_matmul_nt(x, W):
+    M, N = len(x), len(W)
+    K = len(W[0]) if N else 0
+    return [[sum(x[m][k] * W[n][k] for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+TINY = [  # M, K, N, c, BK, BN
+    (3, 16, 8, 2, 4, 4),
+    (5, 24, 6, 3, 2, 3),
+    (1, 32, 8, 4, 2, 2),
+    (4, 12, 4, 1, 3, 4),
+    (2, 64, 12, 8, 1, 12),
+    (0, 16, 8, 2, 4, 4),
+]
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", TINY)
+def test_forward_equals_brute_force_dense_integer_exact(M, K, N, c, BK, BN):
+    Kc = K // c
+    x = draw("int4", 100 + M, (M, K)).astype(np.float64)
+    Wc = draw("int4", 200 + K, (N, Kc)).astype(np.float64)
+    h, s = oracle.plan(9, K, N, c, BK, BN)
+    y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    W = _brute_dense(Wc, h, s, K, N, BK, BN)
+    ref = np.array(_naive_matmul_nt(x.tolist(), W), dtype=np.float64).reshape(M, N)
+    assert y.shape == (M, N)
+    assert np.array_equal(y, ref)  # integers: exact in float64
+    assert np.array_equal(oracle.dense_expand(Wc, h, s, K, N, c, BK, BN), np.array(W))
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", TINY[:5])
+def test_forward_equals_brute_force_dense_random(M, K, N, c, BK, BN):
+    Kc = K // c
+    x = draw("normal", 300 + M, (M, K)).astype(np.float64)
+    Wc = draw("normal", 400 + K, (N, Kc)).astype(np.float64)
+    h, s = oracle.plan(21, K, N, c, BK, BN)
+    y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    ref = np.array(_naive_matmul_nt(x.tolist(), _brute_dense(Wc, h, s, K, N, BK, BN)))
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_identity_plan_is_dense_linear():
+    # the tiny float32 workload's shape with c = 1 and the identity plan
+    M, K, N, BK, BN = 64, 256, 256, 32, 32
+    x = draw("normal", 1, (M, K)).astype(np.float64)
+    W = draw("uniform16", 2, (N, K)).astype(np.float64)
+    h, s = oracle.identity_plan(K, N, BK, BN)
+    y = oracle.forward(x, W, h, s, K, N, 1, BK, BN)
+    assert np.allclose(y, x @ W.T, rtol=1e-13, atol=1e-13)
+    xi = draw("int4", 3, (M, K)).astype(np.float64)
+    Wi = draw("int4", 4, (N, K)).astype(np.float64)
+    assert np.array_equal(oracle.forward(xi, Wi, h, s, K, N, 1, BK, BN), xi @ Wi.T)
+
+
+def test_c1_random_plan_is_signed_chunk_permutation():
+    M, K, N, BK, BN = 5, 32, 8, 4, 4
+    x = draw("int4", 5, (M, K)).astype(np.float64)
+    Wc = draw("int4", 6, (N, K)).astype(np.float64)
+    h, s = oracle.plan(2, K, N, 1, BK, BN)
+    y = oracle.forward(x, Wc, h, s, K, N, 1, BK, BN)
+    for g in range(N // BN):
+        # build the permuted, signed input for this group by moving whole chunks
+        xp = np.zeros_like(x)
+        for j in range(K // BK):
+            xp[:, h[g, j] * BK:(h[g, j] + 1) * BK] = s[g, j] * x[:, j * BK:(j + 1) * BK]
+        assert np.array_equal(y[:, g * BN:(g + 1) * BN], xp @ Wc[g * BN:(g + 1) * BN].T)
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", SHAPES)
+def test_sketch_kronecker_form(K, N, c, BK, BN):
+    d = oracle.dims(K, N, c, BK, BN)
+    M = 3
+    x = draw("normal", 7, (M, K)).astype(np.float64)
+    h, s = oracle.plan(4, K, N, c, BK, BN)
+    z = oracle.sketch(x, h, s, K, N, c, BK, BN)
+    for g in range(d["G"]):
+        S = np.zeros((d["Jc"], d["J"]))
+        S[h[g], np.arange(d["J"])] = s[g]
+        # a CountSketch matrix: one nonzero per column, c per row (balanced)
+        assert ((S != 0).sum(axis=0) == 1).all() and ((S != 0).sum(axis=1) == c).all()
+        P = np.kron(S, np.eye(BK))
+        assert np.allclose(z[g], x @ P.T, rtol=1e-13, atol=1e-13)
+
+
+def test_bk1_bn1_is_textbook_countsketch():
+    # BK = 1, BN = 1: every neuron holds its own CountSketch of the input
+    # (bucket = hash, random sign), the scatter-add form of the textbook sketch.
+    M, K, N, c = 4, 40, 6, 5
+    x = draw("normal", 8, (M, K)).astype(np.float64)
+    Wc = draw("normal", 9, (N, K // c)).astype(np.float64)
+    h, s = oracle.plan(6, K, N, c, 1, 1)
+    y = oracle.forward(x, Wc, h, s, K, N, c, 1, 1)
+    for n in range(N):
+        for m in range(M):
+            buckets = np.zeros(K // c)
+            np.add.at(buckets, h[n], s[n] * x[m])
+            assert abs(y[m, n] - buckets @ Wc[n]) < 1e-12
+
+
+def test_all_plus_signs_preserve_chunk_sums():
+    M, K, N, c, BK, BN = 3, 48, 6, 3, 4, 2
+    x = draw("int4", 10, (M, K)).astype(np.float64)
+    h, _ = oracle.plan(8, K, N, c, BK, BN)
+    s = np.ones_like(h, dtype=np.int8)
+    z = oracle.sketch(x, h, s, K, N, c, BK, BN)
+    for g in range(N // BN):
+        assert np.array_equal(z[g].reshape(M, -1, BK).sum(axis=1), x.reshape(M, -1, BK).sum(axis=1))
+
+
+def test_group_sign_flip_negates_only_that_group():
+    M, K, N, c, BK, BN = 4, 32, 12, 2, 4, 4
+    x = draw("normal", 11, (M, K))
+    Wc = draw("normal", 12, (N, K // c))
+    h, s = oracle.plan(10, K, N, c, BK, BN)
+    y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    s2 = s.copy(); s2[1] = -s2[1]
+    y2 = oracle.forward(x, Wc, h, s2, K, N, c, BK, BN)
+    assert np.array_equal(y2[:, 4:8], -y[:, 4:8])
+    assert np.array_equal(y2[:, :4], y[:, :4]) and np.array_equal(y2[:, 8:], y[:, 8:])
+
+
+def test_linearity():
+    M, K, N, c, BK, BN = 5, 32, 8, 4, 2, 4
+    h, s = oracle.plan(13, K, N, c, BK, BN)
+    x1, x2 = draw("int4", 14, (M, K)), draw("int4", 15, (M, K))
+    W1, W2 = draw("int4", 16, (N, K // c)), draw("int4", 17, (N, K // c))
+    f = lambda x, W: oracle.forward(x, W, h, s, K, N, c, BK, BN)
+    assert np.array_equal(f(2 * x1 - x2, W1), 2 * f(x1, W1) - f(x2, W1))
+    assert np.array_equal(f(x1, W1 + 3 * W2), f(x1, W1) + 3 * f(x1, W2))
+
+
+def test_unbalanced_hash_is_accepted_by_forward():
+    M, K, N, c, BK, BN = 2, 16, 4, 2, 2, 4
+    x = draw("int4", 18, (M, K)).astype(np.float64)
+    Wc = draw("int4", 19, (N, K // c)).astype(np.float64)
+    h = np.zeros((1, 8), dtype=np.int32)  # every chunk into slot 0
+    s = np.ones((1, 8), dtype=np.int8)
+    y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    ref = np.array(_naive_matmul_nt(x.tolist(), _brute_dense(Wc, h, s, K, N, BK, BN)))
+    assert np.array_equal(y, ref)
+
+
+def test_bf16_widening_is_exact():
+    vals = np.array([0.0, 1.0, -2.5, 3.140625, 1e-3, -65504.0, 2.0 ** -100], dtype=np.float32)
+    bits = f32_to_bf16_bits(vals)
+    assert np.array_equal(oracle.bf16_bits_to_f64(bits), bf16_bits_to_f32(bits).astype(np.float64))
+    assert oracle.bf16_bits_to_f64(np.array([0x3F80, 0xC020], dtype=np.uint16)).tolist() == [1.0, -2.5]
+
+
+def test_mirror_sketch_rounding():
+    # c = 2 with bf16 inputs: float32 holds the pair sum exactly unless the
+    # exponents differ a lot, so the mirror sketch's bf16 value must be the
+    # ties-to-even rounding of the float32 sum; the bit-level encoder used for
+    # inputs is an independent rounding routine to compare with.
+    M, K, N, c, BK, BN = 64, 128, 8, 2, 8, 8
+    xb = f32_to_bf16_bits(draw("normal", 20, (M, K)))
+    x = bf16_bits_to_f32(xb)
+    h, s = oracle.plan(14, K, N, c, BK, BN)
+    zr = oracle.sketch_rounded(x, h, s, K, N, c, BK, BN, to_bf16=True)
+    z32 = oracle.sketch_rounded(x, h, s, K, N, c, BK, BN, to_bf16=False)
+    z = oracle.sketch(x.astype(np.float64), h, s, K, N, c, BK, BN)
+    assert np.array_equal(z32, z)  # exact pair sums
+    ref = bf16_bits_to_f32(f32_to_bf16_bits(z32.astype(np.float32))).astype(np.float64)
+    assert np.array_equal(zr, ref)
+    # ties go to even
+    t = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8], dtype=np.float32)
+    from oracle.ss1_oracle import _round_f32_to_bf16
+    assert _round_f32_to_bf16(t).tolist() == [1.0, 1.0 + 2.0 ** -6]
+
+
+def test_flops_accounting():
+    f = oracle.flops(8192, 768, 3072, 2)
+    assert f["dense_equiv"] == 2 * 8192 * 768 * 3072 and f["compressed"] * 2 == f["dense_equiv"]
+
+
+def test_all_small_pairings_enumerated_match_dense():
+    # exhaustive over every balanced plan and sign pattern of a 4-chunk, c = 2
+    # layer with one group: forward must equal the dense expansion each time
+    M, K, N, c, BK, BN = 2, 8, 2, 2, 2, 2
+    x = draw("int4", 21, (M, K)).astype(np.float64)
+    Wc = draw("int4", 22, (N, K // c)).astype(np.float64)
+    for perm in itertools.permutations(range(4)):
+        h = np.array([[p // 2 for p in np.argsort(perm)]], dtype=np.int32)
+        for signs in itertools.product((-1, 1), repeat=4):
+            s = np.array([signs], dtype=np.int8)
+            y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+            ref = np.array(_naive_matmul_nt(x.tolist(), _brute_dense(Wc, h, s, K, N, BK, BN)))
+            assert np.array_equal(y, ref)
+
+
+def test_plan_worked_examples():
+    with open(os.path.join(GOLDEN, "plan_worked_examples.txt")) as f:
+        rows = [l for l in f if l.strip() and not l.startswith("#")]
+    assert rows
+    for line in rows:
+        head, hs, ss = (p.split() for p in line.split("|"))
+        seed, K, N, c, BK, BN = (int(v) for v in head)
+        h, s = oracle.plan(seed, K, N, c, BK, BN)
+        assert h[0].tolist() == [int(v) for v in hs]
+        assert s[0, :len(ss)].tolist() == [int(v) for v in ss]
