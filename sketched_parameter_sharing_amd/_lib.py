@@ -1,0 +1,204 @@
+"""ctypes binding of libss1.so: argument marshalling only.
+
+Every step of the SS1 forward runs in the library's HIP kernels; this module
+turns torch tensors (device memory) and NumPy arrays (host plan arrays) into
+the pointers and sizes of the C ABI declared in ``include/ss1.h``.  It raises
+:class:`SS1Error` for any non-zero status and refuses to run at all when the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libss1.so")
+
+# status codes (ss1_status)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = range(8)
+# dtypes (ss1_dtype)
+F32, BF16 = 0, 1
+# kernel choice (ss1_algo)
+ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC = range(4)
+ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC}
+
+EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
+           "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_sketch")
+
+
+class SS1Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _status_string(status) if _LIB is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def load():
+    """Load libss1.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sketched_parameter_sharing_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+    tp = ctypes.POINTER(Tensor)
+    lib.ss1_version.restype = ctypes.c_char_p
+    lib.ss1_version.argtypes = []
+    lib.ss1_status_string.restype = ctypes.c_char_p
+    lib.ss1_status_string.argtypes = [i32]
+    lib.ss1_plan.restype = i32
+    lib.ss1_plan.argtypes = [u64, i64, i64, i32, i32, i32, vp, vp]
+    lib.ss1_plan_index.restype = i32
+    lib.ss1_plan_index.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp]
+    for name in ("ss1_forward", "ss1_forward_idx"):
+        f = getattr(lib, name)
+        f.restype = i32
+        f.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, vp]
+    for name in ("ss1_forward_algo", "ss1_forward_idx_algo"):
+        f = getattr(lib, name)
+        f.restype = i32
+        f.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, i32, vp]
+    lib.ss1_sketch.restype = i32
+    lib.ss1_sketch.argtypes = [tp, vp, vp, i32, i32, i32, i64, tp, vp]
+    _LIB = lib
+    return lib
+
+
+def _status_string(s: int) -> str:
+    return load().ss1_status_string(int(s)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise SS1Error(status, where)
+
+
+def version() -> str:
+    return load().ss1_version().decode()
+
+
+# ------------------------------------------------------------------ host plan
+def _np_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def plan(seed: int, K: int, N: int, c: int, BK: int, BN: int):
+    """Seeded balanced plan from the library (host): int32 hash [G][J], int8
+    sign [G][J]."""
+    if K <= 0 or BK <= 0 or N <= 0 or BN <= 0 or K % BK or N % BN:
+        _check(load().ss1_plan(seed, K, N, c, BK, BN, None, None), "ss1_plan")
+    G, J = N // BN, K // BK
+    h = np.empty((G, J), dtype=np.int32)
+    s = np.empty((G, J), dtype=np.int8)
+    _check(load().ss1_plan(int(seed) & (2**64 - 1), K, N, c, BK, BN, _np_ptr(h), _np_ptr(s)), "ss1_plan")
+    return h, s
+
+
+def plan_index(hash_, sign, K: int, N: int, c: int, BK: int, BN: int):
+    """Validated inverse index from the library (host): int32 idx [G][Jc][c]
+    and int8 isign [G][Jc][c]."""
+    h = np.ascontiguousarray(hash_, dtype=np.int32)
+    s = np.ascontiguousarray(sign, dtype=np.int8)
+    G, J = N // BN, K // BK
+    if h.size != G * J or s.size != G * J:
+        raise ValueError("plan arrays do not match (K, N, BK, BN)")
+    idx = np.empty(h.size, dtype=np.int32)
+    isg = np.empty(h.size, dtype=np.int8)
+    _check(load().ss1_plan_index(_np_ptr(h), _np_ptr(s), K, N, c, BK, BN, _np_ptr(idx), _np_ptr(isg)),
+           "ss1_plan_index")
+    Jc = J // c
+    return idx.reshape(G, Jc, c), isg.reshape(G, Jc, c)
+
+
+# ------------------------------------------------------------- device calls
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _desc(t) -> Tensor:
+    if t.dim() != 2 or not t.is_contiguous():
+        raise ValueError("matrices must be 2-D and contiguous")
+    return Tensor(t.data_ptr() if t.numel() else None, _dtype_code(t), 0, t.shape[0], t.shape[1])
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def _check_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("device entry points take GPU tensors")
+
+
+def forward(x, W_c, hash_, sign, c: int, BK: int, BN: int, y=None, algo: str = "auto", stream=None):
+    """y = SS1(x) on the GPU (ss1_forward / ss1_forward_algo).  ``hash_`` and
+    ``sign`` are device tensors (int32 / int8) of shape [G][J]."""
+    import torch
+    _check_device(x, W_c, hash_, sign)
+    if y is None:
+        y = torch.empty((x.shape[0], W_c.shape[0]), dtype=x.dtype, device=x.device)
+    dx, dw, dy = _desc(x), _desc(W_c), _desc(y)
+    lib = load()
+    if algo == "auto":
+        st = lib.ss1_forward(ctypes.byref(dx), ctypes.byref(dw), hash_.data_ptr(), sign.data_ptr(),
+                             c, BK, BN, ctypes.byref(dy), _stream(stream))
+    else:
+        st = lib.ss1_forward_algo(ctypes.byref(dx), ctypes.byref(dw), hash_.data_ptr(), sign.data_ptr(),
+                                  c, BK, BN, ctypes.byref(dy), ALGOS[algo], _stream(stream))
+    _check(st, "ss1_forward")
+    return y
+
+
+def forward_idx(x, W_c, idx, isign, c: int, BK: int, BN: int, y=None, algo: str = "auto", stream=None):
+    """As :func:`forward` with the inverse index (device int32 / int8
+    tensors [G][Jc][c]) instead of the forward hash."""
+    import torch
+    _check_device(x, W_c, idx, isign)
+    if y is None:
+        y = torch.empty((x.shape[0], W_c.shape[0]), dtype=x.dtype, device=x.device)
+    dx, dw, dy = _desc(x), _desc(W_c), _desc(y)
+    lib = load()
+    if algo == "auto":
+        st = lib.ss1_forward_idx(ctypes.byref(dx), ctypes.byref(dw), idx.data_ptr(), isign.data_ptr(),
+                                 c, BK, BN, ctypes.byref(dy), _stream(stream))
+    else:
+        st = lib.ss1_forward_idx_algo(ctypes.byref(dx), ctypes.byref(dw), idx.data_ptr(), isign.data_ptr(),
+                                      c, BK, BN, ctypes.byref(dy), ALGOS[algo], _stream(stream))
+    _check(st, "ss1_forward_idx")
+    return y
+
+
+def sketch(x, hash_, sign, c: int, BK: int, BN: int, N: int, z=None, out_dtype=None, stream=None):
+    """Standalone sketch on the GPU (ss1_sketch): returns z as a [G*M][K/c]
+    tensor (float32 by default, or ``out_dtype``)."""
+    import torch
+    _check_device(x, hash_, sign)
+    G = N // BN
+    if z is None:
+        z = torch.empty((G * x.shape[0], x.shape[1] // c), dtype=out_dtype or torch.float32, device=x.device)
+    dx, dz = _desc(x), _desc(z)
+    st = load().ss1_sketch(ctypes.byref(dx), hash_.data_ptr(), sign.data_ptr(), c, BK, BN, N,
+                           ctypes.byref(dz), _stream(stream))
+    _check(st, "ss1_sketch")
+    return z

@@ -1,0 +1,153 @@
+// The C ABI of the SS1 forward library: argument checks, then kernel choice
+// and launch.  Every check runs on the host before any HIP call, so a call
+// that fails a check has enqueued nothing.
+#include <stdint.h>
+
+#include "ss1_internal.h"
+
+using ss1::Dims;
+using ss1::ForwardArgs;
+using ss1::PlanForm;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_dtype(int32_t t) { return t == SS1_F32 || t == SS1_BF16; }
+
+// Shapes, dtypes and alignment of one forward call.  Fills `a` on success.
+ss1_status check_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* plan_i,
+                         const int8_t* plan_s, int32_t c, int32_t BK, int32_t BN,
+                         const ss1_tensor* y, PlanForm form, void* stream, ForwardArgs* a) {
+    if (!x || !W_c || !y) return SS1_ERR_NULL;
+    if (x->reserved != 0 || W_c->reserved != 0 || y->reserved != 0) return SS1_ERR_SHAPE;
+    if (!valid_dtype(x->dtype) || !valid_dtype(W_c->dtype) || !valid_dtype(y->dtype))
+        return SS1_ERR_DTYPE;
+    if (W_c->dtype != x->dtype || y->dtype != x->dtype) return SS1_ERR_DTYPE;
+    const int64_t M = x->rows;
+    const int64_t K = x->cols;
+    const int64_t N = W_c->rows;
+    Dims d;
+    ss1_status st = ss1::check_chunking(K, N, c, BK, BN, &d);
+    if (st != SS1_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 31) - 1) return SS1_ERR_SHAPE;
+    if (K >= (int64_t(1) << 30) || N >= (int64_t(1) << 31)) return SS1_ERR_SHAPE;
+    if (W_c->cols != d.Kc) return SS1_ERR_SHAPE;
+    if (y->rows != M || y->cols != N) return SS1_ERR_SHAPE;
+    if (x->dtype == SS1_BF16 ? (BK % 8 != 0) : (BK % 4 != 0)) return SS1_ERR_SHAPE;
+    // element counts of each matrix must stay below 2^62 bytes of addressing
+    if (M > 0 && K > (int64_t(1) << 40) / M) return SS1_ERR_SHAPE;
+    if (M > 0 && N > (int64_t(1) << 40) / M) return SS1_ERR_SHAPE;
+    if (M > 0) {
+        if (!x->data || !y->data) return SS1_ERR_NULL;
+    }
+    if (!W_c->data || !plan_i || !plan_s) return SS1_ERR_NULL;
+    if (!aligned(x->data, 16) || !aligned(W_c->data, 16) || !aligned(y->data, 16))
+        return SS1_ERR_ALIGN;
+    if (!aligned(plan_i, 4)) return SS1_ERR_ALIGN;
+    a->x = x->data;
+    a->w = W_c->data;
+    a->y = y->data;
+    a->plan_i = plan_i;
+    a->plan_s = plan_s;
+    a->form = form;
+    a->M = M;
+    a->d = d;
+    a->dtype = x->dtype;
+    a->stream = stream;
+    return SS1_OK;
+}
+
+ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* plan_i,
+                       const int8_t* plan_s, int32_t c, int32_t BK, int32_t BN, ss1_tensor* y,
+                       int32_t algo, PlanForm form, void* stream) {
+    ForwardArgs a;
+    ss1_status st = check_forward(x, W_c, plan_i, plan_s, c, BK, BN, y, form, stream, &a);
+    if (st != SS1_OK) return st;
+    switch (algo) {
+        case SS1_ALGO_AUTO:
+            if (a.M == 0) return SS1_OK;
+            if (ss1::smallm_supported(a)) return ss1::launch_smallm(a);
+            if (ss1::fused_supported(a)) return ss1::launch_fused(a);
+            return ss1::launch_generic(a);
+        case SS1_ALGO_FUSED:
+            if (!ss1::fused_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_fused(a);
+        case SS1_ALGO_SMALLM:
+            if (!ss1::smallm_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_smallm(a);
+        case SS1_ALGO_GENERIC:
+            return a.M == 0 ? SS1_OK : ss1::launch_generic(a);
+        default:
+            return SS1_ERR_ALGO;
+    }
+}
+
+}  // namespace
+
+extern "C" const char* ss1_version(void) { return "0.1.0"; }
+
+extern "C" const char* ss1_status_string(ss1_status s) {
+    switch (s) {
+        case SS1_OK: return "ok";
+        case SS1_ERR_NULL: return "null pointer";
+        case SS1_ERR_SHAPE: return "invalid or inconsistent shape";
+        case SS1_ERR_DTYPE: return "invalid or mismatched dtype";
+        case SS1_ERR_PLAN: return "invalid plan (range, sign or balance)";
+        case SS1_ERR_ALIGN: return "misaligned pointer";
+        case SS1_ERR_HIP: return "HIP launch or runtime error";
+        case SS1_ERR_ALGO: return "requested kernel cannot run this call";
+    }
+    return "unknown status";
+}
+
+extern "C" ss1_status ss1_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash,
+                                  const int8_t* sign, int32_t c, int32_t BK, int32_t BN,
+                                  ss1_tensor* y, void* stream) {
+    return run_forward(x, W_c, hash, sign, c, BK, BN, y, SS1_ALGO_AUTO, PlanForm::Hash, stream);
+}
+
+extern "C" ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
+                                      const int32_t* idx, const int8_t* isign, int32_t c,
+                                      int32_t BK, int32_t BN, ss1_tensor* y, void* stream) {
+    return run_forward(x, W_c, idx, isign, c, BK, BN, y, SS1_ALGO_AUTO, PlanForm::Index, stream);
+}
+
+extern "C" ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
+                                       const int32_t* hash, const int8_t* sign, int32_t c,
+                                       int32_t BK, int32_t BN, ss1_tensor* y, int32_t algo,
+                                       void* stream) {
+    return run_forward(x, W_c, hash, sign, c, BK, BN, y, algo, PlanForm::Hash, stream);
+}
+
+extern "C" ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
+                                           const int32_t* idx, const int8_t* isign, int32_t c,
+                                           int32_t BK, int32_t BN, ss1_tensor* y, int32_t algo,
+                                           void* stream) {
+    return run_forward(x, W_c, idx, isign, c, BK, BN, y, algo, PlanForm::Index, stream);
+}
+
+extern "C" ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* sign,
+                                 int32_t c, int32_t BK, int32_t BN, int64_t N, ss1_tensor* z,
+                                 void* stream) {
+    if (!x || !z) return SS1_ERR_NULL;
+    if (x->reserved != 0 || z->reserved != 0) return SS1_ERR_SHAPE;
+    if (!valid_dtype(x->dtype) || !valid_dtype(z->dtype)) return SS1_ERR_DTYPE;
+    if (x->dtype == SS1_F32 && z->dtype != SS1_F32) return SS1_ERR_DTYPE;
+    const int64_t M = x->rows;
+    const int64_t K = x->cols;
+    Dims d;
+    ss1_status st = ss1::check_chunking(K, N, c, BK, BN, &d);
+    if (st != SS1_OK) return st;
+    if (M < 0 || M > (int64_t(1) << 31) - 1 || K >= (int64_t(1) << 30)) return SS1_ERR_SHAPE;
+    if (x->dtype == SS1_BF16 ? (BK % 8 != 0) : (BK % 4 != 0)) return SS1_ERR_SHAPE;
+    if (z->rows != d.G * M || z->cols != d.Kc) return SS1_ERR_SHAPE;
+    if (d.G > 65535) return SS1_ERR_SHAPE;
+    if (M > 0 && K > (int64_t(1) << 40) / M) return SS1_ERR_SHAPE;
+    if (!hash || !sign) return SS1_ERR_NULL;
+    if (M == 0) return SS1_OK;
+    if (!x->data || !z->data) return SS1_ERR_NULL;
+    if (!aligned(x->data, 16) || !aligned(z->data, 16)) return SS1_ERR_ALIGN;
+    if (!aligned(hash, 4)) return SS1_ERR_ALIGN;
+    return ss1::launch_sketch(x->data, x->dtype, hash, sign, M, d, z->data, z->dtype, stream);
+}

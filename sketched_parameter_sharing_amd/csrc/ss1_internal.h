@@ -1,0 +1,47 @@
+// Internal declarations shared by the host ABI layer and the kernel launchers.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/ss1.h"
+
+namespace ss1 {
+
+struct Dims {
+    int64_t K, N;
+    int32_t c, BK, BN;
+    int64_t J, Jc, Kc, G;
+};
+
+// Checks the chunking (K % BK, (K/BK) % c, N % BN, ranges) and fills `d`.
+ss1_status check_chunking(int64_t K, int64_t N, int32_t c, int32_t BK, int32_t BN, Dims* d);
+
+// How the device reads the plan: the forward hash/sign [G][J], or the inverse
+// index idx/isign [G][Jc][c].
+enum class PlanForm { Hash, Index };
+
+struct ForwardArgs {
+    const void* x;
+    const void* w;
+    void* y;
+    const int32_t* plan_i;
+    const int8_t* plan_s;
+    PlanForm form;
+    int64_t M;
+    Dims d;
+    int32_t dtype;  // ss1_dtype
+    void* stream;
+};
+
+// Which kernels can run a call (host-side checks only).
+bool fused_supported(const ForwardArgs& a);
+bool smallm_supported(const ForwardArgs& a);
+
+// Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
+ss1_status launch_fused(const ForwardArgs& a);
+ss1_status launch_smallm(const ForwardArgs& a);
+ss1_status launch_generic(const ForwardArgs& a);
+ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
+                         int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
+
+}  // namespace ss1

@@ -1,0 +1,791 @@
+// HIP kernels of the SS1 forward for gfx950 (CDNA4), and their launchers.
+//
+// The method ("SS1: Accelerating Inference with Fast and Expressive Sketch
+// Structured Transform", summary page, "Approach"): sketch the layer input by
+// signed additions of BK-wide input chunks into Kc = K/c compressed positions,
+// one sketch per group of BN neurons, then contract each group's sketch with
+// its BN rows of the compressed weight W_c.
+//
+// Kernels:
+//   sketch_kernel   standalone sketch z[g][m][k'] (float32 sum, optional bf16).
+//   generic_kernel  any dtype / chunking: per block a 64x64 output tile of one
+//                   group, sketch slab and weight slab staged in LDS as
+//                   float32, 4x4 register micro-tiles of fused multiply-adds.
+//                   This is the exact float32 path.
+//   fused_kernel    bf16, any M: per block an MT x BN tile of one group; every
+//                   k-stage builds the sketched input tile in LDS from c
+//                   coalesced chunk reads (float32 sum, then bf16), stages the
+//                   W_c tile beside it, and runs 16x16x32 bf16 MFMA with
+//                   float32 accumulators.  Double-buffered LDS, one barrier
+//                   per stage, XCD-aware tile order.
+//   smallm_kernel   bf16, M <= 16 (decode): per block 16 neurons of one group;
+//                   its waves split Kc, build their 16x32 sketch fragments in
+//                   registers straight from x and stream W_c once from HBM into
+//                   MFMA operands; partial tiles are summed in LDS in a fixed
+//                   order.
+//
+// Every kernel reads the plan of its group into LDS first, either from the
+// forward hash/sign (inverting it there) or from the inverse index.  Source
+// offsets are always built from a chunk number in [0, J), so no plan content
+// can make a kernel read outside x.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "ss1_internal.h"
+
+namespace ss1 {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- plan in LDS
+// One 32-bit word per source: element offset of the source chunk inside an x
+// row (bits 0..29), "negative" (bit 31), "absent" (bit 30).
+constexpr uint32_t kNeg = 0x80000000u;
+constexpr uint32_t kAbsent = 0x40000000u;
+constexpr uint32_t kOffMask = 0x3FFFFFFFu;
+
+__device__ __forceinline__ float entry_sign(uint32_t e) {
+    return (e & kAbsent) ? 0.0f : __uint_as_float((e & kNeg) | 0x3F800000u);
+}
+
+__device__ __forceinline__ uint32_t make_entry(int j, int BK, int s) {
+    return static_cast<uint32_t>(j * BK) | (s < 0 ? kNeg : 0u);
+}
+
+// Fills s_src[t*c + r] (t < Jc, r < c) for group g.  From the forward hash the
+// sources of each compressed chunk are gathered with LDS atomics and then put
+// in ascending chunk order; from the inverse index they are copied.  Needs
+// s_cnt[Jc] scratch for the forward form.  Ends with a barrier.
+template <bool FROM_HASH>
+__device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g,
+                           int J, int Jc, int c, int BK, uint32_t* s_src, int* s_cnt) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int32_t* gi = pi + static_cast<size_t>(g) * J;
+    const int8_t* gs = ps + static_cast<size_t>(g) * J;
+    if (FROM_HASH) {
+        for (int e = tid; e < J; e += nt) s_src[e] = kAbsent;
+        for (int t = tid; t < Jc; t += nt) s_cnt[t] = 0;
+        __syncthreads();
+        for (int j = tid; j < J; j += nt) {
+            const int t = gi[j];
+            const int s = gs[j];
+            if (t >= 0 && t < Jc && (s == 1 || s == -1)) {
+                const int slot = atomicAdd(&s_cnt[t], 1);
+                if (slot < c) s_src[t * c + slot] = make_entry(j, BK, s);
+            }
+        }
+        __syncthreads();
+        for (int t = tid; t < Jc; t += nt) {
+            uint32_t* p = s_src + t * c;
+            for (int a = 1; a < c; ++a) {  // insertion sort; absent entries go last
+                const uint32_t v = p[a];
+                int b = a - 1;
+                while (b >= 0 && (p[b] & ~kNeg) > (v & ~kNeg)) {
+                    p[b + 1] = p[b];
+                    --b;
+                }
+                p[b + 1] = v;
+            }
+        }
+    } else {
+        for (int e = tid; e < J; e += nt) {
+            const int j = gi[e];
+            const int s = gs[e];
+            s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------- bf16 helpers
+// A 32-bit word holding two bf16 values (element 2i in the low half): their
+// float32 values are the halves moved to the top of a word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two float32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float round_to_bf16(float v) {
+    return __uint_as_float(pack_bf16(v, 0.0f) << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float v) {
+    return static_cast<uint16_t>(pack_bf16(v, 0.0f) & 0xFFFFu);
+}
+
+// Accumulates one 16-byte vector of 8 bf16 into acc[8] (first source sets it).
+__device__ __forceinline__ void acc_bf16x8(float (&acc)[8], const uint4& raw, float s, bool first) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(w[i]);
+        const float hi = bf16_hi(w[i]);
+        if (first) {
+            acc[2 * i] = s * lo;
+            acc[2 * i + 1] = s * hi;
+        } else {
+            acc[2 * i] = fmaf(s, lo, acc[2 * i]);
+            acc[2 * i + 1] = fmaf(s, hi, acc[2 * i + 1]);
+        }
+    }
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&acc)[8]) {
+    uint4 r;
+    r.x = pack_bf16(acc[0], acc[1]);
+    r.y = pack_bf16(acc[2], acc[3]);
+    r.z = pack_bf16(acc[4], acc[5]);
+    r.w = pack_bf16(acc[6], acc[7]);
+    return r;
+}
+
+// Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Renumber so that each XCD works through one contiguous range of tiles and
+// tiles sharing an input row band stay in one L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+    const int per = n / 8;
+    if (b >= per * 8) return b;
+    return (b % 8) * per + b / 8;
+}
+
+// ============================================================ sketch kernel
+template <typename TIn, bool OUT_BF16, bool FROM_HASH>
+__global__ __launch_bounds__(256) void sketch_kernel(const TIn* __restrict__ x,
+                                                     const int32_t* __restrict__ pi,
+                                                     const int8_t* __restrict__ ps,
+                                                     void* __restrict__ z, int M, int K, int J,
+                                                     int Jc, int c, int BK, int Kc) {
+    extern __shared__ uint32_t smem[];
+    uint32_t* s_src = smem;
+    int* s_cnt = reinterpret_cast<int*>(smem + J);
+    const int g = blockIdx.y;
+    stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
+
+    constexpr bool IN_BF16 = sizeof(TIn) == 2;
+    constexpr int V = 16 / sizeof(TIn);  // elements per 16-byte vector
+    const int vpc = BK / V;
+    const long long items = static_cast<long long>(M) * Jc * vpc;
+    const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+    for (long long it = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; it < items;
+         it += stride) {
+        const int v = static_cast<int>(it % vpc);
+        const long long rest = it / vpc;
+        const int t = static_cast<int>(rest % Jc);
+        const int m = static_cast<int>(rest / Jc);
+        const TIn* xr = x + static_cast<size_t>(m) * K + v * V;
+        float acc[8];
+        for (int r = 0; r < c; ++r) {
+            const uint32_t e = s_src[t * c + r];
+            const float s = entry_sign(e);
+            const uint4 raw = *reinterpret_cast<const uint4*>(xr + (e & kOffMask));
+            if constexpr (IN_BF16) {
+                acc_bf16x8(acc, raw, s, r == 0);
+            } else {
+                const float f[4] = {__uint_as_float(raw.x), __uint_as_float(raw.y),
+                                    __uint_as_float(raw.z), __uint_as_float(raw.w)};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = (r == 0) ? s * f[i] : fmaf(s, f[i], acc[i]);
+            }
+        }
+        const size_t o = (static_cast<size_t>(g) * M + m) * Kc + static_cast<size_t>(t) * BK + v * V;
+        if constexpr (OUT_BF16) {
+            static_assert(V == 8, "bf16 output needs bf16 input");
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(z) + o) = pack_bf16x8(acc);
+        } else {
+            float* zo = static_cast<float*>(z) + o;
+            *reinterpret_cast<float4*>(zo) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if constexpr (V == 8)
+                *reinterpret_cast<float4*>(zo + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+    }
+}
+
+// =========================================================== generic kernel
+// Block: 256 threads as 16 x 16, output tile 64 rows x 64 columns of one group
+// (columns [nt*64, nt*64+64) of the group, clipped to BN), 4 x 4 per thread.
+// k' runs in ascending order; every product is a float32 fused multiply-add.
+template <typename TIn, bool BF16_SKETCH_AND_OUT, bool FROM_HASH>
+__global__ __launch_bounds__(256) void generic_kernel(const TIn* __restrict__ x,
+                                                      const TIn* __restrict__ w,
+                                                      const int32_t* __restrict__ pi,
+                                                      const int8_t* __restrict__ ps,
+                                                      void* __restrict__ y, int M, int K, int N,
+                                                      int J, int Jc, int c, int BK, int BN,
+                                                      int KW, int n_sub) {
+    constexpr int TM = 64, TN = 64, KWMAX = 32;
+    __shared__ float zs[KWMAX][TM + 4];
+    __shared__ float ws[KWMAX][TN + 4];
+    extern __shared__ uint32_t smem[];
+    uint32_t* s_src = smem;
+    int* s_cnt = reinterpret_cast<int*>(smem + J);
+
+    const int G = N / BN;
+    const int sub = blockIdx.x % n_sub;
+    const int g = (blockIdx.x / n_sub) % G;
+    const int mt = blockIdx.x / (n_sub * G);
+    stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
+
+    const int m0 = mt * TM;
+    const int col0 = sub * TN;                  // column inside the group
+    const int width = min(TN, BN - col0);       // columns of this tile
+    const int n0 = g * BN + col0;
+    const int Kc = Jc * BK;
+    const int tid = threadIdx.x;
+    const int tx = tid % 16, ty = tid / 16;
+
+    auto load = [](const TIn* p) -> float {
+        if constexpr (sizeof(TIn) == 2)
+            return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(p)) << 16);
+        else
+            return *reinterpret_cast<const float*>(p);
+    };
+
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    for (int t = 0; t < Jc; ++t) {
+        for (int u0 = 0; u0 < BK; u0 += KW) {
+            // sketch slab [TM][KW] and weight slab [TN][KW], stored k-major
+            for (int e = tid; e < TM * KW; e += 256) {
+                const int r = e / KW, k = e % KW;
+                const int m = m0 + r;
+                float v = 0.0f;
+                if (m < M) {
+                    const TIn* xr = x + static_cast<size_t>(m) * K + u0 + k;
+                    for (int q = 0; q < c; ++q) {
+                        const uint32_t en = s_src[t * c + q];
+                        const float s = entry_sign(en);
+                        const float xv = load(xr + (en & kOffMask));
+                        v = (q == 0) ? s * xv : fmaf(s, xv, v);
+                    }
+                    if (BF16_SKETCH_AND_OUT) v = round_to_bf16(v);
+                }
+                zs[k][r] = v;
+            }
+            for (int e = tid; e < TN * KW; e += 256) {
+                const int r = e / KW, k = e % KW;
+                float v = 0.0f;
+                if (r < width) v = load(w + static_cast<size_t>(n0 + r) * Kc + t * BK + u0 + k);
+                ws[k][r] = v;
+            }
+            __syncthreads();
+            for (int k = 0; k < KW; ++k) {
+                float a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = zs[k][ty * 4 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[j] = ws[k][tx * 4 + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+            }
+            __syncthreads();
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int cc = tx * 4 + j;
+            if (cc >= width) continue;
+            const size_t o = static_cast<size_t>(m) * N + n0 + cc;
+            if (BF16_SKETCH_AND_OUT)
+                static_cast<uint16_t*>(y)[o] = to_bf16_bits(acc[i][j]);
+            else
+                static_cast<float*>(y)[o] = acc[i][j];
+        }
+    }
+}
+
+// ============================================================= fused kernel
+// Block: 256 threads (4 waves as WM x WN), output tile MT x BN of one group.
+// Stage s covers k' in [s*KS, s*KS + KS), all inside compressed chunk
+// t = s*KS / BK (KS divides BK).  LDS rows are padded by 8 bf16 (16 bytes).
+template <int MT, int BN, int WM, int WN, int KS, int C_T, bool FROM_HASH>
+__global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ w,
+                                                    const int32_t* __restrict__ pi,
+                                                    const int8_t* __restrict__ ps,
+                                                    uint16_t* __restrict__ y, int M, int K, int N,
+                                                    int J, int Jc, int c_rt, int BK, int n_mt) {
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int TMW = MT / WM, TNW = BN / WN;  // wave tile
+    constexpr int FM = TMW / 16, FN = TNW / 16;  // 16x16 MFMA blocks per wave
+    static_assert(FM * 16 == TMW && FN * 16 == TNW, "wave tile must be a multiple of 16");
+    constexpr int LDP = KS + 8;                  // LDS row pitch (elements)
+    constexpr int VPR = KS / 8;                  // 16-byte vectors per tile row
+    constexpr int AV = MT * VPR / 256;           // sketch vectors per thread per stage
+    constexpr int BV = (BN * VPR + 255) / 256;   // weight vectors per thread per stage
+    static_assert(AV * 256 == MT * VPR, "A tile must split evenly");
+    constexpr int CR = (C_T > 0) ? C_T : 1;      // raw sources held per vector
+
+    extern __shared__ uint32_t smem[];
+    uint16_t* As = reinterpret_cast<uint16_t*>(smem);          // [2][MT][LDP]
+    uint16_t* Bs = As + 2 * MT * LDP;                          // [2][BN][LDP]
+    uint32_t* s_src = reinterpret_cast<uint32_t*>(Bs + 2 * BN * LDP);
+    int* s_cnt = reinterpret_cast<int*>(s_src + J);
+
+    const int c = (C_T > 0) ? C_T : c_rt;
+    const int G = N / BN;
+    const int tile = xcd_tile(blockIdx.x, n_mt * G);
+    const int g = tile % G;
+    const int mt = tile / G;
+    stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
+
+    const int m0 = mt * MT;
+    const int n0 = g * BN;
+    const int Kc = Jc * BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nstage = Kc / KS;
+
+    // per-thread load coordinates
+    int a_row[AV], a_col[AV];
+    bool a_ok[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+        const int v = tid + i * 256;
+        a_row[i] = v / VPR;
+        a_col[i] = (v % VPR) * 8;
+        a_ok[i] = (m0 + a_row[i]) < M;
+    }
+    int b_row[BV], b_col[BV];
+    bool b_ok[BV];
+#pragma unroll
+    for (int i = 0; i < BV; ++i) {
+        const int v = tid + i * 256;
+        b_row[i] = v / VPR;
+        b_col[i] = (v % VPR) * 8;
+        b_ok[i] = v < BN * VPR;
+    }
+
+    uint4 araw[AV][CR];
+    float asg[CR];
+    uint4 braw[BV];
+
+    auto issue_loads = [&](int s) {
+        const int k0 = s * KS;
+        const int t = k0 / BK;
+        const int u0 = k0 - t * BK;
+        if constexpr (C_T > 0) {
+#pragma unroll
+            for (int r = 0; r < C_T; ++r) {
+                const uint32_t e = s_src[t * C_T + r];
+                asg[r] = entry_sign(e);
+                const uint16_t* src = x + (e & kOffMask) + u0;
+#pragma unroll
+                for (int i = 0; i < AV; ++i) {
+                    araw[i][r] = a_ok[i] ? *reinterpret_cast<const uint4*>(
+                                               src + static_cast<size_t>(m0 + a_row[i]) * K + a_col[i])
+                                         : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BV; ++i) {
+            braw[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(
+                                    w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i])
+                              : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    auto store_stage = [&](int s, int buf) {
+        uint16_t* A = As + buf * MT * LDP;
+        uint16_t* B = Bs + buf * BN * LDP;
+        if constexpr (C_T == 1) {
+            // one source: the sketch is the chunk itself with its sign bit flipped
+            const uint32_t flip = (asg[0] < 0.0f) ? 0x80008000u : 0u;
+            const uint32_t zero = (asg[0] == 0.0f) ? 0u : 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                uint4 v = araw[i][0];
+                v.x = (v.x ^ flip) & zero;
+                v.y = (v.y ^ flip) & zero;
+                v.z = (v.z ^ flip) & zero;
+                v.w = (v.w ^ flip) & zero;
+                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = v;
+            }
+        } else if constexpr (C_T > 1) {
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                float acc[8];
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) acc_bf16x8(acc, araw[i][r], asg[r], r == 0);
+                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = pack_bf16x8(acc);
+            }
+        } else {
+            // runtime c: read and sum the sources here, one after another
+            const int k0 = s * KS;
+            const int t = k0 / BK;
+            const int u0 = k0 - t * BK;
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                float acc[8];
+                for (int r = 0; r < c; ++r) {
+                    const uint32_t e = s_src[t * c + r];
+                    const uint4 raw = a_ok[i] ? *reinterpret_cast<const uint4*>(
+                                                    x + (e & kOffMask) + u0 +
+                                                    static_cast<size_t>(m0 + a_row[i]) * K + a_col[i])
+                                              : make_uint4(0, 0, 0, 0);
+                    acc_bf16x8(acc, raw, entry_sign(e), r == 0);
+                }
+                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = pack_bf16x8(acc);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < BV; ++i)
+            if (b_ok[i]) *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = braw[i];
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    issue_loads(0);
+    store_stage(0, 0);
+    __syncthreads();
+
+    const int fr = lane & 15;       // row (A) / column (B) inside a 16x16 block
+    const int fk = (lane >> 4) * 8; // first k of this lane's 8
+    for (int s = 0; s < nstage; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nstage) issue_loads(s + 1);
+        const uint16_t* A = As + buf * MT * LDP;
+        const uint16_t* B = Bs + buf * BN * LDP;
+#pragma unroll
+        for (int kk = 0; kk < KS; kk += 32) {
+            bf16x8 af[FM], bfr[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(A + (wm * TMW + i * 16 + fr) * LDP + kk + fk);
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(B + (wn * TNW + j * 16 + fr) * LDP + kk + fk);
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (s + 1 < nstage) store_stage(s + 1, buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds rows 4*(lane/16) + 0..3, column lane % 16 of each block
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * TNW + j * 16 + fr;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + wm * TMW + i * 16 + (lane >> 4) * 4 + q;
+                if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(acc[i][j][q]);
+            }
+        }
+    }
+}
+
+// ============================================================ small-M kernel
+// Block: NW waves, 16 neurons (rows nb*16 .. +15 of group g).  Wave w takes the
+// 32-wide k-steps [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each
+// lane builds 8 sketch values of token (lane % 16) straight from x and loads 8
+// weights of neuron (lane % 16); one 16x16x32 MFMA per step.  Tokens >= M are
+// zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.
+template <int NW, int C_T, bool FROM_HASH>
+__global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w,
+                                                         const int32_t* __restrict__ pi,
+                                                         const int8_t* __restrict__ ps,
+                                                         uint16_t* __restrict__ y, int M, int K,
+                                                         int N, int J, int Jc, int c_rt, int BK,
+                                                         int BN) {
+    extern __shared__ uint32_t smem[];
+    f32x4* red = reinterpret_cast<f32x4*>(smem);                  // [NW][64]
+    uint32_t* s_src = smem + NW * 64 * 4;
+    int* s_cnt = reinterpret_cast<int*>(s_src + J);
+
+    const int c = (C_T > 0) ? C_T : c_rt;
+    const int nblk = BN / 16;
+    const int g = blockIdx.x / nblk;
+    const int nb = blockIdx.x % nblk;
+    stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
+
+    const int Kc = Jc * BK;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int S = Kc / 32;
+    const int s_begin = static_cast<int>(static_cast<long long>(S) * wave / NW);
+    const int s_end = static_cast<int>(static_cast<long long>(S) * (wave + 1) / NW);
+
+    const int tok = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const bool tok_ok = tok < M;
+    const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : 0) * K + kq;
+    const int n = g * BN + nb * 16 + (lane & 15);
+    const uint16_t* wrow = w + static_cast<size_t>(n) * Kc + kq;
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    constexpr int U = 4;  // steps in flight per wave
+    int s = s_begin;
+    for (; s + U <= s_end; s += U) {
+        uint4 wr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) wr[u] = *reinterpret_cast<const uint4*>(wrow + (s + u) * 32);
+        uint4 xr[U][(C_T > 0) ? C_T : 1];
+        float sg[U][(C_T > 0) ? C_T : 1];
+        if constexpr (C_T > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k0 = (s + u) * 32;
+                const int t = k0 / BK;
+                const int u0 = k0 - t * BK;
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) {
+                    const uint32_t e = s_src[t * C_T + r];
+                    sg[u][r] = entry_sign(e);
+                    xr[u][r] = tok_ok ? *reinterpret_cast<const uint4*>(xrow + (e & kOffMask) + u0)
+                                      : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float a[8];
+            if constexpr (C_T > 0) {
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) acc_bf16x8(a, xr[u][r], sg[u][r], r == 0);
+            } else {
+                const int k0 = (s + u) * 32;
+                const int t = k0 / BK;
+                const int u0 = k0 - t * BK;
+                for (int r = 0; r < c; ++r) {
+                    const uint32_t e = s_src[t * c + r];
+                    const uint4 raw = tok_ok ? *reinterpret_cast<const uint4*>(xrow + (e & kOffMask) + u0)
+                                             : make_uint4(0, 0, 0, 0);
+                    acc_bf16x8(a, raw, entry_sign(e), r == 0);
+                }
+            }
+            const uint4 ap = pack_bf16x8(a);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
+                                                          __builtin_bit_cast(bf16x8, wr[u]), acc, 0, 0, 0);
+        }
+    }
+    for (; s < s_end; ++s) {
+        const uint4 wr = *reinterpret_cast<const uint4*>(wrow + s * 32);
+        const int k0 = s * 32;
+        const int t = k0 / BK;
+        const int u0 = k0 - t * BK;
+        float a[8];
+        for (int r = 0; r < c; ++r) {
+            const uint32_t e = s_src[t * c + r];
+            const uint4 raw = tok_ok ? *reinterpret_cast<const uint4*>(xrow + (e & kOffMask) + u0)
+                                     : make_uint4(0, 0, 0, 0);
+            acc_bf16x8(a, raw, entry_sign(e), r == 0);
+        }
+        const uint4 ap = pack_bf16x8(a);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
+                                                      __builtin_bit_cast(bf16x8, wr), acc, 0, 0, 0);
+    }
+
+    red[wave * 64 + lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 sum = red[lane];
+        for (int v = 1; v < NW; ++v) {
+            const f32x4 p = red[v * 64 + lane];
+            sum[0] += p[0];
+            sum[1] += p[1];
+            sum[2] += p[2];
+            sum[3] += p[3];
+        }
+        const int col = g * BN + nb * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = (lane >> 4) * 4 + q;
+            if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(sum[q]);
+        }
+    }
+}
+
+// ================================================================ launchers
+inline ss1_status launch_status() {
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
+inline size_t plan_lds_bytes(const Dims& d) {
+    return static_cast<size_t>(d.J) * 4 + static_cast<size_t>(d.Jc) * 4;
+}
+
+template <bool FROM_HASH>
+ss1_status launch_generic_t(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    int KW = 32;
+    while (d.BK % KW) KW >>= 1;
+    const int n_sub = static_cast<int>((d.BN + 63) / 64);
+    const long long mt = (a.M + 63) / 64;
+    const long long blocks = mt * d.G * n_sub;
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(a.stream);
+    const size_t lds = plan_lds_bytes(d);
+    if (a.dtype == SS1_F32) {
+        hipLaunchKernelGGL((generic_kernel<float, false, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(256), lds, st, static_cast<const float*>(a.x),
+                           static_cast<const float*>(a.w), a.plan_i, a.plan_s, a.y, (int)a.M,
+                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub);
+    } else {
+        hipLaunchKernelGGL((generic_kernel<uint16_t, true, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(256), lds, st, static_cast<const uint16_t*>(a.x),
+                           static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, a.y, (int)a.M,
+                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub);
+    }
+    return launch_status();
+}
+
+template <int MT, int BN, int WM, int WN, int KS, int C_T, bool FROM_HASH>
+ss1_status launch_fused_cfg(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    const int n_mt = static_cast<int>((a.M + MT - 1) / MT);
+    const long long blocks = static_cast<long long>(n_mt) * d.G;
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    constexpr int LDP = KS + 8;
+    const size_t lds = static_cast<size_t>(2) * (MT + BN) * LDP * 2 + plan_lds_bytes(d);
+    if (lds > 64 * 1024) {
+        if (hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&fused_kernel<MT, BN, WM, WN, KS, C_T, FROM_HASH>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+            return SS1_ERR_HIP;
+    }
+    hipLaunchKernelGGL((fused_kernel<MT, BN, WM, WN, KS, C_T, FROM_HASH>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds,
+                       static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s,
+                       static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K, (int)d.N, (int)d.J,
+                       (int)d.Jc, d.c, d.BK, n_mt);
+    return launch_status();
+}
+
+template <int BN, int WM, int WN, int KS, bool FROM_HASH>
+ss1_status launch_fused_c(const ForwardArgs& a) {
+    switch (a.d.c) {
+        case 1: return launch_fused_cfg<128, BN, WM, WN, KS, 1, FROM_HASH>(a);
+        case 2: return launch_fused_cfg<128, BN, WM, WN, KS, 2, FROM_HASH>(a);
+        case 4: return launch_fused_cfg<128, BN, WM, WN, KS, 4, FROM_HASH>(a);
+        case 8: return launch_fused_cfg<128, BN, WM, WN, KS, 8, FROM_HASH>(a);
+        default: return launch_fused_cfg<128, BN, WM, WN, KS, 0, FROM_HASH>(a);
+    }
+}
+
+template <int KS, bool FROM_HASH>
+ss1_status launch_fused_bn(const ForwardArgs& a) {
+    switch (a.d.BN) {
+        case 32: return launch_fused_c<32, 4, 1, KS, FROM_HASH>(a);
+        case 64: return launch_fused_c<64, 2, 2, KS, FROM_HASH>(a);
+        case 128: return launch_fused_c<128, 2, 2, KS, FROM_HASH>(a);
+        default: return SS1_ERR_ALGO;
+    }
+}
+
+template <bool FROM_HASH>
+ss1_status launch_fused_t(const ForwardArgs& a) {
+    if (a.d.BK % 64 == 0) return launch_fused_bn<64, FROM_HASH>(a);
+    return launch_fused_bn<32, FROM_HASH>(a);
+}
+
+template <int C_T, bool FROM_HASH>
+ss1_status launch_smallm_cfg(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    constexpr int NW = 8;
+    const long long blocks = d.G * (d.BN / 16);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    const size_t lds = static_cast<size_t>(NW) * 64 * 16 + plan_lds_bytes(d);
+    hipLaunchKernelGGL((smallm_kernel<NW, C_T, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(NW * 64), lds, static_cast<hipStream_t>(a.stream),
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w),
+                       a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K,
+                       (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN);
+    return launch_status();
+}
+
+template <bool FROM_HASH>
+ss1_status launch_smallm_t(const ForwardArgs& a) {
+    switch (a.d.c) {
+        case 1: return launch_smallm_cfg<1, FROM_HASH>(a);
+        case 2: return launch_smallm_cfg<2, FROM_HASH>(a);
+        case 4: return launch_smallm_cfg<4, FROM_HASH>(a);
+        case 8: return launch_smallm_cfg<8, FROM_HASH>(a);
+        default: return launch_smallm_cfg<0, FROM_HASH>(a);
+    }
+}
+
+}  // namespace
+
+bool fused_supported(const ForwardArgs& a) {
+    return a.dtype == SS1_BF16 && a.d.BK % 32 == 0 &&
+           (a.d.BN == 32 || a.d.BN == 64 || a.d.BN == 128);
+}
+
+bool smallm_supported(const ForwardArgs& a) {
+    return a.dtype == SS1_BF16 && a.M <= 16 && a.d.BK % 32 == 0 && a.d.BN % 16 == 0;
+}
+
+ss1_status launch_generic(const ForwardArgs& a) {
+    return a.form == PlanForm::Hash ? launch_generic_t<true>(a) : launch_generic_t<false>(a);
+}
+
+ss1_status launch_fused(const ForwardArgs& a) {
+    return a.form == PlanForm::Hash ? launch_fused_t<true>(a) : launch_fused_t<false>(a);
+}
+
+ss1_status launch_smallm(const ForwardArgs& a) {
+    return a.form == PlanForm::Hash ? launch_smallm_t<true>(a) : launch_smallm_t<false>(a);
+}
+
+ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i,
+                         const int8_t* plan_s, int64_t M, const Dims& d, void* z,
+                         int32_t z_dtype, void* stream) {
+    const int V = (x_dtype == SS1_BF16) ? 8 : 4;
+    const long long items = M * d.Jc * (d.BK / V);
+    long long per_group = (items + 255) / 256;
+    if (per_group > 4096) per_group = 4096;
+    if (per_group < 1) per_group = 1;
+    if (d.G > 65535) return SS1_ERR_SHAPE;
+    const dim3 grid(static_cast<unsigned>(per_group), static_cast<unsigned>(d.G));
+    const size_t lds = plan_lds_bytes(d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the sketch kernel reads the forward hash
+    if (x_dtype == SS1_BF16 && z_dtype == SS1_BF16)
+        hipLaunchKernelGGL((sketch_kernel<uint16_t, true, true>), grid, dim3(256), lds, st,
+                           static_cast<const uint16_t*>(x), plan_i, plan_s, z, (int)M, (int)d.K,
+                           (int)d.J, (int)d.Jc, d.c, d.BK, (int)d.Kc);
+    else if (x_dtype == SS1_BF16)
+        hipLaunchKernelGGL((sketch_kernel<uint16_t, false, true>), grid, dim3(256), lds, st,
+                           static_cast<const uint16_t*>(x), plan_i, plan_s, z, (int)M, (int)d.K,
+                           (int)d.J, (int)d.Jc, d.c, d.BK, (int)d.Kc);
+    else
+        hipLaunchKernelGGL((sketch_kernel<float, false, true>), grid, dim3(256), lds, st,
+                           static_cast<const float*>(x), plan_i, plan_s, z, (int)M, (int)d.K,
+                           (int)d.J, (int)d.Jc, d.c, d.BK, (int)d.Kc);
+    return launch_status();
+}
+
+}  // namespace ss1

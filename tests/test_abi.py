@@ -1,0 +1,193 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+function ``include/ss1.h`` declares, the C++ plan equals the oracle's plan bit
+for bit, and every argument check returns its status before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import sketched_parameter_sharing_amd as ss1
+from sketched_parameter_sharing_amd import _lib
+from ss1_inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "ss1.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ss1_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(declared) == sorted(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert ss1.version().count(".") == 2
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code in range(8):
+        assert lib.ss1_status_string(code).decode() not in ("", "unknown status")
+    assert lib.ss1_status_string(99).decode() == "unknown status"
+
+
+PLAN_CASES = sorted({(w.plan_seed, w.K, w.N, w.c, w.BK, w.BN) for w in WORKLOADS.values()}) + [
+    (0, 48, 12, 3, 4, 3), (2**64 - 1, 64, 8, 8, 1, 8), (123, 4096, 32, 1, 1, 32),
+    (77, 8 * 4096, 1, 4096, 8, 1),
+]
+
+
+@pytest.mark.parametrize("seed,K,N,c,BK,BN", PLAN_CASES)
+def test_plan_matches_oracle_bit_exact(seed, K, N, c, BK, BN):
+    if c > 64:
+        pytest.skip("beyond the library's c limit")
+    h, s = ss1.plan(seed, K, N, c, BK, BN)
+    ho, so = oracle.plan(seed, K, N, c, BK, BN)
+    assert h.dtype == np.int32 and s.dtype == np.int8
+    assert np.array_equal(h, ho) and np.array_equal(s, so)
+    idx, isg = ss1.plan_index(h, s, K, N, c, BK, BN)
+    io, iso = oracle.plan_index(ho, so, K, N, c, BK, BN)
+    assert np.array_equal(idx, io) and np.array_equal(isg, iso)
+
+
+def test_plan_rejects_bad_chunking():
+    for args in [(256, 256, 2, 30, 32), (256, 256, 3, 32, 32), (256, 250, 2, 32, 32),
+                 (256, 256, 0, 32, 32), (-256, 256, 2, 32, 32), (256, 256, 65, 1, 32)]:
+        with pytest.raises(ss1.SS1Error) as e:
+            ss1.plan(1, *args)
+        assert e.value.status == _lib.ERR_SHAPE
+    with pytest.raises(ss1.SS1Error) as e:  # J = K/BK above the chunk limit
+        ss1.plan(1, 8192, 4, 2, 1, 4)
+    assert e.value.status == _lib.ERR_SHAPE
+    lib = _lib.load()
+    assert lib.ss1_plan(1, 64, 8, 2, 8, 4, None, None) == _lib.ERR_NULL
+
+
+def test_plan_index_rejects_bad_plans():
+    K, N, c, BK, BN = 64, 8, 2, 8, 4
+    h, s = ss1.plan(3, K, N, c, BK, BN)
+    for mutate in (lambda h, s: h.__setitem__((0, 0), 4),        # out of range
+                   lambda h, s: h.__setitem__((0, 0), -1),
+                   lambda h, s: s.__setitem__((1, 2), 0),        # not +-1
+                   lambda h, s: s.__setitem__((1, 2), 2),
+                   lambda h, s: h.__setitem__((1, 0), (h[1, 0] + 1) % 4)):  # unbalanced
+        hh, sh = h.copy(), s.copy()
+        mutate(hh, sh)
+        with pytest.raises(ss1.SS1Error) as e:
+            ss1.plan_index(hh, sh, K, N, c, BK, BN)
+        assert e.value.status == _lib.ERR_PLAN
+    lib = _lib.load()
+    buf = np.zeros(64, dtype=np.int32)
+    assert lib.ss1_plan_index(None, buf.ctypes.data, K, N, c, BK, BN, buf.ctypes.data,
+                              buf.ctypes.data) == _lib.ERR_NULL
+
+
+# ----------------------------------------------- forward / sketch arg checks
+# Fake device addresses: every case below fails a host check, so the library
+# returns before touching them or calling HIP.
+A = 0x10000  # 16-byte aligned
+
+
+def T(rows, cols, dtype=_lib.BF16, data=A, reserved=0):
+    return _lib.Tensor(data, dtype, reserved, rows, cols)
+
+
+def fwd(x, w, y, c=2, BK=64, BN=64, h=A, s=A, algo=None, idx=False):
+    lib = _lib.load()
+    args = [ctypes.byref(x), ctypes.byref(w), h, s, c, BK, BN, ctypes.byref(y)]
+    if algo is None:
+        f = lib.ss1_forward_idx if idx else lib.ss1_forward
+        return f(*args, None)
+    f = lib.ss1_forward_idx_algo if idx else lib.ss1_forward_algo
+    return f(*args, algo, None)
+
+
+FORWARD_ERRORS = [
+    # (description, x, W_c, y, kwargs, expected)
+    ("K % BK", T(8, 770), T(64, 385), T(8, 64), {}, _lib.ERR_SHAPE),
+    ("J % c", T(8, 192), T(64, 64), T(8, 64), {"c": 2}, _lib.ERR_SHAPE),
+    ("N % BN", T(8, 256), T(96, 128), T(8, 96), {}, _lib.ERR_SHAPE),
+    ("W_c cols", T(8, 256), T(64, 256), T(8, 64), {}, _lib.ERR_SHAPE),
+    ("y rows", T(8, 256), T(64, 128), T(9, 64), {}, _lib.ERR_SHAPE),
+    ("y cols", T(8, 256), T(64, 128), T(8, 128), {}, _lib.ERR_SHAPE),
+    ("negative M", T(-1, 256), T(64, 128), T(-1, 64), {}, _lib.ERR_SHAPE),
+    ("bf16 BK % 8", T(8, 256), T(64, 128), T(8, 64), {"BK": 4}, _lib.ERR_SHAPE),
+    ("f32 BK % 4", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32), {"BK": 2}, _lib.ERR_SHAPE),
+    ("c = 0", T(8, 256), T(64, 128), T(8, 64), {"c": 0}, _lib.ERR_SHAPE),
+    ("c > max", T(8, 65 * 64), T(64, 64), T(8, 64), {"c": 65}, _lib.ERR_SHAPE),
+    ("reserved", T(8, 256, reserved=1), T(64, 128), T(8, 64), {}, _lib.ERR_SHAPE),
+    ("dtype mix", T(8, 256, _lib.F32), T(64, 128), T(8, 64), {}, _lib.ERR_DTYPE),
+    ("y dtype", T(8, 256), T(64, 128), T(8, 64, _lib.F32), {}, _lib.ERR_DTYPE),
+    ("bad dtype", T(8, 256, 7), T(64, 128, 7), T(8, 64, 7), {}, _lib.ERR_DTYPE),
+    ("null x data", T(8, 256, data=None), T(64, 128), T(8, 64), {}, _lib.ERR_NULL),
+    ("null y data", T(8, 256), T(64, 128), T(8, 64, data=None), {}, _lib.ERR_NULL),
+    ("null W data", T(8, 256), T(64, 128, data=None), T(8, 64), {}, _lib.ERR_NULL),
+    ("null hash", T(8, 256), T(64, 128), T(8, 64), {"h": None}, _lib.ERR_NULL),
+    ("null sign", T(8, 256), T(64, 128), T(8, 64), {"s": None}, _lib.ERR_NULL),
+    ("x align", T(8, 256, data=A + 2), T(64, 128), T(8, 64), {}, _lib.ERR_ALIGN),
+    ("W align", T(8, 256), T(64, 128, data=A + 8), T(8, 64), {}, _lib.ERR_ALIGN),
+    ("y align", T(8, 256), T(64, 128), T(8, 64, data=A + 4), {}, _lib.ERR_ALIGN),
+    ("hash align", T(8, 256), T(64, 128), T(8, 64), {"h": A + 2}, _lib.ERR_ALIGN),
+    ("algo fused f32", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32),
+     {"algo": _lib.ALGO_FUSED}, _lib.ERR_ALGO),
+    ("algo fused BK", T(8, 256), T(64, 128), T(8, 64), {"BK": 16, "algo": _lib.ALGO_FUSED}, _lib.ERR_ALGO),
+    ("algo fused BN", T(8, 256), T(48, 128), T(8, 48), {"BN": 48, "algo": _lib.ALGO_FUSED}, _lib.ERR_ALGO),
+    ("algo smallm M", T(17, 256), T(64, 128), T(17, 64), {"algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
+    ("algo smallm BN", T(4, 256), T(40, 128), T(4, 40), {"BN": 40, "algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
+    ("algo unknown", T(8, 256), T(64, 128), T(8, 64), {"algo": 9}, _lib.ERR_ALGO),
+]
+
+
+@pytest.mark.parametrize("idx", [False, True])
+@pytest.mark.parametrize("desc,x,w,y,kw,expected", FORWARD_ERRORS, ids=[e[0] for e in FORWARD_ERRORS])
+def test_forward_argument_checks(desc, x, w, y, kw, expected, idx):
+    assert fwd(x, w, y, idx=idx, **kw) == expected
+
+
+def test_forward_null_descriptors():
+    lib = _lib.load()
+    x, w, y = T(8, 256), T(64, 128), T(8, 64)
+    assert lib.ss1_forward(None, ctypes.byref(w), A, A, 2, 64, 64, ctypes.byref(y), None) == _lib.ERR_NULL
+    assert lib.ss1_forward(ctypes.byref(x), None, A, A, 2, 64, 64, ctypes.byref(y), None) == _lib.ERR_NULL
+    assert lib.ss1_forward(ctypes.byref(x), ctypes.byref(w), A, A, 2, 64, 64, None, None) == _lib.ERR_NULL
+
+
+def test_forward_m0_is_a_noop_without_hip():
+    # M = 0 returns before any HIP call, even with null x / y data
+    for algo in (None, _lib.ALGO_AUTO, _lib.ALGO_FUSED, _lib.ALGO_SMALLM, _lib.ALGO_GENERIC):
+        assert fwd(T(0, 256, data=None), T(64, 128), T(0, 64, data=None), algo=algo) == _lib.OK
+
+
+def _sk(x, z, c=2, BK=64, BN=64, N=128, h=A, s=A):
+    return _lib.load().ss1_sketch(ctypes.byref(x), h, s, c, BK, BN, N, ctypes.byref(z), None)
+
+
+def test_sketch_argument_checks():
+    assert _sk(T(8, 256), T(15, 128)) == _lib.ERR_SHAPE            # z rows != G*M
+    assert _sk(T(8, 256), T(16, 64)) == _lib.ERR_SHAPE             # z cols != K/c
+    assert _sk(T(8, 250), T(16, 125)) == _lib.ERR_SHAPE            # K % BK
+    assert _sk(T(8, 256, _lib.F32), T(16, 128, _lib.BF16)) == _lib.ERR_DTYPE
+    assert _sk(T(8, 256, 5), T(16, 128)) == _lib.ERR_DTYPE
+    assert _sk(T(8, 256), T(16, 128), h=None) == _lib.ERR_NULL
+    assert _sk(T(8, 256, data=A + 2), T(16, 128)) == _lib.ERR_ALIGN
+    assert _sk(T(8, 256), T(16, 128), h=A + 1) == _lib.ERR_ALIGN
+    assert _sk(T(0, 256, data=None), T(0, 128, data=None)) == _lib.OK
+    lib = _lib.load()
+    assert lib.ss1_sketch(None, A, A, 2, 64, 64, 128, None, None) == _lib.ERR_NULL
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)
+    w = torch.zeros(64, 128, dtype=torch.bfloat16)
+    h = torch.zeros(1, 4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        ss1.forward(x, w, h, h.to(torch.int8), 2, 64, 64)

@@ -1,0 +1,281 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Plans: the library's ``ss1_plan`` output goes to the GPU, the oracle builds
+its own plan from the same seed (the two are checked equal on the CPU).
+
+Bars (written in each test):
+* float32 layers: max|y - y_ref| / max|y_ref| <= 1e-5 (y_ref float64 oracle).
+* bf16 layers: max|y - y_ref| / max|y_ref| <= 2e-2, and elementwise against
+  the oracle's mirror (float32 sketch rounded to bf16, float64 contraction):
+  |y - y_mirror| <= 2^-7 |y_mirror| + 1e-5 max|y_mirror| (one bf16 ulp plus
+  float32 accumulation-order slack).
+* integer-valued inputs: every intermediate is an exact integer, so float32
+  output equals the oracle exactly and bf16 output equals the oracle rounded to
+  bf16 (nearest, ties to even) bit for bit.
+* standalone sketch: bit-exact against the oracle's float32 mirror sketch.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sketched_parameter_sharing_amd as ss1
+from ss1_inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ss1.load()
+
+
+# ------------------------------------------------------------------ helpers
+def dev(t, wl_dtype):
+    """Host inputs -> device tensor of the layer's dtype."""
+    if wl_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t, dtype=np.float32)).cuda()
+
+
+def host(y):
+    """Device output -> float64 numpy (bf16 decoded exactly)."""
+    if y.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return y.cpu().numpy().astype(np.float64)
+
+
+def bits(y):
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def device_plan(wl):
+    return ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+
+
+def oracle_plan(wl):
+    return oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+
+
+def run(wl, inp, plan, algo="auto", use_index=False, rows=None):
+    xs = inp.x_bits if wl.dtype == "bf16" else inp.x
+    ws = inp.w_bits if wl.dtype == "bf16" else inp.w
+    x = dev(xs, wl.dtype)
+    w = dev(ws, wl.dtype)
+    y = plan.forward(x, w, algo=algo, use_index=use_index)
+    torch.cuda.synchronize()
+    return y
+
+
+def rel_err(y, ref):
+    scale = np.max(np.abs(ref)) if ref.size else 1.0
+    return float(np.max(np.abs(y - ref)) / scale) if ref.size else 0.0
+
+
+def check_bf16(wl, inp, y, rows=None):
+    """Tolerance gate against the float64 oracle plus the mirror check, on all
+    rows or on the given sample of rows."""
+    h, s = oracle_plan(wl)
+    x = inp.x if rows is None else inp.x[rows]
+    yg = host(y) if rows is None else host(y)[rows]
+    ref = oracle.forward(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    err = rel_err(yg, ref)
+    assert err <= TOL_BF16, f"{wl.name}: normwise error {err:.3e} > {TOL_BF16}"
+    mir = oracle.forward_mirror(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, sketch_bf16=True)
+    bound = 2.0 ** -7 * np.abs(mir) + 1e-5 * np.max(np.abs(mir))
+    bad = np.abs(yg - mir) > bound
+    assert not bad.any(), f"{wl.name}: {int(bad.sum())} outputs off the mirror oracle by more than one bf16 ulp"
+    return err
+
+
+# ------------------------------------------------------------ float32 path
+def test_tiny_fp32_parity():
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl))
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    yh = host(y)
+    assert rel_err(yh, ref) <= TOL_F32
+    big = np.abs(ref) >= 1e-2 * np.max(np.abs(ref))
+    assert np.max(np.abs(yh - ref)[big] / np.abs(ref)[big]) <= 1e-4
+
+
+def test_tiny_fp32_identity_plan_is_dense():
+    # c = 1 with the identity plan must be the dense layer y = x W^T
+    wl = WORKLOADS["tiny"]
+    M, K, N, BK, BN = wl.M, wl.K, wl.N, wl.BK, wl.BN
+    rng = np.random.Generator(np.random.PCG64(wl.x_seed))
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    W = rng.uniform(-1 / 16, 1 / 16, size=(N, K)).astype(np.float32)
+    G, J = N // BN, K // BK
+    h = torch.arange(J, dtype=torch.int32).repeat(G, 1).contiguous().cuda()
+    s = torch.ones((G, J), dtype=torch.int8).cuda()
+    y = ss1.forward(dev(x, "f32"), dev(W, "f32"), h, s, 1, BK, BN)
+    torch.cuda.synchronize()
+    ref = x.astype(np.float64) @ W.astype(np.float64).T
+    assert rel_err(host(y), ref) <= TOL_F32
+
+
+def test_tiny_fp32_integer_exact():
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl))
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(host(y), ref)
+
+
+# --------------------------------------------------------------- bf16 path
+BF16_NAMES = ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m4096", "llama_down_m4096"] + [
+    f"square_c{c}_bn{bn}" for c in (1, 2, 4, 8) for bn in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("name", BF16_NAMES)
+@pytest.mark.parametrize("algo", ["auto", "generic"])
+def test_bf16_reduced_m(name, algo):
+    # M = 300: two full 128-row tiles and a ragged tail
+    wl = WORKLOADS[name].with_m(300)
+    if algo == "generic" and wl.N * wl.K > 4096 * 4096:
+        pytest.skip("generic kernel checked on the smaller layers")
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo=algo)
+    print(f"{name} algo={algo} err={check_bf16(wl, inp, y):.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", BF16_NAMES + ["llama_gateup_m16", "llama_down_m16",
+                                               "llama_gateup_m1", "llama_down_m1"])
+def test_bf16_full_size_sampled_rows(name):
+    wl = WORKLOADS[name]
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl))
+    rng = np.random.Generator(np.random.PCG64(99))
+    if wl.M <= 64:
+        rows = np.arange(wl.M)
+    else:
+        rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, 62, replace=False)]))
+    assert np.isfinite(host(y)).all()
+    print(f"{name} full M={wl.M} err={check_bf16(wl, inp, y, rows):.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("gpt2l_down", "fused"),
+                                       ("llama_gateup_m16", "smallm"), ("llama_down_m16", "smallm"),
+                                       ("square_c8_bn128", "fused"), ("square_c1_bn32", "fused"),
+                                       ("gpt2l_up", "generic")])
+def test_bf16_integer_bit_exact(name, algo):
+    wl = WORKLOADS[name]
+    wl = wl.with_m(min(wl.M, 300 if algo != "smallm" else 16))
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl), algo=algo)
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.max(np.abs(ref)) < 2 ** 24
+    expect = f32_to_bf16_bits(ref.astype(np.float32))
+    assert np.array_equal(bits(y), expect)
+
+
+@pytest.mark.parametrize("name", ["llama_gateup_m16", "llama_down_m16"])
+@pytest.mark.parametrize("M", [1, 2, 5, 16])
+def test_smallm_parity(name, M):
+    wl = WORKLOADS[name].with_m(M)
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="smallm")
+    check_bf16(wl, inp, y)
+    ya = run(wl, inp, p)  # auto picks the same kernel at M <= 16
+    assert torch.equal(y, ya)
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [
+    (200, 384, 128, 3, 64, 64),     # runtime c on the fused kernel
+    (130, 640, 256, 5, 64, 128),
+    (77, 1920, 96, 3, 32, 32),
+    (9, 2048, 64, 2, 32, 16),       # smallm with BN = 16
+    (33, 240, 96, 2, 24, 48),       # generic: BK % 32 != 0, BN not 32/64/128
+    (65, 160, 30, 5, 8, 3),
+    (1, 64, 8, 8, 8, 8),
+    (129, 512, 64, 1, 32, 64),
+])
+def test_bf16_odd_shapes(M, K, N, c, BK, BN):
+    wl = Workload("odd", 9, 0, M, K, N, c, BK, BN, "bf16")
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    ys = {}
+    for algo in ("auto", "fused", "smallm", "generic"):
+        try:
+            ys[algo] = run(wl, inp, p, algo=algo)
+        except ss1.SS1Error as e:
+            assert e.status == 7  # kernel not applicable to this shape
+            continue
+        check_bf16(wl, inp, ys[algo])
+    assert "auto" in ys and "generic" in ys
+
+
+@pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("llama_down_m16", "smallm"),
+                                       ("gpt2l_up", "generic"), ("tiny", "generic")])
+def test_hash_and_index_forms_agree(name, algo):
+    wl = WORKLOADS[name]
+    wl = wl.with_m(min(wl.M, 256))
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y1 = run(wl, inp, p, algo=algo)
+    y2 = run(wl, inp, p, algo=algo, use_index=True)
+    y3 = run(wl, inp, p, algo=algo)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)  # same bits, run to run
+
+
+def test_m0_is_noop_and_y_fully_written():
+    wl = WORKLOADS["gpt2s_up"]
+    p = device_plan(wl)
+    x = torch.empty((0, wl.K), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((wl.N, wl.Kc), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((0, wl.N), dtype=torch.bfloat16, device="cuda")
+    ss1.forward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, y)
+    # every output is written: start from NaN
+    wl2 = wl.with_m(131)
+    inp = make_inputs(wl2)
+    for algo in ("fused", "generic"):
+        y = torch.full((131, wl.N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        p.forward(dev(inp.x_bits, "bf16"), dev(inp.w_bits, "bf16"), y=y, algo=algo)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+
+
+def test_runs_on_a_side_stream():
+    wl = WORKLOADS["gpt2s_up"].with_m(256)
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    x, w = dev(inp.x_bits, "bf16"), dev(inp.w_bits, "bf16")
+    ref = p.forward(x, w)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        y = p.forward(x, w)
+    s.synchronize()
+    assert torch.equal(ref, y)
+
+
+# ----------------------------------------------------------- sketch kernel
+@pytest.mark.parametrize("name,M", [("gpt2s_up", 40), ("gpt2l_down", 17), ("llama_down_m16", 3),
+                                    ("square_c8_bn64", 5), ("tiny", 64)])
+def test_sketch_bit_exact(name, M):
+    wl = WORKLOADS[name].with_m(M)
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    h, s = oracle_plan(wl)
+    xs = inp.x_bits if wl.dtype == "bf16" else inp.x
+    x = dev(xs, wl.dtype)
+    z32 = ss1.sketch(x, p.hash, p.sign, wl.c, wl.BK, wl.BN, wl.N)
+    torch.cuda.synchronize()
+    ref32 = oracle.sketch_rounded(inp.x, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, to_bf16=False)
+    assert np.array_equal(host(z32).reshape(ref32.shape), ref32)
+    if wl.dtype == "bf16":
+        zb = ss1.sketch(x, p.hash, p.sign, wl.c, wl.BK, wl.BN, wl.N, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        refb = oracle.sketch_rounded(inp.x, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, to_bf16=True)
+        assert np.array_equal(host(zb).reshape(refb.shape), refb)
