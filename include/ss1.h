@@ -69,7 +69,8 @@ typedef enum {
     SS1_ALGO_AUTO = 0,     /* what ss1_forward picks                                  */
     SS1_ALGO_FUSED = 1,    /* bf16: sketch tile built in LDS, then MFMA (M of any size) */
     SS1_ALGO_SMALLM = 2,   /* bf16: decode shapes, M <= 16, W_c streamed once          */
-    SS1_ALGO_GENERIC = 3   /* any dtype and chunking: LDS-tiled FMA kernel             */
+    SS1_ALGO_GENERIC = 3,  /* any dtype and chunking: LDS-tiled FMA kernel             */
+    SS1_ALGO_BAND = 4      /* bf16, short rows: a band of input rows held in LDS        */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */
@@ -162,6 +163,8 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *   FUSED  : BF16, BK % 32 == 0, BN in {32, 64, 128}
  *   SMALLM : BF16, M <= 16, BK % 32 == 0, BN % 16 == 0
  *   GENERIC: any valid call
+ *   BAND   : BF16, BK % 32 == 0, BN in {32, 64, 128}, and 32 input rows of K
+ *            bf16 (plus the plan) fit in one block's LDS (K up to about 2400)
  */
 ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
                             const int32_t* hash, const int8_t* sign,

@@ -14,15 +14,17 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libss1.so")
+# the in-tree build; SS1_LIBRARY may name another build of the same ABI
+LIB_PATH = os.environ.get("SS1_LIBRARY") or os.path.join(HERE, "libss1.so")
 
 # status codes (ss1_status)
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = range(8)
 # dtypes (ss1_dtype)
 F32, BF16 = 0, 1
 # kernel choice (ss1_algo)
-ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC = range(4)
-ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC}
+ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND = range(5)
+ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC,
+         "band": ALGO_BAND}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_sketch")

@@ -68,6 +68,7 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_AUTO:
             if (a.M == 0) return SS1_OK;
             if (ss1::smallm_supported(a)) return ss1::launch_smallm(a);
+            if (ss1::band_supported(a, 48)) return ss1::launch_band(a);
             if (ss1::fused_supported(a)) return ss1::launch_fused(a);
             return ss1::launch_generic(a);
         case SS1_ALGO_FUSED:
@@ -76,6 +77,9 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_SMALLM:
             if (!ss1::smallm_supported(a)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_smallm(a);
+        case SS1_ALGO_BAND:
+            if (!ss1::band_supported(a, 32)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_band(a);
         case SS1_ALGO_GENERIC:
             return a.M == 0 ? SS1_OK : ss1::launch_generic(a);
         default:

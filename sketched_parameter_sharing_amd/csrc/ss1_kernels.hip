@@ -32,6 +32,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ss1_internal.h"
 
 namespace ss1 {
@@ -147,6 +149,91 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&acc)[8]) {
     r.z = pack_bf16(acc[4], acc[5]);
     r.w = pack_bf16(acc[6], acc[7]);
     return r;
+}
+
+// Sketch of 8 consecutive elements from one more signed source.  The first
+// source is exact in float32: its sign goes onto the bf16 sign bits (sgnx,
+// 0x80008000 or 0) and the halves are widened.  Each further source is added
+// with the bf16 dot-product instruction: dot2(w, (s, 0), acc) adds s * w.lo to
+// acc and dot2(w, (0, s), acc) adds s * w.hi, each with one float32 rounding,
+// so the sources are summed one after another in float32 exactly as a plain
+// signed add would.  sgn is the bf16 pattern of the sign (+1, -1, or 0 for a
+// source a malformed plan leaves absent).
+__device__ __forceinline__ void acc_dot2x8(float (&acc)[8], const uint4& raw, uint32_t sgn, uint32_t sgnx,
+                                           bool first) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const bf16x2 slo = __builtin_bit_cast(bf16x2, sgn);
+    const bf16x2 shi = __builtin_bit_cast(bf16x2, sgn << 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (first) {
+            const uint32_t v = w[i] ^ sgnx;
+            acc[2 * i] = bf16_lo(v);
+            acc[2 * i + 1] = bf16_hi(v);
+        } else {
+            const bf16x2 v = __builtin_bit_cast(bf16x2, w[i]);
+            acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(v, slo, acc[2 * i], false);
+            acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, shi, acc[2 * i + 1], false);
+        }
+    }
+}
+
+// Sign of a plan entry as a mask on a pair of bf16 values.
+__device__ __forceinline__ uint32_t entry_sign_xor(uint32_t e) {
+    return (e & kNeg) ? 0x80008000u : 0u;
+}
+
+// bf16 pattern of a plan entry's sign: 0x3F80 (+1), 0xBF80 (-1), 0 (absent).
+__device__ __forceinline__ uint32_t entry_sign_bf16(uint32_t e) {
+    return (e & kAbsent) ? 0u : ((e & kNeg) ? 0xBF80u : 0x3F80u);
+}
+
+// Plans of `count` consecutive groups starting at g0, one J-entry row per
+// group in s_src (same encoding as stage_plan).  s_cnt needs count*Jc ints in
+// the forward form.  Ends with a barrier.
+template <bool FROM_HASH>
+__device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g0,
+                            int count, int J, int Jc, int c, int BK, uint32_t* s_src, int* s_cnt) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int total = count * J;
+    const int32_t* gi = pi + static_cast<size_t>(g0) * J;
+    const int8_t* gs = ps + static_cast<size_t>(g0) * J;
+    if (FROM_HASH) {
+        for (int e = tid; e < total; e += nt) s_src[e] = kAbsent;
+        for (int e = tid; e < count * Jc; e += nt) s_cnt[e] = 0;
+        __syncthreads();
+        for (int e = tid; e < total; e += nt) {
+            const int gl = e / J;
+            const int j = e - gl * J;
+            const int t = gi[e];
+            const int s = gs[e];
+            if (t >= 0 && t < Jc && (s == 1 || s == -1)) {
+                const int slot = atomicAdd(&s_cnt[gl * Jc + t], 1);
+                if (slot < c) s_src[gl * J + t * c + slot] = make_entry(j, BK, s);
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < count * Jc; e += nt) {
+            uint32_t* p = s_src + e * c;  // (gl, t) -> row gl*J + t*c
+            for (int a = 1; a < c; ++a) {
+                const uint32_t v = p[a];
+                int b = a - 1;
+                while (b >= 0 && (p[b] & ~kNeg) > (v & ~kNeg)) {
+                    p[b + 1] = p[b];
+                    --b;
+                }
+                p[b + 1] = v;
+            }
+        }
+    } else {
+        for (int e = tid; e < total; e += nt) {
+            const int j = gi[e];
+            const int s = gs[e];
+            s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
+        }
+    }
+    __syncthreads();
 }
 
 // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
@@ -628,6 +715,189 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
     }
 }
 
+// ============================================================== band kernel
+// For layers whose input rows are short enough that a band of MT rows fits in
+// LDS (MT*K bf16).  Block: NW waves; it loads input rows [m0, m0+MT) once and
+// then each wave takes whole groups of the block's group range, one after
+// another, with no further barrier.  Per 32-wide k-step a wave loads its
+// group's W_c slice from global memory and, for each 16-row block of the band,
+// reads the c source chunks from the band, sums them in float32 with bf16
+// dot-product instructions, rounds the sketch to bf16 and feeds it to one MFMA
+// per 16 neurons.  The steps run as a two-stage software pipeline: the plan
+// entries, band reads and W_c loads of step s+1 are issued before the
+// arithmetic of step s, so LDS and L2 latency overlap with the math.
+// The MFMA computes the transposed tile y^T = W_c * z^T so that each lane ends
+// up with 4*BN/16 consecutive outputs of one row (W_c rows are loaded in the
+// matching permuted order) and stores them as 16-byte vectors.
+template <int MT, int BN, int C_T, int NW, bool FROM_HASH>
+__global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ w,
+                                                       const int32_t* __restrict__ pi,
+                                                       const int8_t* __restrict__ ps,
+                                                       uint16_t* __restrict__ y, int M, int K, int N,
+                                                       int J, int Jc, int c_rt, int BK, int gsplit) {
+    constexpr int RB = MT / 16;  // 16-row blocks of the band
+    constexpr int NB = BN / 16;  // 16-neuron blocks of a group
+    static_assert(RB * 16 == MT && NB * 16 == BN && NB % 2 == 0, "tile sizes");
+    constexpr int CR = (C_T > 0) ? C_T : 1;
+    extern __shared__ uint32_t smem[];
+    const int LDK = K + 8;  // band row pitch (elements): 16-byte skew between rows
+    uint16_t* band = reinterpret_cast<uint16_t*>(smem);
+    uint32_t* s_src = smem + (MT * LDK) / 2;
+
+    const int c = (C_T > 0) ? C_T : c_rt;
+    const int G = N / BN;
+    const int bi = blockIdx.x / gsplit;
+    const int gs = blockIdx.x - bi * gsplit;
+    const int g0 = static_cast<int>(static_cast<long long>(G) * gs / gsplit);
+    const int g1 = static_cast<int>(static_cast<long long>(G) * (gs + 1) / gsplit);
+    const int GW = g1 - g0;
+    int* s_cnt = reinterpret_cast<int*>(s_src + GW * J);
+    const int m0 = bi * MT;
+
+    // band of input rows, zero rows past M; eight 16-byte loads in flight per
+    // thread before their LDS stores
+    {
+        constexpr int U = 8;
+        const int vpr = K / 8;
+        const int total = MT * vpr;
+        for (int v0 = threadIdx.x; v0 < total; v0 += U * NW * 64) {
+            uint4 val[U];
+            int dst[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * NW * 64;
+                const int r = v / vpr;
+                const int col = (v - r * vpr) * 8;
+                dst[u] = (v < total) ? r * LDK + col : -1;
+                val[u] = make_uint4(0, 0, 0, 0);
+                if (v < total && m0 + r < M)
+                    val[u] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m0 + r) * K + col);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (dst[u] >= 0) *reinterpret_cast<uint4*>(band + dst[u]) = val[u];
+        }
+    }
+    stage_plans<FROM_HASH>(pi, ps, g0, GW, J, Jc, c, BK, s_src, s_cnt);  // ends with a barrier
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;          // MFMA row/column index of this lane
+    const int q = lane >> 4;           // which 8 of the 32 k of a step, and output quarter
+    const int Kc = Jc * BK;
+    const int steps = Kc / 32;
+    // W_c row loaded by this lane for neuron block nb: MFMA row li of block nb
+    // is neuron (li/4)*4*NB + nb*4 + li%4 of the group.
+    int wrow[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) wrow[nb] = (li >> 2) * 4 * NB + nb * 4 + (li & 3);
+    const uint16_t* lrow = band + li * LDK + q * 8;  // this lane's band row (block 0) and k offset
+
+    for (int gl = wave; gl < GW; gl += NW) {
+        const int g = g0 + gl;
+        const uint32_t* plan = s_src + gl * J;
+        const uint16_t* wg = w + static_cast<size_t>(g) * BN * Kc + q * 8;
+        f32x4 acc[RB][NB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        if constexpr (C_T > 0) {
+            // operands of one step: band reads, their signs, and the W_c slice
+            struct Stage {
+                uint4 raw[RB][CR];
+                uint32_t sg[CR];
+                uint32_t sx[CR];
+                uint4 wf[NB];
+            };
+            auto load = [&](int s, Stage& st) {
+                const int k0 = s * 32;
+                const int t = k0 / BK;
+                const int ub = k0 - t * BK;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    st.wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) {
+                    const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * C_T + r]);
+                    st.sg[r] = entry_sign_bf16(e);
+                    st.sx[r] = entry_sign_xor(e);
+                    const uint16_t* src = lrow + (e & kOffMask) + ub;
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        st.raw[rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK);
+                }
+            };
+            auto compute = [&](const Stage& st) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float a[8];
+#pragma unroll
+                    for (int r = 0; r < C_T; ++r) acc_dot2x8(a, st.raw[rb][r], st.sg[r], st.sx[r], r == 0);
+                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, st.wf[nb]), zf, acc[rb][nb], 0, 0, 0);
+                }
+            };
+            Stage sa, sb;
+            load(0, sa);
+            int s = 0;
+            for (; s + 2 <= steps; s += 2) {
+                load(s + 1, sb);
+                compute(sa);
+                if (s + 2 < steps) load(s + 2, sa);
+                compute(sb);
+            }
+            if (s < steps) compute(sa);
+        } else {
+            // runtime c: no pipelining
+            for (int s = 0; s < steps; ++s) {
+                const int k0 = s * 32;
+                const int t = k0 / BK;
+                const int ub = k0 - t * BK;
+                uint4 wf[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float a[8];
+                    for (int r = 0; r < c; ++r) {
+                        const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * c + r]);
+                        const uint4 raw = *reinterpret_cast<const uint4*>(lrow + rb * 16 * LDK + (e & kOffMask) + ub);
+                        acc_dot2x8(a, raw, entry_sign_bf16(e), entry_sign_xor(e), r == 0);
+                    }
+                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wf[nb]), zf, acc[rb][nb], 0, 0, 0);
+                }
+            }
+        }
+        // lane holds y[m0 + rb*16 + li][g*BN + q*4*NB + nb*4 + i]
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int m = m0 + rb * 16 + li;
+            if (m >= M) continue;
+            uint16_t* yr = y + static_cast<size_t>(m) * N + static_cast<size_t>(g) * BN + q * 4 * NB;
+#pragma unroll
+            for (int h = 0; h < NB / 2; ++h) {
+                uint4 o;
+                o.x = pack_bf16(acc[rb][2 * h][0], acc[rb][2 * h][1]);
+                o.y = pack_bf16(acc[rb][2 * h][2], acc[rb][2 * h][3]);
+                o.z = pack_bf16(acc[rb][2 * h + 1][0], acc[rb][2 * h + 1][1]);
+                o.w = pack_bf16(acc[rb][2 * h + 1][2], acc[rb][2 * h + 1][3]);
+                *reinterpret_cast<uint4*>(yr + h * 8) = o;
+            }
+        }
+    }
+}
+
 // ================================================================ launchers
 inline ss1_status launch_status() {
     return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
@@ -737,7 +1007,117 @@ ss1_status launch_smallm_t(const ForwardArgs& a) {
     }
 }
 
+// ------------------------------------------------------------ band launch
+struct DeviceInfo {
+    int cus;
+    int lds_per_block;
+};
+
+// Compute units and the largest LDS a block may take on the current device.
+inline DeviceInfo device_info() {
+    int dev = 0;
+    DeviceInfo di{256, 64 * 1024};
+    if (hipGetDevice(&dev) != hipSuccess) return di;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) di.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+        di.lds_per_block = v;
+    return di;
+}
+
+struct BandCfg {
+    int MT;      // rows per band, 0 when the layer does not fit
+    int gsplit;  // blocks per band, each taking a contiguous range of groups
+    size_t lds;
+};
+
+inline size_t band_lds(int MT, const Dims& d, int gsplit) {
+    const long long gw = (d.G + gsplit - 1) / gsplit;
+    return static_cast<size_t>(MT) * (d.K + 8) * 2 + static_cast<size_t>(gw) * (d.J + d.Jc) * 4;
+}
+
+// Largest band (64, 48 or 32 rows) that fits in LDS, and the group split that
+// gives every compute unit work while the group plans still fit.
+inline BandCfg band_config(const Dims& d, int64_t M, const DeviceInfo& di) {
+    for (int MT : {64, 48, 32}) {
+        const long long nbands = (M + MT - 1) / MT;
+        const size_t band_bytes = static_cast<size_t>(MT) * (d.K + 8) * 2;
+        if (band_bytes + static_cast<size_t>(d.J + d.Jc) * 4 > static_cast<size_t>(di.lds_per_block)) continue;
+        const long long per_cu = std::max<long long>(1, di.lds_per_block / static_cast<long long>(band_bytes + 1024));
+        long long gsplit = (static_cast<long long>(di.cus) * per_cu + nbands - 1) / nbands;
+        gsplit = std::max<long long>(1, std::min<long long>(gsplit, d.G));
+        while (gsplit < d.G && band_lds(MT, d, static_cast<int>(gsplit)) > static_cast<size_t>(di.lds_per_block))
+            ++gsplit;
+        if (band_lds(MT, d, static_cast<int>(gsplit)) > static_cast<size_t>(di.lds_per_block)) continue;
+        if (nbands * gsplit > 0x7FFFFFFFLL) continue;
+        return BandCfg{MT, static_cast<int>(gsplit), band_lds(MT, d, static_cast<int>(gsplit))};
+    }
+    return BandCfg{0, 0, 0};
+}
+
+template <int MT, int BN, int C_T, bool FROM_HASH>
+ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
+    const Dims& d = a.d;
+    // two waves per SIMD leave a lane 256 registers; the tiles whose two
+    // pipeline stages and accumulators need more run one wave per SIMD
+    constexpr int NW = (BN == 128 || C_T >= 8 || (C_T == 4 && MT == 64)) ? 4 : 8;
+    const long long nbands = (a.M + MT - 1) / MT;
+    auto kern = &band_kernel<MT, BN, C_T, NW, FROM_HASH>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(cfg.lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((band_kernel<MT, BN, C_T, NW, FROM_HASH>), dim3(static_cast<unsigned>(nbands * cfg.gsplit)),
+                       dim3(NW * 64), cfg.lds, static_cast<hipStream_t>(a.stream),
+                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.plan_i,
+                       a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K, (int)d.N, (int)d.J,
+                       (int)d.Jc, d.c, d.BK, cfg.gsplit);
+    return launch_status();
+}
+
+template <int MT, int BN, bool FROM_HASH>
+ss1_status launch_band_c(const ForwardArgs& a, const BandCfg& cfg) {
+    switch (a.d.c) {
+        case 1: return launch_band_cfg<MT, BN, 1, FROM_HASH>(a, cfg);
+        case 2: return launch_band_cfg<MT, BN, 2, FROM_HASH>(a, cfg);
+        case 4: return launch_band_cfg<MT, BN, 4, FROM_HASH>(a, cfg);
+        case 8: return launch_band_cfg<MT, BN, 8, FROM_HASH>(a, cfg);
+        default: return launch_band_cfg<MT, BN, 0, FROM_HASH>(a, cfg);
+    }
+}
+
+template <int MT, bool FROM_HASH>
+ss1_status launch_band_bn(const ForwardArgs& a, const BandCfg& cfg) {
+    switch (a.d.BN) {
+        case 32: return launch_band_c<MT, 32, FROM_HASH>(a, cfg);
+        case 64: return launch_band_c<MT, 64, FROM_HASH>(a, cfg);
+        case 128: return launch_band_c<MT, 128, FROM_HASH>(a, cfg);
+        default: return SS1_ERR_ALGO;
+    }
+}
+
+template <bool FROM_HASH>
+ss1_status launch_band_t(const ForwardArgs& a) {
+    const BandCfg cfg = band_config(a.d, a.M, device_info());
+    switch (cfg.MT) {
+        case 64: return launch_band_bn<64, FROM_HASH>(a, cfg);
+        case 48: return launch_band_bn<48, FROM_HASH>(a, cfg);
+        case 32: return launch_band_bn<32, FROM_HASH>(a, cfg);
+        default: return SS1_ERR_ALGO;
+    }
+}
+
 }  // namespace
+
+bool band_supported(const ForwardArgs& a, int min_rows) {
+    if (!(a.dtype == SS1_BF16 && a.d.BK % 32 == 0 && (a.d.BN == 32 || a.d.BN == 64 || a.d.BN == 128)))
+        return false;
+    const BandCfg cfg = band_config(a.d, a.M > 0 ? a.M : 1, device_info());
+    return cfg.MT >= min_rows;
+}
+
+ss1_status launch_band(const ForwardArgs& a) {
+    return a.form == PlanForm::Hash ? launch_band_t<true>(a) : launch_band_t<false>(a);
+}
 
 bool fused_supported(const ForwardArgs& a) {
     return a.dtype == SS1_BF16 && a.d.BK % 32 == 0 &&
