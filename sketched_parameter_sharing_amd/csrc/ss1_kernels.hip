@@ -151,19 +151,17 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&acc)[8]) {
     return r;
 }
 
-// Sketch of 8 consecutive elements from one more signed source.  The first
-// source is exact in float32: its sign goes onto the bf16 sign bits (sgnx,
-// 0x80008000 or 0) and the halves are widened.  Each further source is added
-// with the bf16 dot-product instruction: dot2(w, (s, 0), acc) adds s * w.lo to
-// acc and dot2(w, (0, s), acc) adds s * w.hi, each with one float32 rounding,
-// so the sources are summed one after another in float32 exactly as a plain
-// signed add would.  sgn is the bf16 pattern of the sign (+1, -1, or 0 for a
-// source a malformed plan leaves absent).
-__device__ __forceinline__ void acc_dot2x8(float (&acc)[8], const uint4& raw, uint32_t sgn, uint32_t sgnx,
-                                           bool first) {
+// Sketch of 8 consecutive elements from one more signed source, in float32.
+// The first source is exact: its sign goes onto the bf16 sign bits (sgnx,
+// 0x80008000 or 0) before the halves are widened.  Each further source is
+// widened and added with a fused multiply-add by its sign (+-1.0, or 0 for a
+// source a malformed plan leaves absent), one float32 rounding per add, in
+// source order.  On gfx950 these integer and FMA instructions issue alongside
+// the MFMAs of other waves; the bf16 dot-product instructions do not, which is
+// why they are not used here.
+__device__ __forceinline__ void acc_sign8(float (&acc)[8], const uint4& raw, float sgn, uint32_t sgnx,
+                                          bool first) {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    const bf16x2 slo = __builtin_bit_cast(bf16x2, sgn);
-    const bf16x2 shi = __builtin_bit_cast(bf16x2, sgn << 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if (first) {
@@ -171,9 +169,8 @@ __device__ __forceinline__ void acc_dot2x8(float (&acc)[8], const uint4& raw, ui
             acc[2 * i] = bf16_lo(v);
             acc[2 * i + 1] = bf16_hi(v);
         } else {
-            const bf16x2 v = __builtin_bit_cast(bf16x2, w[i]);
-            acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(v, slo, acc[2 * i], false);
-            acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, shi, acc[2 * i + 1], false);
+            acc[2 * i] = fmaf(sgn, bf16_lo(w[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(sgn, bf16_hi(w[i]), acc[2 * i + 1]);
         }
     }
 }
@@ -181,11 +178,6 @@ __device__ __forceinline__ void acc_dot2x8(float (&acc)[8], const uint4& raw, ui
 // Sign of a plan entry as a mask on a pair of bf16 values.
 __device__ __forceinline__ uint32_t entry_sign_xor(uint32_t e) {
     return (e & kNeg) ? 0x80008000u : 0u;
-}
-
-// bf16 pattern of a plan entry's sign: 0x3F80 (+1), 0xBF80 (-1), 0 (absent).
-__device__ __forceinline__ uint32_t entry_sign_bf16(uint32_t e) {
-    return (e & kAbsent) ? 0u : ((e & kNeg) ? 0xBF80u : 0x3F80u);
 }
 
 // Plans of `count` consecutive groups starting at g0, one J-entry row per
@@ -234,6 +226,25 @@ __device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __rest
         }
     }
     __syncthreads();
+}
+
+// W_c fragments are read from global memory in a coalesced pattern (lane l
+// reads 16 bytes at row l/4, k-chunk l%4, so each group of 4 lanes reads 64
+// contiguous bytes of one row) and then moved into the MFMA operand pattern
+// (lane l holds row l%16, k-chunk l/16) with a fixed cross-lane permutation.
+// Read straight in the operand pattern, consecutive lanes would touch
+// different rows and every lane quad different cache lines.
+__device__ __forceinline__ int coalesced_src_lane_bytes(int lane) {
+    return ((lane & 15) * 4 + (lane >> 4)) * 4;
+}
+
+__device__ __forceinline__ uint4 to_operand_layout(const uint4& v, int src_bytes) {
+    uint4 r;
+    r.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.x)));
+    r.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.y)));
+    r.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.z)));
+    r.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.w)));
+    return r;
 }
 
 // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
@@ -598,7 +609,8 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 // 32-wide k-steps [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each
 // lane builds 8 sketch values of token (lane % 16) straight from x and loads 8
 // weights of neuron (lane % 16); one 16x16x32 MFMA per step.  Tokens >= M are
-// zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.
+// zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.  W_c is
+// read coalesced and permuted into the operand pattern across lanes.
 template <int NW, int C_T, bool FROM_HASH>
 __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w,
@@ -629,8 +641,11 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
     const int kq = (lane >> 4) * 8;
     const bool tok_ok = tok < M;
     const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : 0) * K + kq;
-    const int n = g * BN + nb * 16 + (lane & 15);
-    const uint16_t* wrow = w + static_cast<size_t>(n) * Kc + kq;
+    // W_c is read coalesced (this lane: neuron lane/4 of the block, k-chunk
+    // lane%4) and permuted into the MFMA operand pattern before use
+    const int n = g * BN + nb * 16 + (lane >> 2);
+    const uint16_t* wrow = w + static_cast<size_t>(n) * Kc + (lane & 3) * 8;
+    const int perm_src = coalesced_src_lane_bytes(lane);
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int U = 4;  // steps in flight per wave
@@ -675,7 +690,8 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
             }
             const uint4 ap = pack_bf16x8(a);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
-                                                          __builtin_bit_cast(bf16x8, wr[u]), acc, 0, 0, 0);
+                                                          __builtin_bit_cast(bf16x8, to_operand_layout(wr[u], perm_src)),
+                                                          acc, 0, 0, 0);
         }
     }
     for (; s < s_end; ++s) {
@@ -692,7 +708,8 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
         }
         const uint4 ap = pack_bf16x8(a);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
-                                                      __builtin_bit_cast(bf16x8, wr), acc, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8, to_operand_layout(wr, perm_src)),
+                                                      acc, 0, 0, 0);
     }
 
     red[wave * 64 + lane] = acc;
@@ -721,11 +738,12 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
 // then each wave takes whole groups of the block's group range, one after
 // another, with no further barrier.  Per 32-wide k-step a wave loads its
 // group's W_c slice from global memory and, for each 16-row block of the band,
-// reads the c source chunks from the band, sums them in float32 with bf16
-// dot-product instructions, rounds the sketch to bf16 and feeds it to one MFMA
+// reads the c source chunks from the band, sums them in float32 (sign flips
+// and fused multiply-adds), rounds the sketch to bf16 and feeds it to one MFMA
 // per 16 neurons.  The steps run as a two-stage software pipeline: the plan
 // entries, band reads and W_c loads of step s+1 are issued before the
-// arithmetic of step s, so LDS and L2 latency overlap with the math.
+// arithmetic of step s, so LDS and L2 latency overlap with the math; the
+// pipeline runs on across the wave's groups.
 // The MFMA computes the transposed tile y^T = W_c * z^T so that each lane ends
 // up with 4*BN/16 consecutive outputs of one row (W_c rows are loaded in the
 // matching permuted order) and stores them as 16-byte vectors.
@@ -787,99 +805,21 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
     const int q = lane >> 4;           // which 8 of the 32 k of a step, and output quarter
     const int Kc = Jc * BK;
     const int steps = Kc / 32;
-    // W_c row loaded by this lane for neuron block nb: MFMA row li of block nb
-    // is neuron (li/4)*4*NB + nb*4 + li%4 of the group.
+    // MFMA row r of neuron block nb is neuron (r/4)*4*NB + nb*4 + r%4 of the
+    // group.  W_c is loaded coalesced (this lane: row lane/4 of the block,
+    // k-chunk lane%4) and permuted into the operand pattern before use.
     int wrow[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) wrow[nb] = (li >> 2) * 4 * NB + nb * 4 + (li & 3);
+    for (int nb = 0; nb < NB; ++nb) {
+        const int r = lane >> 2;
+        wrow[nb] = (r >> 2) * 4 * NB + nb * 4 + (r & 3);
+    }
+    const int wchunk = (lane & 3) * 8;
+    const int perm_src = coalesced_src_lane_bytes(lane);
     const uint16_t* lrow = band + li * LDK + q * 8;  // this lane's band row (block 0) and k offset
 
-    for (int gl = wave; gl < GW; gl += NW) {
-        const int g = g0 + gl;
-        const uint32_t* plan = s_src + gl * J;
-        const uint16_t* wg = w + static_cast<size_t>(g) * BN * Kc + q * 8;
-        f32x4 acc[RB][NB];
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-        if constexpr (C_T > 0) {
-            // operands of one step: band reads, their signs, and the W_c slice
-            struct Stage {
-                uint4 raw[RB][CR];
-                uint32_t sg[CR];
-                uint32_t sx[CR];
-                uint4 wf[NB];
-            };
-            auto load = [&](int s, Stage& st) {
-                const int k0 = s * 32;
-                const int t = k0 / BK;
-                const int ub = k0 - t * BK;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    st.wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
-#pragma unroll
-                for (int r = 0; r < C_T; ++r) {
-                    const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * C_T + r]);
-                    st.sg[r] = entry_sign_bf16(e);
-                    st.sx[r] = entry_sign_xor(e);
-                    const uint16_t* src = lrow + (e & kOffMask) + ub;
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        st.raw[rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK);
-                }
-            };
-            auto compute = [&](const Stage& st) {
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    float a[8];
-#pragma unroll
-                    for (int r = 0; r < C_T; ++r) acc_dot2x8(a, st.raw[rb][r], st.sg[r], st.sx[r], r == 0);
-                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, st.wf[nb]), zf, acc[rb][nb], 0, 0, 0);
-                }
-            };
-            Stage sa, sb;
-            load(0, sa);
-            int s = 0;
-            for (; s + 2 <= steps; s += 2) {
-                load(s + 1, sb);
-                compute(sa);
-                if (s + 2 < steps) load(s + 2, sa);
-                compute(sb);
-            }
-            if (s < steps) compute(sa);
-        } else {
-            // runtime c: no pipelining
-            for (int s = 0; s < steps; ++s) {
-                const int k0 = s * 32;
-                const int t = k0 / BK;
-                const int ub = k0 - t * BK;
-                uint4 wf[NB];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    float a[8];
-                    for (int r = 0; r < c; ++r) {
-                        const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * c + r]);
-                        const uint4 raw = *reinterpret_cast<const uint4*>(lrow + rb * 16 * LDK + (e & kOffMask) + ub);
-                        acc_dot2x8(a, raw, entry_sign_bf16(e), entry_sign_xor(e), r == 0);
-                    }
-                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, wf[nb]), zf, acc[rb][nb], 0, 0, 0);
-                }
-            }
-        }
-        // lane holds y[m0 + rb*16 + li][g*BN + q*4*NB + nb*4 + i]
+    // lane holds y[m0 + rb*16 + li][g*BN + q*4*NB + nb*4 + i] of acc[rb][nb][i]
+    auto store_tile = [&](int g, f32x4 (&acc)[RB][NB]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int m = m0 + rb * 16 + li;
@@ -894,6 +834,133 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
                 o.w = pack_bf16(acc[rb][2 * h + 1][2], acc[rb][2 * h + 1][3]);
                 *reinterpret_cast<uint4*>(yr + h * 8) = o;
             }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    f32x4 acc[RB][NB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if constexpr (C_T > 0) {
+        // Two-stage software pipeline over the wave's (group, step) items:
+        // the operands of the next item (the next group's first step at a
+        // group's end) are requested before the arithmetic of the current
+        // one.  Every prefetch is unconditional (past the last item it
+        // re-reads the last one) and the order is pinned with scheduling
+        // barriers, so the compiler neither sinks a prefetch next to its use
+        // nor has to wait conservatively at control-flow joins; a group's
+        // output stores come after the prefetch of the next group.
+        const int ngw = (wave < GW) ? (GW - wave + NW - 1) / NW : 0;
+        struct Stage {
+            uint4 raw[RB][CR];
+            float sg[CR];
+            uint32_t sx[CR];
+            uint4 wf[NB];
+        };
+        auto load = [&](int gi, int s, Stage& st) {
+            if (s >= steps) {  // next group's first step, or the last item again
+                if (gi + 1 < ngw) {
+                    ++gi;
+                    s = 0;
+                } else {
+                    s = steps - 1;
+                }
+            }
+            const int gl = wave + gi * NW;
+            const uint32_t* plan = s_src + gl * J;
+            const uint16_t* wg = w + static_cast<size_t>(g0 + gl) * BN * Kc + wchunk;
+            const int k0 = s * 32;
+            const int t = k0 / BK;
+            const int ub = k0 - t * BK;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st.wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
+#pragma unroll
+            for (int r = 0; r < C_T; ++r) {
+                const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * C_T + r]);
+                st.sg[r] = entry_sign(e);
+                st.sx[r] = entry_sign_xor(e);
+                const uint16_t* src = lrow + (e & kOffMask) + ub;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    st.raw[rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK);
+            }
+        };
+        auto compute = [&](const Stage& st) {
+            uint4 wop[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) wop[nb] = to_operand_layout(st.wf[nb], perm_src);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                float a[8];
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) acc_sign8(a, st.raw[rb][r], st.sg[r], st.sx[r], r == 0);
+                const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wop[nb]), zf, acc[rb][nb], 0, 0, 0);
+            }
+        };
+        Stage sa, sb;
+        if (ngw > 0) load(0, 0, sa);
+        for (int gi = 0; gi < ngw; ++gi) {
+            int s = 0;
+            for (; s + 2 <= steps; s += 2) {
+                load(gi, s + 1, sb);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(sa);
+                __builtin_amdgcn_sched_barrier(0);
+                load(gi, s + 2, sa);
+                __builtin_amdgcn_sched_barrier(0);
+                compute(sb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (s < steps) {  // odd step count: the last step sits in sa
+                compute(sa);
+                __builtin_amdgcn_sched_barrier(0);
+                load(gi, steps, sa);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            store_tile(g0 + wave + gi * NW, acc);
+        }
+    } else {
+        // runtime c: no pipelining
+        for (int gl = wave; gl < GW; gl += NW) {
+            const int g = g0 + gl;
+            const uint32_t* plan = s_src + gl * J;
+            const uint16_t* wg = w + static_cast<size_t>(g) * BN * Kc + wchunk;
+            for (int s = 0; s < steps; ++s) {
+                const int k0 = s * 32;
+                const int t = k0 / BK;
+                const int ub = k0 - t * BK;
+                uint4 wf[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    wf[nb] = to_operand_layout(
+                        *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0), perm_src);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float a[8];
+                    for (int r = 0; r < c; ++r) {
+                        const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * c + r]);
+                        const uint4 raw = *reinterpret_cast<const uint4*>(lrow + rb * 16 * LDK + (e & kOffMask) + ub);
+                        acc_sign8(a, raw, entry_sign(e), entry_sign_xor(e), r == 0);
+                    }
+                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wf[nb]), zf, acc[rb][nb], 0, 0, 0);
+                }
+            }
+            store_tile(g, acc);
         }
     }
 }
