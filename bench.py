@@ -16,10 +16,18 @@ oracle timed on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload gpt2s_up]
                     [--algo auto] [--index] [--warm] [--no-cpu-baseline]
                     [--sweep FILE]   # one extra JSON line per workload into FILE
+    python bench.py --copy-calibration   # a plain 256 MiB device copy, for counters
+
+roofline.traffic is the HBM traffic of one launch measured with rocprofv3
+FETCH_SIZE and WRITE_SIZE counters, each scaled by what the counter reads for
+the plain copy of --copy-calibration; it is read from
+profiles/traffic_counters.json and reported only while the kernel source the
+counters were taken on is unchanged (else null).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -66,8 +74,49 @@ def roofline(wl, t):
     else:
         r = {"bound": "hbm", **hb, "other": {"bound": "mfma", **mf}}
     r["t_lower_us"] = max(t_f, t_b) * 1e6
-    r["traffic"] = None
+    traffic = recorded_traffic(wl.name)
+    r["traffic"] = traffic
+    r["traffic_unit"] = "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)"
+    r["traffic_vs_algorithmic"] = (traffic / wk["bytes"]) if traffic else None
     return r
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "sketched_parameter_sharing_amd", "csrc", "ss1_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_sha256():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(name):
+    """Calibrated HBM bytes per launch for workload `name` from the committed
+    counter record, or None when there is none or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    w = rec.get("workloads", {}).get(name)
+    if not w:
+        return None
+    return w.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(n=20):
+    """A plain device copy of 256 MiB, repeated n times: the known-size
+    reference for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    nbytes = 256 << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": n}))
 
 
 def to_dev(a, dtype):
@@ -115,15 +164,11 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm):
 
 
 def kernel_name(wl, algo):
+    """The kernel a call runs: the requested one, or what the library picks."""
     if algo != "auto":
         return algo
-    if wl.dtype != "bf16":
-        return "generic"
-    if wl.M <= 16 and wl.BK % 32 == 0 and wl.BN % 16 == 0:
-        return "smallm"
-    if wl.BK % 32 == 0 and wl.BN in (32, 64, 128):
-        return "fused"
-    return "generic"
+    import sketched_parameter_sharing_amd as ss1
+    return ss1.select_algo(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype)
 
 
 def cpu_baseline(wl, budget_s=10.0):
@@ -173,6 +218,8 @@ def main():
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default=None, help="also time every workload, JSON lines into this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -184,6 +231,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import sketched_parameter_sharing_amd as ss1
     from ss1_inputs import WORKLOADS
     ss1.load()

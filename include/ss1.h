@@ -176,6 +176,17 @@ ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
                                 ss1_tensor* y, int32_t algo, void* stream);
 
 /*
+ * ss1_select_algo -- HOST.  The kernel (an ss1_algo value, never AUTO) that
+ * ss1_forward would run for a layer with these descriptors; only their
+ * dtypes and sizes are read (data may be NULL).  For M == 0 it reports the
+ * kernel a non-empty call of the same layer would use.  May query the current
+ * HIP device's properties.  Errors: as the shape and dtype checks of
+ * ss1_forward.
+ */
+ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
+                           int32_t BN, int32_t* algo);
+
+/*
  * ss1_sketch -- DEVICE, asynchronous.  The standalone input sketch (the first
  * of the two steps on the SS1 summary page, "Approach") for every group:
  *   z[g][m][k'] for g < G = N/BN, m < M, k' < Kc, written as a [G*M][Kc]

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     load,
     plan,
     plan_index,
+    select_algo,
     sketch,
     version,
 )

@@ -27,7 +27,8 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
          "band": ALGO_BAND}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
-           "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_sketch")
+           "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch")
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
 class SS1Error(RuntimeError):
@@ -74,6 +75,8 @@ def load():
         f.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, i32, vp]
     lib.ss1_sketch.restype = i32
     lib.ss1_sketch.argtypes = [tp, vp, vp, i32, i32, i32, i64, tp, vp]
+    lib.ss1_select_algo.restype = i32
+    lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     _LIB = lib
     return lib
 
@@ -189,6 +192,18 @@ def forward_idx(x, W_c, idx, isign, c: int, BK: int, BN: int, y=None, algo: str 
                                       c, BK, BN, ctypes.byref(dy), ALGOS[algo], _stream(stream))
     _check(st, "ss1_forward_idx")
     return y
+
+
+def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16") -> str:
+    """Name of the kernel ss1_forward runs for this layer ("fused", "smallm",
+    "band" or "generic")."""
+    code = BF16 if dtype == "bf16" else F32
+    x = Tensor(None, code, 0, M, K)
+    w = Tensor(None, code, 0, N, K // c if c > 0 else 0)
+    out = ctypes.c_int32(-1)
+    _check(load().ss1_select_algo(ctypes.byref(x), ctypes.byref(w), c, BK, BN, ctypes.byref(out)),
+           "ss1_select_algo")
+    return ALGO_NAMES[out.value]
 
 
 def sketch(x, hash_, sign, c: int, BK: int, BN: int, N: int, z=None, out_dtype=None, stream=None):

@@ -58,6 +58,23 @@ ss1_status check_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32
     return SS1_OK;
 }
 
+// The kernel ss1_forward picks for a validated call.
+int32_t auto_algo(const ForwardArgs& a) {
+    if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
+    if (ss1::band_supported(a, 48)) return SS1_ALGO_BAND;
+    if (ss1::fused_supported(a)) return SS1_ALGO_FUSED;
+    return SS1_ALGO_GENERIC;
+}
+
+ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
+    switch (algo) {
+        case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
+        case SS1_ALGO_BAND: return ss1::launch_band(a);
+        case SS1_ALGO_FUSED: return ss1::launch_fused(a);
+        default: return ss1::launch_generic(a);
+    }
+}
+
 ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* plan_i,
                        const int8_t* plan_s, int32_t c, int32_t BK, int32_t BN, ss1_tensor* y,
                        int32_t algo, PlanForm form, void* stream) {
@@ -67,10 +84,7 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
     switch (algo) {
         case SS1_ALGO_AUTO:
             if (a.M == 0) return SS1_OK;
-            if (ss1::smallm_supported(a)) return ss1::launch_smallm(a);
-            if (ss1::band_supported(a, 48)) return ss1::launch_band(a);
-            if (ss1::fused_supported(a)) return ss1::launch_fused(a);
-            return ss1::launch_generic(a);
+            return launch_algo(a, auto_algo(a));
         case SS1_ALGO_FUSED:
             if (!ss1::fused_supported(a)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_fused(a);
@@ -129,6 +143,25 @@ extern "C" ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor
                                            int32_t BK, int32_t BN, ss1_tensor* y, int32_t algo,
                                            void* stream) {
     return run_forward(x, W_c, idx, isign, c, BK, BN, y, algo, PlanForm::Index, stream);
+}
+
+extern "C" ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
+                                      int32_t BN, int32_t* algo) {
+    if (!x || !W_c || !algo) return SS1_ERR_NULL;
+    // shape and dtype checks of ss1_forward on a stand-in output and plan
+    ss1_tensor y{x->data, x->dtype, 0, x->rows, W_c->rows};
+    static const int32_t plan_i = 0;
+    static const int8_t plan_s = 0;
+    ss1_tensor xs = *x, ws = *W_c;
+    static char dummy[16] __attribute__((aligned(16)));
+    if (!xs.data) xs.data = dummy;
+    if (!ws.data) ws.data = dummy;
+    y.data = xs.data;
+    ForwardArgs a;
+    ss1_status st = check_forward(&xs, &ws, &plan_i, &plan_s, c, BK, BN, &y, PlanForm::Index, nullptr, &a);
+    if (st != SS1_OK) return st;
+    *algo = auto_algo(a);
+    return SS1_OK;
 }
 
 extern "C" ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* sign,

@@ -191,3 +191,20 @@ def test_binding_refuses_host_tensors():
     h = torch.zeros(1, 4, dtype=torch.int32)
     with pytest.raises(ValueError):
         ss1.forward(x, w, h, h.to(torch.int8), 2, 64, 64)
+
+
+def test_select_algo_host():
+    # decode shapes take the small-M kernel, float32 the generic one; invalid
+    # shapes give the forward's own status codes
+    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64) == "smallm"
+    assert ss1.select_algo(16, 14336, 4096, 2, 64, 64) == "smallm"
+    assert ss1.select_algo(64, 256, 256, 2, 32, 32, "f32") == "generic"
+    assert ss1.select_algo(300, 240, 96, 2, 24, 48) == "generic"
+    assert ss1.select_algo(4096, 4096, 4096, 2, 64, 64) in ("fused", "band")
+    with pytest.raises(ss1.SS1Error) as e:
+        ss1.select_algo(8, 250, 64, 2, 64, 64)
+    assert e.value.status == _lib.ERR_SHAPE
+    lib = _lib.load()
+    out = ctypes.c_int32(0)
+    assert lib.ss1_select_algo(None, ctypes.byref(T(1, 1)), 2, 64, 64, ctypes.byref(out)) == _lib.ERR_NULL
+    assert lib.ss1_select_algo(ctypes.byref(T(8, 256)), ctypes.byref(T(64, 128)), 2, 64, 64, None) == _lib.ERR_NULL

@@ -285,3 +285,14 @@ def test_sketch_bit_exact(name, M):
         torch.cuda.synchronize()
         refb = oracle.sketch_rounded(inp.x, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, to_bf16=True)
         assert np.array_equal(host(zb).reshape(refb.shape), refb)
+
+
+@pytest.mark.parametrize("name", ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m16", "tiny"])
+def test_auto_runs_the_selected_kernel(name):
+    wl = WORKLOADS[name].with_m(min(WORKLOADS[name].M, 200))
+    algo = ss1.select_algo(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype)
+    if name in ("gpt2s_up", "gpt2l_up"):
+        assert algo == "band"
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    assert torch.equal(run(wl, inp, p), run(wl, inp, p, algo=algo))
