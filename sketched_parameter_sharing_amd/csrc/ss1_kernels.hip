@@ -44,6 +44,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Workgroup barrier that orders LDS only: global loads still in flight stay in
+// flight (a plain __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Buffer-resource loads: a scalar base (the descriptor) plus a per-lane 32-bit
+// byte offset and a scalar byte offset, so per-step addressing costs no vector
+// instructions.  Reads at or past `bytes` return zero.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data format, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // ---------------------------------------------------------------- plan in LDS
 // One 32-bit word per source: element offset of the source chunk inside an x
 // row (bits 0..29), "negative" (bit 31), "absent" (bit 30).
@@ -415,6 +434,8 @@ __global__ __launch_bounds__(256) void generic_kernel(const TIn* __restrict__ x,
 // Block: 256 threads (4 waves as WM x WN), output tile MT x BN of one group.
 // Stage s covers k' in [s*KS, s*KS + KS), all inside compressed chunk
 // t = s*KS / BK (KS divides BK).  LDS rows are padded by 8 bf16 (16 bytes).
+// The sketch tile of a stage is summed in registers (sign flip + FMA, float32)
+// and written to LDS as bf16 next to the W_c tile; both are double-buffered.
 template <int MT, int BN, int WM, int WN, int KS, int C_T, bool FROM_HASH>
 __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ w,
@@ -441,9 +462,18 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 
     const int c = (C_T > 0) ? C_T : c_rt;
     const int G = N / BN;
+    // Tile order: each XCD works through a contiguous range of tiles (see
+    // xcd_tile), and inside that range the two row tiles of a pair come
+    // next to each other for every group, so the blocks running together on
+    // one XCD share one pair of row bands (x gathers hit L2) and each W_c
+    // slice they fetch serves two row tiles.
+    constexpr int MG = 2;
     const int tile = xcd_tile(blockIdx.x, n_mt * G);
-    const int g = tile % G;
-    const int mt = tile / G;
+    const int mgi = tile / (MG * G);
+    const int mg_eff = min(MG, n_mt - mgi * MG);
+    const int rem = tile - mgi * MG * G;
+    const int g = rem / mg_eff;
+    const int mt = mgi * MG + rem % mg_eff;
     stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
 
     const int m0 = mt * MT;
@@ -455,16 +485,17 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
     const int wm = wave / WN, wn = wave % WN;
     const int nstage = Kc / KS;
 
-    // per-thread load coordinates
+    // per-thread load coordinates; rows past M read row M-1 (never stored)
     int a_row[AV], a_col[AV];
-    bool a_ok[AV];
+    size_t a_src[AV];
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         const int v = tid + i * 256;
         a_row[i] = v / VPR;
         a_col[i] = (v % VPR) * 8;
-        a_ok[i] = (m0 + a_row[i]) < M;
+        a_src[i] = static_cast<size_t>(min(m0 + a_row[i], M - 1)) * K + a_col[i];
     }
+    constexpr bool B_FULL = (BN * VPR) % 256 == 0;
     int b_row[BV], b_col[BV];
     bool b_ok[BV];
 #pragma unroll
@@ -472,86 +503,9 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
         const int v = tid + i * 256;
         b_row[i] = v / VPR;
         b_col[i] = (v % VPR) * 8;
-        b_ok[i] = v < BN * VPR;
+        b_ok[i] = B_FULL || v < BN * VPR;
+        if (!b_ok[i]) b_row[i] = 0;
     }
-
-    uint4 araw[AV][CR];
-    float asg[CR];
-    uint4 braw[BV];
-
-    auto issue_loads = [&](int s) {
-        const int k0 = s * KS;
-        const int t = k0 / BK;
-        const int u0 = k0 - t * BK;
-        if constexpr (C_T > 0) {
-#pragma unroll
-            for (int r = 0; r < C_T; ++r) {
-                const uint32_t e = s_src[t * C_T + r];
-                asg[r] = entry_sign(e);
-                const uint16_t* src = x + (e & kOffMask) + u0;
-#pragma unroll
-                for (int i = 0; i < AV; ++i) {
-                    araw[i][r] = a_ok[i] ? *reinterpret_cast<const uint4*>(
-                                               src + static_cast<size_t>(m0 + a_row[i]) * K + a_col[i])
-                                         : make_uint4(0, 0, 0, 0);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < BV; ++i) {
-            braw[i] = b_ok[i] ? *reinterpret_cast<const uint4*>(
-                                    w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i])
-                              : make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    auto store_stage = [&](int s, int buf) {
-        uint16_t* A = As + buf * MT * LDP;
-        uint16_t* B = Bs + buf * BN * LDP;
-        if constexpr (C_T == 1) {
-            // one source: the sketch is the chunk itself with its sign bit flipped
-            const uint32_t flip = (asg[0] < 0.0f) ? 0x80008000u : 0u;
-            const uint32_t zero = (asg[0] == 0.0f) ? 0u : 0xFFFFFFFFu;
-#pragma unroll
-            for (int i = 0; i < AV; ++i) {
-                uint4 v = araw[i][0];
-                v.x = (v.x ^ flip) & zero;
-                v.y = (v.y ^ flip) & zero;
-                v.z = (v.z ^ flip) & zero;
-                v.w = (v.w ^ flip) & zero;
-                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = v;
-            }
-        } else if constexpr (C_T > 1) {
-#pragma unroll
-            for (int i = 0; i < AV; ++i) {
-                float acc[8];
-#pragma unroll
-                for (int r = 0; r < C_T; ++r) acc_bf16x8(acc, araw[i][r], asg[r], r == 0);
-                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = pack_bf16x8(acc);
-            }
-        } else {
-            // runtime c: read and sum the sources here, one after another
-            const int k0 = s * KS;
-            const int t = k0 / BK;
-            const int u0 = k0 - t * BK;
-#pragma unroll
-            for (int i = 0; i < AV; ++i) {
-                float acc[8];
-                for (int r = 0; r < c; ++r) {
-                    const uint32_t e = s_src[t * c + r];
-                    const uint4 raw = a_ok[i] ? *reinterpret_cast<const uint4*>(
-                                                    x + (e & kOffMask) + u0 +
-                                                    static_cast<size_t>(m0 + a_row[i]) * K + a_col[i])
-                                              : make_uint4(0, 0, 0, 0);
-                    acc_bf16x8(acc, raw, entry_sign(e), r == 0);
-                }
-                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = pack_bf16x8(acc);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < BV; ++i)
-            if (b_ok[i]) *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = braw[i];
-    };
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -559,15 +513,9 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    issue_loads(0);
-    store_stage(0, 0);
-    __syncthreads();
-
     const int fr = lane & 15;       // row (A) / column (B) inside a 16x16 block
     const int fk = (lane >> 4) * 8; // first k of this lane's 8
-    for (int s = 0; s < nstage; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nstage) issue_loads(s + 1);
+    auto mma = [&](int buf) {
         const uint16_t* A = As + buf * MT * LDP;
         const uint16_t* B = Bs + buf * BN * LDP;
 #pragma unroll
@@ -585,8 +533,128 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < nstage) store_stage(s + 1, buf ^ 1);
+    };
+
+    if constexpr (C_T > 0) {
+        // Register stage: the raw source vectors of the sketch tile, their
+        // signs, and the W_c tile of one k-stage.  Stage s+2 is requested
+        // while stage s is multiplied, and written to LDS (summed, rounded)
+        // one stage later; the order is pinned with scheduling barriers.
+        constexpr bool DEEP = C_T * AV <= 8;  // two register stages fit without spilling
+        struct Regs {
+            uint4 a[AV][CR];
+            float sg[CR];
+            uint32_t sx[CR];
+            uint4 b[BV];
+        };
+        auto issue = [&](int s, Regs& R) {
+            s = min(s, nstage - 1);
+            const int k0 = s * KS;
+            const int t = k0 / BK;
+            const int u0 = k0 - t * BK;
+#pragma unroll
+            for (int r = 0; r < C_T; ++r) {
+                const uint32_t e = __builtin_amdgcn_readfirstlane(s_src[t * C_T + r]);
+                R.sg[r] = entry_sign(e);
+                R.sx[r] = entry_sign_xor(e);
+                const uint16_t* src = x + (e & kOffMask) + u0;
+#pragma unroll
+                for (int i = 0; i < AV; ++i) R.a[i][r] = *reinterpret_cast<const uint4*>(src + a_src[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < BV; ++i)
+                R.b[i] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
+        };
+        auto commit = [&](const Regs& R, int buf) {
+            uint16_t* A = As + buf * MT * LDP;
+            uint16_t* B = Bs + buf * BN * LDP;
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                uint4 v;
+                if constexpr (C_T == 1) {
+                    const uint32_t fl = R.sx[0];
+                    v = make_uint4(R.a[i][0].x ^ fl, R.a[i][0].y ^ fl, R.a[i][0].z ^ fl, R.a[i][0].w ^ fl);
+                } else {
+                    float sum[8];
+#pragma unroll
+                    for (int r = 0; r < C_T; ++r) acc_sign8(sum, R.a[i][r], R.sg[r], R.sx[r], r == 0);
+                    v = pack_bf16x8(sum);
+                }
+                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = v;
+            }
+#pragma unroll
+            for (int i = 0; i < BV; ++i)
+                if (b_ok[i]) *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = R.b[i];
+        };
+
+        if constexpr (DEEP) {
+            Regs r0, r1;
+            issue(0, r0);
+            issue(1, r1);
+            commit(r0, 0);
+            lds_barrier();
+            int s = 0;
+            for (; s + 2 <= nstage; s += 2) {
+                issue(s + 2, r0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(0);
+                __builtin_amdgcn_sched_barrier(0);
+                commit(r1, 1);  // stage s+1 (re-writes the last stage when s+1 == nstage)
+                lds_barrier();
+                issue(s + 3, r1);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(1);
+                __builtin_amdgcn_sched_barrier(0);
+                commit(r0, 0);  // stage s+2
+                lds_barrier();
+            }
+            if (s < nstage) mma(0);
+        } else {
+            // one register stage: stage s+1 is requested while stage s is multiplied
+            Regs r0;
+            issue(0, r0);
+            commit(r0, 0);
+            lds_barrier();
+            for (int s = 0; s < nstage; ++s) {
+                issue(s + 1, r0);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(s & 1);
+                __builtin_amdgcn_sched_barrier(0);
+                commit(r0, (s + 1) & 1);  // past the last stage this re-writes the idle buffer
+                lds_barrier();
+            }
+        }
+    } else {
+        // runtime c: stage the sketch straight from global memory each step
+        auto build = [&](int s, int buf) {
+            const int k0 = s * KS;
+            const int t = k0 / BK;
+            const int u0 = k0 - t * BK;
+            uint16_t* A = As + buf * MT * LDP;
+            uint16_t* B = Bs + buf * BN * LDP;
+#pragma unroll
+            for (int i = 0; i < AV; ++i) {
+                float sum[8];
+                for (int r = 0; r < c; ++r) {
+                    const uint32_t e = s_src[t * c + r];
+                    const uint4 raw = *reinterpret_cast<const uint4*>(x + (e & kOffMask) + u0 + a_src[i]);
+                    acc_sign8(sum, raw, entry_sign(e), entry_sign_xor(e), r == 0);
+                }
+                *reinterpret_cast<uint4*>(A + a_row[i] * LDP + a_col[i]) = pack_bf16x8(sum);
+            }
+#pragma unroll
+            for (int i = 0; i < BV; ++i)
+                if (b_ok[i])
+                    *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = *reinterpret_cast<const uint4*>(
+                        w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
+        };
+        build(0, 0);
         __syncthreads();
+        for (int s = 0; s < nstage; ++s) {
+            if (s + 1 < nstage) build(s + 1, (s + 1) & 1);
+            mma(s & 1);
+            __syncthreads();
+        }
     }
 
     // epilogue: lane holds rows 4*(lane/16) + 0..3, column lane % 16 of each block
@@ -747,7 +815,7 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
 // The MFMA computes the transposed tile y^T = W_c * z^T so that each lane ends
 // up with 4*BN/16 consecutive outputs of one row (W_c rows are loaded in the
 // matching permuted order) and stores them as 16-byte vectors.
-template <int MT, int BN, int C_T, int NW, bool FROM_HASH>
+template <int MT, int BN, int C_T, int NW, int RS, int KH, bool RAW_PF, int PD, bool FROM_HASH>
 __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ w,
                                                        const int32_t* __restrict__ pi,
@@ -757,6 +825,12 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
     constexpr int RB = MT / 16;  // 16-row blocks of the band
     constexpr int NB = BN / 16;  // 16-neuron blocks of a group
     static_assert(RB * 16 == MT && NB * 16 == BN && NB % 2 == 0, "tile sizes");
+    static_assert(KH == 1 || (KH == 2 && C_T > 0), "a step is 32*KH wide; 64 needs a fixed c");
+    // RS waves share a group, each taking RBW of the band's row blocks; NG
+    // groups are in progress at a time
+    constexpr int RBW = RB / RS;
+    constexpr int NG = NW / RS;
+    static_assert(RBW * RS == RB && NG * RS == NW, "row split");
     constexpr int CR = (C_T > 0) ? C_T : 1;
     extern __shared__ uint32_t smem[];
     const int LDK = K + 8;  // band row pitch (elements): 16-byte skew between rows
@@ -800,29 +874,33 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
     stage_plans<FROM_HASH>(pi, ps, g0, GW, J, Jc, c, BK, s_src, s_cnt);  // ends with a barrier
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+    const int gl0 = wave / RS;          // first group (inside the block's range) of this wave
+    const int rb0 = (wave % RS) * RBW;  // first row block of this wave
     const int li = lane & 15;          // MFMA row/column index of this lane
     const int q = lane >> 4;           // which 8 of the 32 k of a step, and output quarter
     const int Kc = Jc * BK;
-    const int steps = Kc / 32;
+    const int steps = Kc / (32 * KH);  // KH == 2 needs BK % 64 == 0 (a step stays in one chunk)
     // MFMA row r of neuron block nb is neuron (r/4)*4*NB + nb*4 + r%4 of the
     // group.  W_c is loaded coalesced (this lane: row lane/4 of the block,
     // k-chunk lane%4) and permuted into the operand pattern before use.
-    int wrow[NB];
+    // (byte offsets inside the group's W_c slice; BN*Kc*2 is far below 2^32
+    // for any layer whose band fits in LDS)
+    uint32_t woff[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int r = lane >> 2;
-        wrow[nb] = (r >> 2) * 4 * NB + nb * 4 + (r & 3);
+        woff[nb] = static_cast<uint32_t>(((r >> 2) * 4 * NB + nb * 4 + (r & 3)) * Kc + (lane & 3) * 8) * 2u;
     }
-    const int wchunk = (lane & 3) * 8;
+    const uint32_t wslice_bytes = static_cast<uint32_t>(BN * Kc * 2);
     const int perm_src = coalesced_src_lane_bytes(lane);
-    const uint16_t* lrow = band + li * LDK + q * 8;  // this lane's band row (block 0) and k offset
+    const uint16_t* lrow = band + (rb0 * 16 + li) * LDK + q * 8;  // this lane's band row (first block), k offset
 
-    // lane holds y[m0 + rb*16 + li][g*BN + q*4*NB + nb*4 + i] of acc[rb][nb][i]
-    auto store_tile = [&](int g, f32x4 (&acc)[RB][NB]) {
+    // lane holds y[m0 + (rb0+rb)*16 + li][g*BN + q*4*NB + nb*4 + i] of acc[rb][nb][i]
+    auto store_tile = [&](int g, f32x4 (&acc)[RBW][NB]) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int m = m0 + rb * 16 + li;
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int m = m0 + (rb0 + rb) * 16 + li;
             if (m >= M) continue;
             uint16_t* yr = y + static_cast<size_t>(m) * N + static_cast<size_t>(g) * BN + q * 4 * NB;
 #pragma unroll
@@ -836,14 +914,14 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
             }
         }
 #pragma unroll
-        for (int i = 0; i < RB; ++i)
+        for (int i = 0; i < RBW; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     };
 
-    f32x4 acc[RB][NB];
+    f32x4 acc[RBW][NB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+    for (int i = 0; i < RBW; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -856,97 +934,128 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
         // barriers, so the compiler neither sinks a prefetch next to its use
         // nor has to wait conservatively at control-flow joins; a group's
         // output stores come after the prefetch of the next group.
-        const int ngw = (wave < GW) ? (GW - wave + NW - 1) / NW : 0;
+        const int ngw = (gl0 < GW) ? (GW - gl0 + NG - 1) / NG : 0;
+        // A stage holds what one step needs from outside LDS: its W_c slices
+        // (prefetched a step ahead) and its plan entries.  With RAW_PF the band
+        // reads are prefetched too; otherwise they are issued at the start of
+        // the step, ahead of the operand permutes.
         struct Stage {
-            uint4 raw[RB][CR];
+            uint4 wf[KH][NB];
             float sg[CR];
             uint32_t sx[CR];
-            uint4 wf[NB];
+            uint32_t off[CR];
+            uint4 raw[RAW_PF ? KH : 1][RAW_PF ? RBW : 1][RAW_PF ? CR : 1];
+        };
+        auto read_band = [&](const Stage& st, uint4 (&raw)[KH][RBW][CR]) {
+#pragma unroll
+            for (int r = 0; r < C_T; ++r) {
+                const uint16_t* src = lrow + st.off[r];
+#pragma unroll
+                for (int h = 0; h < KH; ++h)
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb)
+                        raw[h][rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK + 32 * h);
+            }
         };
         auto load = [&](int gi, int s, Stage& st) {
-            if (s >= steps) {  // next group's first step, or the last item again
-                if (gi + 1 < ngw) {
-                    ++gi;
-                    s = 0;
-                } else {
-                    s = steps - 1;
-                }
+            if (gi >= ngw) {  // past the wave's last item: request the last one again
+                gi = ngw - 1;
+                s = steps - 1;
             }
-            const int gl = wave + gi * NW;
+            gi = __builtin_amdgcn_readfirstlane(gi);
+            s = __builtin_amdgcn_readfirstlane(s);
+            const int gl = gl0 + gi * NG;
             const uint32_t* plan = s_src + gl * J;
-            const uint16_t* wg = w + static_cast<size_t>(g0 + gl) * BN * Kc + wchunk;
-            const int k0 = s * 32;
+            const int k0 = s * 32 * KH;
             const int t = k0 / BK;
             const int ub = k0 - t * BK;
+            // both 32-wide halves of a row's 128-byte line are requested back to back
+            const auto wr = make_rsrc(w + static_cast<size_t>(g0 + gl) * BN * Kc, wslice_bytes);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
-                st.wf[nb] = *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0);
+#pragma unroll
+                for (int h = 0; h < KH; ++h) st.wf[h][nb] = buf_load16(wr, woff[nb], (k0 + 32 * h) * 2);
 #pragma unroll
             for (int r = 0; r < C_T; ++r) {
                 const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * C_T + r]);
                 st.sg[r] = entry_sign(e);
                 st.sx[r] = entry_sign_xor(e);
-                const uint16_t* src = lrow + (e & kOffMask) + ub;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    st.raw[rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK);
+                st.off[r] = (e & kOffMask) + ub;
             }
+            if constexpr (RAW_PF) read_band(st, st.raw);
         };
         auto compute = [&](const Stage& st) {
-            uint4 wop[NB];
+            uint4 rawj[KH][RBW][CR];
+            if constexpr (!RAW_PF) read_band(st, rawj);
+            const auto& raw = [&]() -> const uint4(&)[KH][RBW][CR] {
+                if constexpr (RAW_PF) return st.raw; else return rawj;
+            }();
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) wop[nb] = to_operand_layout(st.wf[nb], perm_src);
+            for (int h = 0; h < KH; ++h) {
+                uint4 wop[NB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                float a[8];
+                for (int nb = 0; nb < NB; ++nb) wop[nb] = to_operand_layout(st.wf[h][nb], perm_src);
 #pragma unroll
-                for (int r = 0; r < C_T; ++r) acc_sign8(a, st.raw[rb][r], st.sg[r], st.sx[r], r == 0);
-                const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+                for (int rb = 0; rb < RBW; ++rb) {
+                    float a[8];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, wop[nb]), zf, acc[rb][nb], 0, 0, 0);
+                    for (int r = 0; r < C_T; ++r) acc_sign8(a, raw[h][rb][r], st.sg[r], st.sx[r], r == 0);
+                    const bf16x8 zf = __builtin_bit_cast(bf16x8, pack_bf16x8(a));
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wop[nb]), zf, acc[rb][nb], 0, 0, 0);
+                }
             }
         };
-        Stage sa, sb;
-        if (ngw > 0) load(0, 0, sa);
-        for (int gi = 0; gi < ngw; ++gi) {
-            int s = 0;
-            for (; s + 2 <= steps; s += 2) {
-                load(gi, s + 1, sb);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(sa);
-                __builtin_amdgcn_sched_barrier(0);
-                load(gi, s + 2, sa);
-                __builtin_amdgcn_sched_barrier(0);
-                compute(sb);
-                __builtin_amdgcn_sched_barrier(0);
+        // Flat walk over the wave's (group, step) items with a ring of PD
+        // stages: item i+PD-1 is requested before item i is computed.  The
+        // item count is padded to a multiple of PD; padding items re-read the
+        // last item and only touch accumulators that are never stored again.
+        if (ngw > 0) {
+            auto advance = [&](int& gi, int& s) {
+                if (++s == steps) {
+                    s = 0;
+                    ++gi;
+                }
+            };
+            const int total = ngw * steps;
+            Stage st[PD];
+            int lg = 0, ls = 0;  // next item to request
+#pragma unroll
+            for (int j = 0; j < PD - 1; ++j) {
+                load(lg, ls, st[j]);
+                advance(lg, ls);
             }
-            if (s < steps) {  // odd step count: the last step sits in sa
-                compute(sa);
-                __builtin_amdgcn_sched_barrier(0);
-                load(gi, steps, sa);
-                __builtin_amdgcn_sched_barrier(0);
+            int cg = 0, cs = 0;  // next item to compute
+            for (int i0 = 0; i0 < total; i0 += PD) {
+#pragma unroll
+                for (int j = 0; j < PD; ++j) {
+                    load(lg, ls, st[(j + PD - 1) % PD]);
+                    advance(lg, ls);
+                    __builtin_amdgcn_sched_barrier(0);
+                    compute(st[j]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (cs == steps - 1 && cg < ngw) store_tile(g0 + gl0 + cg * NG, acc);
+                    advance(cg, cs);
+                }
             }
-            store_tile(g0 + wave + gi * NW, acc);
         }
     } else {
         // runtime c: no pipelining
-        for (int gl = wave; gl < GW; gl += NW) {
+        for (int gl = gl0; gl < GW; gl += NG) {
             const int g = g0 + gl;
             const uint32_t* plan = s_src + gl * J;
-            const uint16_t* wg = w + static_cast<size_t>(g) * BN * Kc + wchunk;
             for (int s = 0; s < steps; ++s) {
                 const int k0 = s * 32;
                 const int t = k0 / BK;
                 const int ub = k0 - t * BK;
+                const auto wr = make_rsrc(w + static_cast<size_t>(g) * BN * Kc, wslice_bytes);
                 uint4 wf[NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    wf[nb] = to_operand_layout(
-                        *reinterpret_cast<const uint4*>(wg + static_cast<size_t>(wrow[nb]) * Kc + k0), perm_src);
+                for (int nb = 0; nb < NB; ++nb) wf[nb] = to_operand_layout(buf_load16(wr, woff[nb], k0 * 2), perm_src);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
+                for (int rb = 0; rb < RBW; ++rb) {
                     float a[8];
                     for (int r = 0; r < c; ++r) {
                         const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * c + r]);
@@ -1122,33 +1231,47 @@ inline BandCfg band_config(const Dims& d, int64_t M, const DeviceInfo& di) {
     return BandCfg{0, 0, 0};
 }
 
-template <int MT, int BN, int C_T, bool FROM_HASH>
+// Launch shapes of the band kernel:
+//   WIDE (c <= 2, BK % 64 == 0): 64-wide steps, so each pair of W_c requests
+//        covers whole 128-byte lines; band reads issued at the start of a step
+//   BASE: 32-wide steps, band reads a step ahead where registers allow
+// Both run 8 waves (4 when the tile needs more than 256 registers) with W_c
+// requested one step ahead.  (Splitting a group's rows over two waves for
+// four waves per SIMD measured slower: the kernel is not latency-starved.)
+enum class BandShape { BASE, WIDE };
+
+template <int MT, int BN, int C_T, BandShape SH, bool FROM_HASH>
 ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
     const Dims& d = a.d;
-    // two waves per SIMD leave a lane 256 registers; the tiles whose two
-    // pipeline stages and accumulators need more run one wave per SIMD
     constexpr int NW = (BN == 128 || C_T >= 8 || (C_T == 4 && MT == 64)) ? 4 : 8;
+    constexpr int RS = 1;
+    constexpr int KH = SH == BandShape::WIDE ? 2 : 1;
+    constexpr bool RAW_PF = KH == 1 && C_T <= 4 && BN < 128;
+    constexpr int PD = 2;
     const long long nbands = (a.M + MT - 1) / MT;
-    auto kern = &band_kernel<MT, BN, C_T, NW, FROM_HASH>;
+    auto kern = &band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(cfg.lds)) != hipSuccess)
         return SS1_ERR_HIP;
-    hipLaunchKernelGGL((band_kernel<MT, BN, C_T, NW, FROM_HASH>), dim3(static_cast<unsigned>(nbands * cfg.gsplit)),
-                       dim3(NW * 64), cfg.lds, static_cast<hipStream_t>(a.stream),
-                       static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w), a.plan_i,
-                       a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K, (int)d.N, (int)d.J,
-                       (int)d.Jc, d.c, d.BK, cfg.gsplit);
+    hipLaunchKernelGGL((band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH>),
+                       dim3(static_cast<unsigned>(nbands * cfg.gsplit)), dim3(NW * 64), cfg.lds,
+                       static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, cfg.gsplit);
     return launch_status();
 }
 
 template <int MT, int BN, bool FROM_HASH>
 ss1_status launch_band_c(const ForwardArgs& a, const BandCfg& cfg) {
+    const bool wide = a.d.BK % 64 == 0;
     switch (a.d.c) {
-        case 1: return launch_band_cfg<MT, BN, 1, FROM_HASH>(a, cfg);
-        case 2: return launch_band_cfg<MT, BN, 2, FROM_HASH>(a, cfg);
-        case 4: return launch_band_cfg<MT, BN, 4, FROM_HASH>(a, cfg);
-        case 8: return launch_band_cfg<MT, BN, 8, FROM_HASH>(a, cfg);
-        default: return launch_band_cfg<MT, BN, 0, FROM_HASH>(a, cfg);
+        case 1: return wide ? launch_band_cfg<MT, BN, 1, BandShape::WIDE, FROM_HASH>(a, cfg)
+                            : launch_band_cfg<MT, BN, 1, BandShape::BASE, FROM_HASH>(a, cfg);
+        case 2: return wide ? launch_band_cfg<MT, BN, 2, BandShape::WIDE, FROM_HASH>(a, cfg)
+                            : launch_band_cfg<MT, BN, 2, BandShape::BASE, FROM_HASH>(a, cfg);
+        case 4: return launch_band_cfg<MT, BN, 4, BandShape::BASE, FROM_HASH>(a, cfg);
+        case 8: return launch_band_cfg<MT, BN, 8, BandShape::BASE, FROM_HASH>(a, cfg);
+        default: return launch_band_cfg<MT, BN, 0, BandShape::BASE, FROM_HASH>(a, cfg);
     }
 }
 
