@@ -1,4 +1,4 @@
-"""CPU oracle for the SS1 forward (test infrastructure only).
+"""CPU oracle for the SS1 forward and weight projection (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package; the product path never does.
@@ -15,6 +15,8 @@ from .ss1_oracle import (  # noqa: F401
     identity_plan,
     plan,
     plan_index,
+    project,
+    project_rounded,
     sketch,
     sketch_rounded,
 )

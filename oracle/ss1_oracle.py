@@ -39,6 +39,9 @@ Readings where the pages are silent (each is listed in the design doc):
 * Plan generator: SplitMix64, Fisher-Yates with plain modulo, then one sign bit
   per chunk (top bit of a draw), all per group in group order.
 * Precision: everything in float64; bf16 inputs are widened exactly.
+* Projection of a dense weight onto SS1 (the pages only say that pre-trained
+  layers can be projected): least squares onto the sharing pattern, i.e. each
+  compressed entry is the mean of its signed sources.
 
 Nothing here is blocked, fused or reordered beyond the definition.
 """
@@ -295,6 +298,72 @@ def forward_mirror(x, Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int,
     for g in range(G):
         y[:, g * BN:(g + 1) * BN] = z[g] @ Wc[g * BN:(g + 1) * BN, :].T
     return y
+
+
+def project(W, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+    """Projection of a dense [N][K] weight onto SS1's sharing pattern, float64.
+
+    The SS1 author abstract states that pre-trained dense layers can be
+    projected onto the operator (and the summary page's *Key results* use such
+    projected BERT and Llama-3-8B layers); the pages give no formula.  The
+    plain reading taken here is the least-squares projection: for row n of
+    group g = n // BN, compressed entry (n, t*BK + u) minimises
+    sum over sources j of t of (W[n, j*BK + u] - sign[g][j] * Wc[n, t*BK + u])^2,
+    whose minimiser is the mean of sign[g][j] * W[n, j*BK + u] over those
+    sources (c of them in a balanced plan).  A compressed chunk with no source
+    gets 0 (the minimum-norm solution).  Sources are walked in ascending j.
+    Returns Wc, [N][Kc] float64."""
+    d = dims(K, N, c, BK, BN)
+    J, Jc, Kc, G = d["J"], d["Jc"], d["Kc"], d["G"]
+    W = np.asarray(W, dtype=np.float64)
+    if W.shape != (N, K):
+        raise ValueError(f"W must have shape {(N, K)}")
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
+    Wc = np.zeros((N, Kc), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * BN, (g + 1) * BN)
+        count = np.zeros(Jc, dtype=np.int64)
+        for j in range(J):
+            t = int(hash_[g, j])
+            Wc[rows, t * BK:(t + 1) * BK] += float(sign[g, j]) * W[rows, j * BK:(j + 1) * BK]
+            count[t] += 1
+        for t in range(Jc):
+            if count[t] > 0:
+                Wc[rows, t * BK:(t + 1) * BK] /= float(count[t])
+    return Wc
+
+
+def project_rounded(W, hash_, sign, K: int, N: int, c: int, BK: int, BN: int,
+                    to_bf16: bool) -> np.ndarray:
+    """Diagnostic "mirror" of :func:`project` for a float32 device path: the
+    signed sources of each compressed chunk summed in float32 in ascending
+    chunk order (from the first signed source), divided by the source count
+    in float32 (IEEE division, nearest), then, when ``to_bf16``, rounded to
+    the nearest bf16 value with ties to even.  Returns float64 values."""
+    d = dims(K, N, c, BK, BN)
+    J, Jc, Kc, G = d["J"], d["Jc"], d["Kc"], d["G"]
+    W32 = np.asarray(W, dtype=np.float32)
+    if W32.shape != (N, K):
+        raise ValueError(f"W must have shape {(N, K)}")
+    check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
+    Wc = np.zeros((N, Kc), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * BN, (g + 1) * BN)
+        acc = [None] * Jc
+        count = [0] * Jc
+        for j in range(J):
+            t = int(hash_[g, j])
+            term = np.float32(sign[g, j]) * W32[rows, j * BK:(j + 1) * BK]
+            acc[t] = term if acc[t] is None else (acc[t] + term).astype(np.float32)
+            count[t] += 1
+        for t in range(Jc):
+            if acc[t] is None:
+                continue
+            v = (acc[t] / np.float32(count[t])).astype(np.float32)
+            if to_bf16:
+                v = _round_f32_to_bf16(v)
+            Wc[rows, t * BK:(t + 1) * BK] = v.astype(np.float64)
+    return Wc
 
 
 def flops(M: int, K: int, N: int, c: int) -> dict:

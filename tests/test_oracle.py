@@ -350,3 +350,94 @@ def test_plan_worked_examples():
         h, s = oracle.plan(seed, K, N, c, BK, BN)
         assert h[0].tolist() == [int(v) for v in hs]
         assert s[0, :len(ss)].tolist() == [int(v) for v in ss]
+
+
+# ----------------------------------------------------------- projection pins
+# The projection is pinned against an explicit least-squares solve of the
+# expansion matrix (numpy.linalg.lstsq), against dense_expand (left inverse,
+# exact on integers), and by orthogonality of its residual.
+PROJ_SHAPES = [  # K, N, c, BK, BN
+    (64, 8, 2, 8, 4), (96, 12, 4, 8, 6), (48, 6, 1, 8, 3), (72, 8, 3, 4, 8), (256, 16, 8, 8, 16)]
+
+
+def _expansion_matrix(hash_, sign, g, K, c, BK):
+    """[K][Kc] matrix E with dense row = E @ compressed row for group g, built
+    entry by entry from the plan's definition."""
+    J = K // BK
+    Kc = K // c
+    E = np.zeros((K, Kc))
+    for j in range(J):
+        t = int(hash_[g, j])
+        for u in range(BK):
+            E[j * BK + u, t * BK + u] = float(sign[g, j])
+    return E
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", PROJ_SHAPES)
+def test_project_matches_least_squares_solve(K, N, c, BK, BN):
+    h, s = oracle.plan(21, K, N, c, BK, BN)
+    W = np.random.default_rng(3).standard_normal((N, K))
+    got = oracle.project(W, h, s, K, N, c, BK, BN)
+    for n in range(N):
+        E = _expansion_matrix(h, s, n // BN, K, c, BK)
+        ref = np.linalg.lstsq(E, W[n], rcond=None)[0]
+        np.testing.assert_allclose(got[n], ref, rtol=0, atol=1e-12)
+
+
+def test_project_least_squares_unbalanced_and_empty_chunks():
+    K, N, c, BK, BN = 48, 4, 2, 8, 2   # J = 6, Jc = 3
+    h, s = oracle.plan(4, K, N, c, BK, BN)
+    h = h.copy()
+    h[0] = [0, 0, 0, 2, 2, 0]          # chunk 1 of group 0 gets no source, chunk 0 four
+    W = np.random.default_rng(5).standard_normal((N, K))
+    got = oracle.project(W, h, s, K, N, c, BK, BN)
+    for n in range(N):
+        E = _expansion_matrix(h, s, n // BN, K, c, BK)
+        ref = np.linalg.lstsq(E, W[n], rcond=None)[0]   # minimum-norm: 0 on the empty chunk
+        np.testing.assert_allclose(got[n], ref, rtol=0, atol=1e-12)
+    assert not got[:BN, BK:2 * BK].any()
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", [p for p in PROJ_SHAPES if p[2] in (1, 2, 4, 8)])
+def test_project_is_exact_left_inverse_of_dense_expand(K, N, c, BK, BN):
+    h, s = oracle.plan(8, K, N, c, BK, BN)
+    Wc = np.random.default_rng(6).integers(-4, 5, size=(N, K // c)).astype(np.float64)
+    W = oracle.dense_expand(Wc, h, s, K, N, c, BK, BN)
+    assert np.array_equal(oracle.project(W, h, s, K, N, c, BK, BN), Wc)
+
+
+@pytest.mark.parametrize("K,N,c,BK,BN", [p for p in PROJ_SHAPES if p[2] in (1, 2, 4, 8)])
+def test_project_residual_is_orthogonal_to_the_sharing_subspace(K, N, c, BK, BN):
+    h, s = oracle.plan(9, K, N, c, BK, BN)
+    W = np.random.default_rng(7).integers(-8, 9, size=(N, K)).astype(np.float64)
+    R = W - oracle.dense_expand(oracle.project(W, h, s, K, N, c, BK, BN), h, s, K, N, c, BK, BN)
+    assert not oracle.project(R, h, s, K, N, c, BK, BN).any()      # exact: c is a power of 2
+    V = np.random.default_rng(8).standard_normal((N, K // c))
+    inner = np.sum(R * oracle.dense_expand(V, h, s, K, N, c, BK, BN))
+    assert abs(inner) <= 1e-9 * np.abs(R).sum()
+
+
+def test_project_c1_inverts_signed_permutation():
+    K, N, c, BK, BN = 64, 6, 1, 8, 3
+    h, s = oracle.plan(10, K, N, c, BK, BN)
+    W = np.random.default_rng(11).standard_normal((N, K))
+    Wc = oracle.project(W, h, s, K, N, c, BK, BN)
+    assert np.array_equal(oracle.dense_expand(Wc, h, s, K, N, c, BK, BN), W)
+
+
+def test_project_rounded_mirror():
+    K, N, c, BK, BN = 64, 8, 4, 8, 4
+    h, s = oracle.plan(12, K, N, c, BK, BN)
+    # integer inputs: float32 sums and the division by 4 are exact, and the
+    # quarter-integers below 2^6 keep at most 8 significant bits
+    W = np.random.default_rng(13).integers(-4, 5, size=(N, K)).astype(np.float64)
+    exact = oracle.project(W, h, s, K, N, c, BK, BN)
+    for to_bf16 in (False, True):
+        assert np.array_equal(oracle.project_rounded(W, h, s, K, N, c, BK, BN, to_bf16), exact)
+    # c = 3: the division rounds; the mirror gives the float32 quotient
+    K3, c3 = 72, 3
+    h3, s3 = oracle.plan(14, K3, N, c3, 4, BN)
+    W3 = np.random.default_rng(15).integers(-4, 5, size=(N, K3)).astype(np.float64)
+    ex3 = oracle.project(W3, h3, s3, K3, N, c3, 4, BN)
+    m3 = oracle.project_rounded(W3, h3, s3, K3, N, c3, 4, BN, False)
+    assert np.array_equal(m3, ex3.astype(np.float32).astype(np.float64))
