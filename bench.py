@@ -17,6 +17,9 @@ oracle timed on a bounded sample of the same workload.
                     [--algo auto] [--index] [--warm] [--no-cpu-baseline]
                     [--sweep FILE]   # one extra JSON line per workload into FILE
     python bench.py --copy-calibration   # a plain 256 MiB device copy, for counters
+    python bench.py --op project [--workload llama_gateup_m1]
+        # ss1_project instead: least-squares projection of the layer's dense
+        # [N][K] weight onto its sharing pattern, GB/s against the HBM roofline
 
 roofline.traffic is the HBM traffic of one launch measured with rocprofv3
 FETCH_SIZE and WRITE_SIZE counters, each scaled by what the counter reads for
@@ -46,6 +49,8 @@ HEADLINE = "gpt2s_up"
 SWEEP = ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m1", "llama_down_m1",
          "llama_gateup_m16", "llama_down_m16", "llama_gateup_m4096", "llama_down_m4096"] + [
     f"square_c{c}_bn{bn}" for c in (1, 2, 4, 8) for bn in (32, 64, 128)]
+PROJECT_HEADLINE = "llama_gateup_m1"   # the Llama-3-8B gate/up weight, 14336 x 4096
+PROJECT_SWEEP = ["llama_gateup_m1", "llama_down_m1", "gpt2s_up", "gpt2l_up"]
 
 
 def work(wl):
@@ -81,18 +86,24 @@ def roofline(wl, t):
     return r
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "sketched_parameter_sharing_amd", "csrc", "ss1_kernels.hip")
+CSRC = os.path.join(ROOT, "sketched_parameter_sharing_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
 def kernel_source_sha256():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Hash of every device source (kernels and the headers they include)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(name):
-    """Calibrated HBM bytes per launch for workload `name` from the committed
-    counter record, or None when there is none or the kernels changed since."""
+    """Calibrated HBM bytes per launch for record `name` (a workload, or
+    "project:<workload>") from the committed counter record, or None when
+    there is none or the kernels changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
@@ -163,6 +174,70 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm):
     return t, nsets
 
 
+def project_work(wl):
+    e = 2 if wl.dtype == "bf16" else 4
+    return {"bytes": e * (wl.N * wl.K + wl.N * wl.Kc) + wl.G * wl.J * 5,
+            "adds": wl.N * wl.Kc * (wl.c - 1)}
+
+
+def time_project(wl, steps, warmup, warm):
+    """ss1_project over rotating weight sets: (seconds per call, sets)."""
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    from ss1_inputs import make_dense_weight
+
+    vals, bits = make_dense_weight(wl)
+    plan = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    set_bytes = project_work(wl)["bytes"]
+    nsets = 1 if warm else min(64, max(2, int(np.ceil(512e6 / set_bytes)) + 1))
+    W0 = to_dev(bits if wl.dtype == "bf16" else vals, wl.dtype)
+    Ws = [W0] + [W0.clone() for _ in range(nsets - 1)]
+    Cs = [torch.empty((wl.N, wl.Kc), dtype=W0.dtype, device="cuda") for _ in range(nsets)]
+
+    def step(i):
+        k = i % nsets
+        ss1.project(Ws[k], plan.hash, plan.sign, wl.c, wl.BK, wl.BN, W_c=Cs[k])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps, nsets
+
+
+def cpu_baseline_project(wl, budget_s=10.0):
+    """The oracle's projection, float64, on a bounded sample of groups."""
+    import oracle
+    from ss1_inputs import make_dense_weight
+
+    cores = len(os.sched_getaffinity(0))
+    h, s = oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    vals, _ = make_dense_weight(wl)
+    vals = vals.astype(np.float64)
+    e = 2 if wl.dtype == "bf16" else 4
+    ng, t, reps = 1, 0.0, 0
+    while True:
+        rows = ng * wl.BN
+        t0 = time.perf_counter()
+        oracle.project(vals[:rows], h[:ng], s[:ng], wl.K, rows, wl.c, wl.BK, wl.BN)
+        t = time.perf_counter() - t0
+        reps += 1
+        if t > budget_s / 4 or ng >= wl.G:
+            break
+        ng = min(wl.G, ng * 4)
+    nbytes = e * rows * (wl.K + wl.Kc)
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ng} of {wl.G} groups ({rows} of {wl.N} rows) of the {wl.name} weight, "
+                      f"float64 NumPy oracle (single-threaded loops), {t:.3f} s "
+                      f"(the sample's algorithmic bytes / time)"}
+
+
 def kernel_name(wl, algo):
     """The kernel a call runs: the requested one, or what the library picks."""
     if algo != "auto":
@@ -212,8 +287,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=HEADLINE)
-    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic"])
+    ap.add_argument("--workload", default=None,
+                    help=f"default: {HEADLINE} (forward), {PROJECT_HEADLINE} (project)")
+    ap.add_argument("--op", default="forward", choices=["forward", "project"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,6 +342,36 @@ def main():
         }
         return rec, wl
 
+    def measure_project(name, steps, warmup):
+        wl = WORKLOADS[name]
+        t, nsets = time_project(wl, steps, warmup, args.warm)
+        wk = project_work(wl)
+        traffic = recorded_traffic("project:" + name)
+        rec = {
+            "metric": "SS1 weight projection GB/s (dense [N][K] read + compressed [N][K/c] written) "
+                      "+ % of HBM roofline",
+            "value": wk["bytes"] / t / 1e9,
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": steps,
+            "warmup": warmup,
+            "ms_per_step": t * 1e3,
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": wl.dtype,
+            "data": "synthetic (seeded N(0,0.02) dense weight, seeded balanced plan)",
+            "config": {"workload": name + "_weight_projection", "N": wl.N, "K": wl.K, "c": wl.c,
+                       "BK": wl.BK, "BN": wl.BN, "kernel": "project",
+                       "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)"},
+            "roofline": {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9,
+                         "unit": "GB/s", "frac": wk["bytes"] / t / PEAK_HBM, "traffic": traffic,
+                         "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                         "traffic_vs_algorithmic": (traffic / wk["bytes"]) if traffic else None,
+                         "t_lower_us": wk["bytes"] / PEAK_HBM * 1e6},
+        }
+        return rec, wl
+
     if args.sweep:
         with open(args.sweep, "w") as f:
             for name in SWEEP:
@@ -273,8 +380,20 @@ def main():
                 print(f"sweep {name}: {rec['ms_per_step'] * 1e3:.1f} us, "
                       f"{rec['roofline']['bound']} frac {rec['roofline']['frac']:.3f}",
                       file=sys.stderr, flush=True)
+            for name in PROJECT_SWEEP:
+                rec, _ = measure_project(name, max(20, args.steps // 4), max(5, args.warmup // 4))
+                f.write(json.dumps(rec) + "\n")
+                print(f"sweep project {name}: {rec['ms_per_step'] * 1e3:.1f} us, "
+                      f"hbm frac {rec['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
 
-    rec, wl = measure(args.workload, args.steps, args.warmup)
+    if args.op == "project":
+        name = args.workload or PROJECT_HEADLINE
+        rec, wl = measure_project(name, args.steps, args.warmup)
+        rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_project(wl)
+        print(json.dumps(rec), flush=True)
+        return
+
+    rec, wl = measure(args.workload or HEADLINE, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(wl)
     else:

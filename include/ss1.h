@@ -199,6 +199,33 @@ ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* si
                       int32_t c, int32_t BK, int32_t BN, int64_t N,
                       ss1_tensor* z, void* stream);
 
+/*
+ * ss1_project -- DEVICE, asynchronous on `stream`.  Projects a dense weight
+ * onto the SS1 sharing pattern, the step that turns a pre-trained layer into
+ * an SS1 layer (the SS1 author abstract: pre-trained models can be projected
+ * onto SS1; the summary page's "Key results" use projected BERT and
+ * Llama-3-8B layers).  The pages give no formula; the projection here is the
+ * least-squares one: for row n of group g = n/BN,
+ *   W_c[n][t*BK + u] = (1/c) * sum over the c sources j of compressed chunk t
+ *                      of sign[g][j] * W[n][j*BK + u],
+ * the mean of the signed dense entries that the shared entry stands for.
+ *   W   : [N][K] row-major, F32 or BF16 (N = W->rows, K = W->cols); read only
+ *   hash, sign : DEVICE arrays [G][J] as written by ss1_plan; the plan must be
+ *         balanced (W_c is unspecified otherwise, but nothing outside the
+ *         buffers is touched)
+ *   W_c : [N][K/c], same dtype as W; written
+ * Arithmetic: the c signed sources summed in float32 in ascending chunk order,
+ * divided by c (IEEE division, nearest), rounded to W_c's dtype (bf16: nearest,
+ * ties to even).  Requirements: as ss1_forward's chunking rules, BK % 8 == 0
+ * for BF16 and % 4 for F32, G <= 65535, W and W_c 16-byte aligned, hash
+ * 4-byte aligned.  The caller owns every buffer.
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (before
+ * any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* sign,
+                       int32_t c, int32_t BK, int32_t BN,
+                       ss1_tensor* W_c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     plan,
     plan_index,
     select_algo,
+    project,
     sketch,
     version,
 )

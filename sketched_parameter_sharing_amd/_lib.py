@@ -27,7 +27,8 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
          "band": ALGO_BAND}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
-           "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch")
+           "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
+           "ss1_project")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -75,6 +76,8 @@ def load():
         f.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, i32, vp]
     lib.ss1_sketch.restype = i32
     lib.ss1_sketch.argtypes = [tp, vp, vp, i32, i32, i32, i64, tp, vp]
+    lib.ss1_project.restype = i32
+    lib.ss1_project.argtypes = [tp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     _LIB = lib
@@ -219,3 +222,17 @@ def sketch(x, hash_, sign, c: int, BK: int, BN: int, N: int, z=None, out_dtype=N
                            ctypes.byref(dz), _stream(stream))
     _check(st, "ss1_sketch")
     return z
+
+
+def project(W, hash_, sign, c: int, BK: int, BN: int, W_c=None, stream=None):
+    """Least-squares projection of a dense [N][K] weight onto the SS1 sharing
+    pattern on the GPU (ss1_project): returns W_c, [N][K/c], W's dtype."""
+    import torch
+    _check_device(W, hash_, sign)
+    if W_c is None:
+        W_c = torch.empty((W.shape[0], W.shape[1] // c), dtype=W.dtype, device=W.device)
+    dw, dc = _desc(W), _desc(W_c)
+    st = load().ss1_project(ctypes.byref(dw), hash_.data_ptr(), sign.data_ptr(), c, BK, BN,
+                            ctypes.byref(dc), _stream(stream))
+    _check(st, "ss1_project")
+    return W_c

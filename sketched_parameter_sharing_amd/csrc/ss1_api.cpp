@@ -188,3 +188,25 @@ extern "C" ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const
     if (!aligned(hash, 4)) return SS1_ERR_ALIGN;
     return ss1::launch_sketch(x->data, x->dtype, hash, sign, M, d, z->data, z->dtype, stream);
 }
+
+extern "C" ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* sign, int32_t c,
+                                  int32_t BK, int32_t BN, ss1_tensor* W_c, void* stream) {
+    if (!W || !W_c) return SS1_ERR_NULL;
+    if (W->reserved != 0 || W_c->reserved != 0) return SS1_ERR_SHAPE;
+    if (!valid_dtype(W->dtype) || !valid_dtype(W_c->dtype)) return SS1_ERR_DTYPE;
+    if (W_c->dtype != W->dtype) return SS1_ERR_DTYPE;
+    const int64_t N = W->rows;
+    const int64_t K = W->cols;
+    Dims d;
+    ss1_status st = ss1::check_chunking(K, N, c, BK, BN, &d);
+    if (st != SS1_OK) return st;
+    if (K >= (int64_t(1) << 30) || N >= (int64_t(1) << 31)) return SS1_ERR_SHAPE;
+    if (N > (int64_t(1) << 40) / K) return SS1_ERR_SHAPE;
+    if (W_c->rows != N || W_c->cols != d.Kc) return SS1_ERR_SHAPE;
+    if (W->dtype == SS1_BF16 ? (BK % 8 != 0) : (BK % 4 != 0)) return SS1_ERR_SHAPE;
+    if (d.G > 65535) return SS1_ERR_SHAPE;
+    if (!W->data || !W_c->data || !hash || !sign) return SS1_ERR_NULL;
+    if (!aligned(W->data, 16) || !aligned(W_c->data, 16)) return SS1_ERR_ALIGN;
+    if (!aligned(hash, 4)) return SS1_ERR_ALIGN;
+    return ss1::launch_project(W->data, W->dtype, hash, sign, d, W_c->data, stream);
+}

@@ -1,0 +1,249 @@
+// Device-side building blocks shared by the SS1 kernels: the plan as kept in
+// LDS, bf16 conversions, the signed sketch accumulation, buffer-resource
+// loads, operand permutes and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace ss1 {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only: global loads still in flight stay in
+// flight (a plain __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Buffer-resource loads: a scalar base (the descriptor) plus a per-lane 32-bit
+// byte offset and a scalar byte offset, so per-step addressing costs no vector
+// instructions.  Reads at or past `bytes` return zero.
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data format, gfx9 family
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kBufferWord3);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// ---------------------------------------------------------------- plan in LDS
+// One 32-bit word per source: element offset of the source chunk inside an x
+// row (bits 0..29), "negative" (bit 31), "absent" (bit 30).
+constexpr uint32_t kNeg = 0x80000000u;
+constexpr uint32_t kAbsent = 0x40000000u;
+constexpr uint32_t kOffMask = 0x3FFFFFFFu;
+
+__device__ __forceinline__ float entry_sign(uint32_t e) {
+    return (e & kAbsent) ? 0.0f : __uint_as_float((e & kNeg) | 0x3F800000u);
+}
+
+__device__ __forceinline__ uint32_t make_entry(int j, int BK, int s) {
+    return static_cast<uint32_t>(j * BK) | (s < 0 ? kNeg : 0u);
+}
+
+// Fills s_src[t*c + r] (t < Jc, r < c) for group g.  From the forward hash the
+// sources of each compressed chunk are gathered with LDS atomics and then put
+// in ascending chunk order; from the inverse index they are copied.  Needs
+// s_cnt[Jc] scratch for the forward form.  Ends with a barrier.
+template <bool FROM_HASH>
+__device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g,
+                           int J, int Jc, int c, int BK, uint32_t* s_src, int* s_cnt) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int32_t* gi = pi + static_cast<size_t>(g) * J;
+    const int8_t* gs = ps + static_cast<size_t>(g) * J;
+    if (FROM_HASH) {
+        for (int e = tid; e < J; e += nt) s_src[e] = kAbsent;
+        for (int t = tid; t < Jc; t += nt) s_cnt[t] = 0;
+        __syncthreads();
+        for (int j = tid; j < J; j += nt) {
+            const int t = gi[j];
+            const int s = gs[j];
+            if (t >= 0 && t < Jc && (s == 1 || s == -1)) {
+                const int slot = atomicAdd(&s_cnt[t], 1);
+                if (slot < c) s_src[t * c + slot] = make_entry(j, BK, s);
+            }
+        }
+        __syncthreads();
+        for (int t = tid; t < Jc; t += nt) {
+            uint32_t* p = s_src + t * c;
+            for (int a = 1; a < c; ++a) {  // insertion sort; absent entries go last
+                const uint32_t v = p[a];
+                int b = a - 1;
+                while (b >= 0 && (p[b] & ~kNeg) > (v & ~kNeg)) {
+                    p[b + 1] = p[b];
+                    --b;
+                }
+                p[b + 1] = v;
+            }
+        }
+    } else {
+        for (int e = tid; e < J; e += nt) {
+            const int j = gi[e];
+            const int s = gs[e];
+            s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------- bf16 helpers
+// A 32-bit word holding two bf16 values (element 2i in the low half): their
+// float32 values are the halves moved to the top of a word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two float32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float round_to_bf16(float v) {
+    return __uint_as_float(pack_bf16(v, 0.0f) << 16);
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float v) {
+    return static_cast<uint16_t>(pack_bf16(v, 0.0f) & 0xFFFFu);
+}
+
+// Accumulates one 16-byte vector of 8 bf16 into acc[8] (first source sets it).
+__device__ __forceinline__ void acc_bf16x8(float (&acc)[8], const uint4& raw, float s, bool first) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float lo = bf16_lo(w[i]);
+        const float hi = bf16_hi(w[i]);
+        if (first) {
+            acc[2 * i] = s * lo;
+            acc[2 * i + 1] = s * hi;
+        } else {
+            acc[2 * i] = fmaf(s, lo, acc[2 * i]);
+            acc[2 * i + 1] = fmaf(s, hi, acc[2 * i + 1]);
+        }
+    }
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&acc)[8]) {
+    uint4 r;
+    r.x = pack_bf16(acc[0], acc[1]);
+    r.y = pack_bf16(acc[2], acc[3]);
+    r.z = pack_bf16(acc[4], acc[5]);
+    r.w = pack_bf16(acc[6], acc[7]);
+    return r;
+}
+
+// Sketch of 8 consecutive elements from one more signed source, in float32.
+// The first source is exact: its sign goes onto the bf16 sign bits (sgnx,
+// 0x80008000 or 0) before the halves are widened.  Each further source is
+// widened and added with a fused multiply-add by its sign (+-1.0, or 0 for a
+// source a malformed plan leaves absent), one float32 rounding per add, in
+// source order.  On gfx950 these integer and FMA instructions issue alongside
+// the MFMAs of other waves; the bf16 dot-product instructions do not, which is
+// why they are not used here.
+__device__ __forceinline__ void acc_sign8(float (&acc)[8], const uint4& raw, float sgn, uint32_t sgnx,
+                                          bool first) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (first) {
+            const uint32_t v = w[i] ^ sgnx;
+            acc[2 * i] = bf16_lo(v);
+            acc[2 * i + 1] = bf16_hi(v);
+        } else {
+            acc[2 * i] = fmaf(sgn, bf16_lo(w[i]), acc[2 * i]);
+            acc[2 * i + 1] = fmaf(sgn, bf16_hi(w[i]), acc[2 * i + 1]);
+        }
+    }
+}
+
+// Sign of a plan entry as a mask on a pair of bf16 values.
+__device__ __forceinline__ uint32_t entry_sign_xor(uint32_t e) {
+    return (e & kNeg) ? 0x80008000u : 0u;
+}
+
+// Plans of `count` consecutive groups starting at g0, one J-entry row per
+// group in s_src (same encoding as stage_plan).  s_cnt needs count*Jc ints in
+// the forward form.  Ends with a barrier.
+template <bool FROM_HASH>
+__device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g0,
+                            int count, int J, int Jc, int c, int BK, uint32_t* s_src, int* s_cnt) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int total = count * J;
+    const int32_t* gi = pi + static_cast<size_t>(g0) * J;
+    const int8_t* gs = ps + static_cast<size_t>(g0) * J;
+    if (FROM_HASH) {
+        for (int e = tid; e < total; e += nt) s_src[e] = kAbsent;
+        for (int e = tid; e < count * Jc; e += nt) s_cnt[e] = 0;
+        __syncthreads();
+        for (int e = tid; e < total; e += nt) {
+            const int gl = e / J;
+            const int j = e - gl * J;
+            const int t = gi[e];
+            const int s = gs[e];
+            if (t >= 0 && t < Jc && (s == 1 || s == -1)) {
+                const int slot = atomicAdd(&s_cnt[gl * Jc + t], 1);
+                if (slot < c) s_src[gl * J + t * c + slot] = make_entry(j, BK, s);
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < count * Jc; e += nt) {
+            uint32_t* p = s_src + e * c;  // (gl, t) -> row gl*J + t*c
+            for (int a = 1; a < c; ++a) {
+                const uint32_t v = p[a];
+                int b = a - 1;
+                while (b >= 0 && (p[b] & ~kNeg) > (v & ~kNeg)) {
+                    p[b + 1] = p[b];
+                    --b;
+                }
+                p[b + 1] = v;
+            }
+        }
+    } else {
+        for (int e = tid; e < total; e += nt) {
+            const int j = gi[e];
+            const int s = gs[e];
+            s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
+        }
+    }
+    __syncthreads();
+}
+
+// W_c fragments are read from global memory in a coalesced pattern (lane l
+// reads 16 bytes at row l/4, k-chunk l%4, so each group of 4 lanes reads 64
+// contiguous bytes of one row) and then moved into the MFMA operand pattern
+// (lane l holds row l%16, k-chunk l/16) with a fixed cross-lane permutation.
+// Read straight in the operand pattern, consecutive lanes would touch
+// different rows and every lane quad different cache lines.
+__device__ __forceinline__ int coalesced_src_lane_bytes(int lane) {
+    return ((lane & 15) * 4 + (lane >> 4)) * 4;
+}
+
+__device__ __forceinline__ uint4 to_operand_layout(const uint4& v, int src_bytes) {
+    uint4 r;
+    r.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.x)));
+    r.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.y)));
+    r.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.z)));
+    r.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src_bytes, static_cast<int>(v.w)));
+    return r;
+}
+
+// Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
+// Renumber so that each XCD works through one contiguous range of tiles and
+// tiles sharing an input row band stay in one L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+    const int per = n / 8;
+    if (b >= per * 8) return b;
+    return (b % 8) * per + b / 8;
+}
+
+}  // namespace dev
+}  // namespace ss1

@@ -47,5 +47,8 @@ ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
                          int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
+// Projection of a dense [N][K] weight onto the sharing pattern (ss1_project.hip).
+ss1_status launch_project(const void* W, int32_t dtype, const int32_t* hash, const int8_t* sign, const Dims& d,
+                          void* Wc, void* stream);
 
 }  // namespace ss1

@@ -160,3 +160,20 @@ def make_inputs(wl: Workload, M: int | None = None, integer: bool = False,
         wb = f32_to_bf16_bits(w)
         return Tensors(bf16_bits_to_f32(xb), bf16_bits_to_f32(wb), xb, wb)
     return Tensors(x, w)
+
+
+def dense_weight_seed(wl: Workload) -> int:
+    """Seed of the dense [N][K] weight that a projection test or benchmark
+    projects onto the layer's sharing pattern."""
+    return 0x55340000 + 256 * wl.cfg + wl.layer
+
+
+def make_dense_weight(wl: Workload, integer: bool = False):
+    """A dense [N][K] weight for projection: N(0, 0.02) (the GPT-2 init scale),
+    or integers in {-4..4}.  Returns (float32 values, uint16 bf16 bits or
+    None); for bf16 layers the values are the exact bf16 values."""
+    w = draw("int4" if integer else "normal002", dense_weight_seed(wl), (wl.N, wl.K))
+    if wl.dtype == "bf16":
+        b = f32_to_bf16_bits(w)
+        return bf16_bits_to_f32(b), b
+    return w, None

@@ -184,6 +184,33 @@ def test_sketch_argument_checks():
     assert lib.ss1_sketch(None, A, A, 2, 64, 64, 128, None, None) == _lib.ERR_NULL
 
 
+def _pj(W, Wc, h=A, s=A, c=2, BK=64, BN=64):
+    lib = _lib.load()
+    return lib.ss1_project(ctypes.byref(W), h, s, c, BK, BN, ctypes.byref(Wc), None)
+
+
+def test_project_argument_checks():
+    assert _pj(T(128, 256), T(127, 128)) == _lib.ERR_SHAPE           # W_c rows != N
+    assert _pj(T(128, 256), T(128, 64)) == _lib.ERR_SHAPE            # W_c cols != K/c
+    assert _pj(T(128, 250), T(128, 125)) == _lib.ERR_SHAPE           # K % BK
+    assert _pj(T(100, 256), T(100, 128)) == _lib.ERR_SHAPE           # N % BN
+    assert _pj(T(128, 256), T(128, 128), c=3) == _lib.ERR_SHAPE      # J % c
+    assert _pj(T(128, 256), T(128, 128), BK=4, c=2) == _lib.ERR_SHAPE  # bf16 needs BK % 8
+    assert _pj(T(128, 256, _lib.F32), T(128, 128, _lib.BF16)) == _lib.ERR_DTYPE
+    assert _pj(T(128, 256, 7), T(128, 128, 7)) == _lib.ERR_DTYPE
+    assert _pj(T(128, 256, reserved=1), T(128, 128)) == _lib.ERR_SHAPE
+    assert _pj(T(128, 256), T(128, 128), h=None) == _lib.ERR_NULL
+    assert _pj(T(128, 256), T(128, 128), s=None) == _lib.ERR_NULL
+    assert _pj(T(128, 256, data=None), T(128, 128)) == _lib.ERR_NULL
+    assert _pj(T(128, 256, data=A + 2), T(128, 128)) == _lib.ERR_ALIGN
+    assert _pj(T(128, 256), T(128, 128, data=A + 8)) == _lib.ERR_ALIGN
+    assert _pj(T(128, 256), T(128, 128), h=A + 2) == _lib.ERR_ALIGN
+    assert _pj(T(65536 * 64, 128), T(65536 * 64, 64)) == _lib.ERR_SHAPE  # G above 65535
+    lib = _lib.load()
+    assert lib.ss1_project(None, A, A, 2, 64, 64, ctypes.byref(T(128, 128)), None) == _lib.ERR_NULL
+    assert lib.ss1_project(ctypes.byref(T(128, 256)), A, A, 2, 64, 64, None, None) == _lib.ERR_NULL
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 256, dtype=torch.bfloat16)
