@@ -1,4 +1,5 @@
-"""CPU oracle for the SS1 forward and weight projection (test infrastructure only).
+"""CPU oracle for the SS1 forward, the SS1 MLP pair and the weight projection
+(test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package; the product path never does.
@@ -12,7 +13,9 @@ from .ss1_oracle import (  # noqa: F401
     flops,
     forward,
     forward_mirror,
+    gelu,
     identity_plan,
+    mlp_forward,
     plan,
     plan_index,
     project,

@@ -47,6 +47,8 @@ Nothing here is blocked, fused or reordered beyond the definition.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 _MASK64 = (1 << 64) - 1
@@ -364,6 +366,35 @@ def project_rounded(W, hash_, sign, K: int, N: int, c: int, BK: int, BN: int,
                 v = _round_f32_to_bf16(v)
             Wc[rows, t * BK:(t + 1) * BK] = v.astype(np.float64)
     return Wc
+
+
+def gelu(v) -> np.ndarray:
+    """GELU in its defining form, v * Phi(v) with Phi the standard normal
+    distribution function, float64.  Phi is taken as 0.5 * erfc(-v / sqrt(2))
+    (the same function as 0.5 * (1 + erf(v / sqrt(2))) without its
+    cancellation for large negative v).  The pages name the GPT-2 MLP
+    (up-projection, activation, down-projection) without fixing the GELU
+    variant; the defining form is the plain reading."""
+    v = np.asarray(v, dtype=np.float64)
+    erfc = np.vectorize(math.erfc, otypes=[np.float64])
+    return v * 0.5 * erfc(-v / math.sqrt(2.0))
+
+
+def mlp_forward(x, up: dict, down: dict, round_h_to_bf16: bool = False):
+    """The SS1 MLP pair: h = GELU(SS1_up(x)), y = SS1_down(h), float64.
+
+    ``up`` and ``down`` hold Wc, hash, sign, K, N, c, BK, BN of each layer
+    (down.K == up.N).  With ``round_h_to_bf16`` the intermediate h is rounded
+    to bf16 (nearest, ties to even) before the down-projection, as a device
+    path that keeps h in bf16 does.  Returns (h, y)."""
+    if down["K"] != up["N"]:
+        raise ValueError("down.K must equal up.N")
+    h = gelu(forward(x, up["Wc"], up["hash"], up["sign"], up["K"], up["N"], up["c"], up["BK"], up["BN"]))
+    if round_h_to_bf16:
+        h = _round_f32_to_bf16(h.astype(np.float32)).astype(np.float64)
+    y = forward(h, down["Wc"], down["hash"], down["sign"], down["K"], down["N"], down["c"], down["BK"],
+                down["BN"])
+    return h, y
 
 
 def flops(M: int, K: int, N: int, c: int) -> dict:

@@ -441,3 +441,59 @@ def test_project_rounded_mirror():
     ex3 = oracle.project(W3, h3, s3, K3, N, c3, 4, BN)
     m3 = oracle.project_rounded(W3, h3, s3, K3, N, c3, 4, BN, False)
     assert np.array_equal(m3, ex3.astype(np.float32).astype(np.float64))
+
+
+# ------------------------------------------------------------ MLP pair pins
+def test_gelu_against_normal_cdf_and_identities():
+    from scipy.stats import norm
+    v = np.concatenate([np.linspace(-8, 8, 161), [-1e-3, 1e-3, 30.0, -30.0]])
+    np.testing.assert_allclose(oracle.gelu(v), v * norm.cdf(v), rtol=1e-12, atol=1e-300)
+    # GELU(v) - GELU(-v) = v (Phi(v) + Phi(-v) = 1); GELU(0) = 0
+    np.testing.assert_allclose(oracle.gelu(v) - oracle.gelu(-v), v, rtol=1e-14, atol=1e-14)
+    assert oracle.gelu(0.0) == 0.0
+    assert oracle.gelu(30.0) == 30.0 and abs(oracle.gelu(-30.0)) < 1e-190
+
+
+def _layer(seed, K, N, c, BK, BN, identity=False, integer=False):
+    h, s = oracle.identity_plan(K, N, BK, BN) if identity else oracle.plan(seed, K, N, c, BK, BN)
+    g = np.random.default_rng(seed)
+    Wc = (g.integers(-2, 3, size=(N, K // c)).astype(np.float64) if integer
+          else g.standard_normal((N, K // c)) * 0.05)
+    return {"Wc": Wc, "hash": h, "sign": s, "K": K, "N": N, "c": c, "BK": BK, "BN": BN}
+
+
+def test_mlp_identity_plans_equal_dense_mlp():
+    from scipy.stats import norm
+    up = _layer(1, 64, 96, 1, 8, 16, identity=True)
+    down = _layer(2, 96, 32, 1, 8, 16, identity=True)
+    x = np.random.default_rng(3).standard_normal((7, 64))
+    a = x @ up["Wc"].T
+    y_ref = (a * norm.cdf(a)) @ down["Wc"].T
+    h, y = oracle.mlp_forward(x, up, down)
+    np.testing.assert_allclose(y, y_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mlp_equals_dense_expansions():
+    from scipy.stats import norm
+    up = _layer(4, 128, 64, 2, 16, 16)
+    down = _layer(5, 64, 48, 4, 8, 16)
+    x = np.random.default_rng(6).standard_normal((5, 128))
+    Wu = oracle.dense_expand(up["Wc"], up["hash"], up["sign"], 128, 64, 2, 16, 16)
+    Wd = oracle.dense_expand(down["Wc"], down["hash"], down["sign"], 64, 48, 4, 8, 16)
+    a = x @ Wu.T
+    h, y = oracle.mlp_forward(x, up, down)
+    np.testing.assert_allclose(h, a * norm.cdf(a), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(y, (a * norm.cdf(a)) @ Wd.T, rtol=1e-11, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.mlp_forward(x, up, _layer(7, 32, 48, 2, 8, 16))
+
+
+def test_mlp_rounded_h_is_bf16():
+    up = _layer(8, 64, 32, 2, 8, 16)
+    down = _layer(9, 32, 16, 2, 8, 16)
+    x = np.random.default_rng(10).standard_normal((4, 64))
+    h, y = oracle.mlp_forward(x, up, down, round_h_to_bf16=True)
+    bits = f32_to_bf16_bits(h.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f32(bits).astype(np.float64), h)
+    h0, _ = oracle.mlp_forward(x, up, down)
+    assert np.all(np.abs(h - h0) <= 2.0 ** -8 * np.abs(h0))
