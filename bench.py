@@ -17,6 +17,10 @@ oracle timed on a bounded sample of the same workload.
                     [--algo auto] [--index] [--warm] [--no-cpu-baseline]
                     [--sweep FILE]   # one extra JSON line per workload into FILE
     python bench.py --copy-calibration   # a plain 256 MiB device copy, for counters
+    python bench.py --op mlp [--mlp-c 4] [--row-chunk 8192]
+        # ss1_mlp_forward: the GPT-2 L MLP pair (8192 x 1280 -> 5120 -> 1280,
+        # GELU between) at compression c, with a c sweep against the dense
+        # pair (torch bf16 matmuls and GELU at the same shapes)
     python bench.py --op project [--workload llama_gateup_m1]
         # ss1_project instead: least-squares projection of the layer's dense
         # [N][K] weight onto its sharing pattern, GB/s against the HBM roofline
@@ -238,6 +242,111 @@ def cpu_baseline_project(wl, budget_s=10.0):
                       f"(the sample's algorithmic bytes / time)"}
 
 
+MLP_SHAPE = {"M": 8192, "K": 1280, "N1": 5120, "N2": 1280, "BK": 64, "BN": 64}  # GPT-2 L MLP pair
+
+
+def mlp_work(c, m=MLP_SHAPE):
+    M, K, N1, N2 = m["M"], m["K"], m["N1"], m["N2"]
+    dense = 2 * M * K * N1 + 2 * M * N1 * N2
+    return {"dense_flops": dense, "compressed_flops": dense // c,
+            "bytes": 2 * (M * K + N1 * K // c + N2 * N1 // c + M * N2)}
+
+
+def mlp_bk(c, m=MLP_SHAPE):
+    """Chunk width of the pair at compression c: 64, or 32 where K/64 chunks
+    do not split into c equal parts (c = 8 at K = 1280)."""
+    return m["BK"] if (m["K"] // m["BK"]) % c == 0 else m["BK"] // 2
+
+
+def make_mlp(c, m=MLP_SHAPE, seed=0x5f00):
+    """Device tensors of an SS1 MLP pair at compression c (seeded inputs)."""
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    from ss1_inputs import draw, f32_to_bf16_bits
+    M, K, N1, N2, BK, BN = m["M"], m["K"], m["N1"], m["N2"], mlp_bk(c, m), m["BN"]
+    x = to_dev(f32_to_bf16_bits(draw("normal", seed, (M, K))), "bf16")
+    layers = []
+    for i, (k, n) in enumerate(((K, N1), (N1, N2))):
+        s = seed + 1 + i + 16 * c
+        w = to_dev(f32_to_bf16_bits(draw("normal002", s, (n, k // c))), "bf16")
+        p = ss1.DevicePlan.make(s, k, n, c, BK, BN)
+        layers.append((w, p.hash, p.sign, c, BK, BN))
+    return x, layers[0], layers[1]
+
+
+def time_events(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def time_mlp(c, steps, warmup, row_chunk):
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    x, up, down = make_mlp(c)
+    h = torch.empty((min(row_chunk, x.shape[0]), up[0].shape[0]), dtype=x.dtype, device="cuda")
+    y = torch.empty((x.shape[0], down[0].shape[0]), dtype=x.dtype, device="cuda")
+    return time_events(lambda: ss1.mlp_forward(x, up, down, h=h, y=y), steps, warmup)
+
+
+def time_dense_mlp(steps, warmup, m=MLP_SHAPE):
+    """The dense pair at the same shapes: torch (hipBLASLt) bf16 matmuls and
+    torch's erf GELU, weights [out][in] as a linear layer's."""
+    import torch
+    from ss1_inputs import draw, f32_to_bf16_bits
+    M, K, N1, N2 = m["M"], m["K"], m["N1"], m["N2"]
+    x = to_dev(f32_to_bf16_bits(draw("normal", 0x5f00, (M, K))), "bf16")
+    w1 = to_dev(f32_to_bf16_bits(draw("normal002", 0x5f01, (N1, K))), "bf16")
+    w2 = to_dev(f32_to_bf16_bits(draw("normal002", 0x5f02, (N2, N1))), "bf16")
+    w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
+    gelu = torch.nn.GELU()
+    return time_events(lambda: torch.matmul(gelu(torch.matmul(x, w1t)), w2t), steps, warmup)
+
+
+def cpu_baseline_mlp(c, budget_s=10.0, m=MLP_SHAPE):
+    """The oracle's MLP pair, float64, on a bounded sample of rows."""
+    import oracle
+    from ss1_inputs import draw, f32_to_bf16_bits, bf16_bits_to_f32
+    K, N1, N2, BK, BN = m["K"], m["N1"], m["N2"], mlp_bk(c, m), m["BN"]
+
+    def layer(k, n, s):
+        w = bf16_bits_to_f32(f32_to_bf16_bits(draw("normal002", s, (n, k // c)))).astype(np.float64)
+        h, sg = oracle.plan(s, k, n, c, BK, BN)
+        return {"Wc": w, "hash": h, "sign": sg, "K": k, "N": n, "c": c, "BK": BK, "BN": BN}
+
+    up, down = layer(K, N1, 0x5f00 + 1 + 16 * c), layer(N1, N2, 0x5f00 + 2 + 16 * c)
+    rows, t = 16, 0.0
+    while True:
+        x = draw("normal", 0x5f00, (rows, K)).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.mlp_forward(x, up, down)
+        t = time.perf_counter() - t0
+        if t > budget_s / 3 or rows >= m["M"]:
+            break
+        rows = min(m["M"], rows * 4)
+    flops = mlp_work(c, dict(m, M=rows))["dense_flops"]
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        nt = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if nt:
+            cores = max(nt)
+    except Exception:
+        pass
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} of {m['M']} rows of the GPT-2 L MLP pair at c={c}, float64 NumPy oracle, "
+                      f"{t:.3f} s (dense-equivalent FLOPs of the sample / time)"}
+
+
 def kernel_name(wl, algo):
     """The kernel a call runs: the requested one, or what the library picks."""
     if algo != "auto":
@@ -289,7 +398,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help=f"default: {HEADLINE} (forward), {PROJECT_HEADLINE} (project)")
-    ap.add_argument("--op", default="forward", choices=["forward", "project"])
+    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp"])
+    ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
+    ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
@@ -385,6 +496,43 @@ def main():
                 f.write(json.dumps(rec) + "\n")
                 print(f"sweep project {name}: {rec['ms_per_step'] * 1e3:.1f} us, "
                       f"hbm frac {rec['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+
+    if args.op == "mlp":
+        c = args.mlp_c
+        t = time_mlp(c, args.steps, args.warmup, args.row_chunk)
+        wk = mlp_work(c)
+        t_dense = time_dense_mlp(max(20, args.steps // 2), max(5, args.warmup // 2))
+        sweep = []
+        for cc in (2, 4, 8):
+            tc = t if cc == c else time_mlp(cc, max(20, args.steps // 2), max(5, args.warmup // 2), args.row_chunk)
+            sweep.append({"c": cc, "BK": mlp_bk(cc), "ms": tc * 1e3, "dense_equiv_tflops": mlp_work(cc)["dense_flops"] / tc / 1e12,
+                          "speedup_vs_dense": t_dense / tc})
+        t_f = wk["compressed_flops"] / PEAK_MFMA_BF16
+        t_b = wk["bytes"] / PEAK_HBM
+        mf = {"bound": "mfma", "achieved": wk["compressed_flops"] / t / 1e12, "peak": PEAK_MFMA_BF16 / 1e12,
+              "unit": "TFLOP/s"}
+        hb = {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        for r in (mf, hb):
+            r["frac"] = r["achieved"] / r["peak"]
+        roof = dict(mf if t_f >= t_b else hb)
+        roof["other"] = hb if t_f >= t_b else mf
+        roof.update({"traffic": None, "t_lower_us": max(t_f, t_b) * 1e6,
+                     "note": "whole pair (both projections and the GELU epilogue) per call"})
+        rec = {
+            "metric": "SS1 MLP pair (up, GELU, down) dense-equiv TFLOP/s + % of MFMA/HBM roofline",
+            "value": wk["dense_flops"] / t / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) compressed weights, seeded balanced plans)",
+            "config": {"workload": f"gpt2l_mlp_pair_c{c}", **MLP_SHAPE, "BK": mlp_bk(c), "c": c,
+                       "row_chunk": args.row_chunk,
+                       "cache": "warm (one buffer set; h chunk stays in the MALL)",
+                       "dense_pair_ms": t_dense * 1e3, "c_sweep": sweep},
+            "roofline": roof,
+        }
+        rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mlp(c)
+        print(json.dumps(rec), flush=True)
+        return
 
     if args.op == "project":
         name = args.workload or PROJECT_HEADLINE

@@ -82,6 +82,18 @@ typedef struct {
     int64_t cols;
 } ss1_tensor;
 
+/* One SS1 layer for the calls that take several: its compressed weight and
+   its plan.  All pointers are the caller's; the library keeps none. */
+typedef struct {
+    ss1_tensor W_c;        /* [N][K/c] row-major, DEVICE */
+    const int32_t* hash;   /* DEVICE [G][J] as written by ss1_plan */
+    const int8_t* sign;    /* DEVICE [G][J] */
+    int32_t c;
+    int32_t BK;
+    int32_t BN;
+    int32_t reserved;      /* must be 0 */
+} ss1_layer;
+
 /* Largest number of input chunks J = K/BK per group the device kernels take
    (their plan is staged in LDS). */
 #define SS1_MAX_CHUNKS 4096
@@ -225,6 +237,33 @@ ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* si
 ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* sign,
                        int32_t c, int32_t BK, int32_t BN,
                        ss1_tensor* W_c, void* stream);
+
+/*
+ * ss1_mlp_forward -- DEVICE, asynchronous on `stream`.  The SS1 MLP pair of a
+ * transformer block (the SS1 summary page's GPT-2 results replace its linear
+ * layers; "Measured effects": GPT-2 M/L end-to-end latency with SS1 layers):
+ *   h = GELU(SS1_up(x)),  y = SS1_down(h),
+ * with GELU in its erf form v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))),
+ * applied to the float32 accumulator of the up-projection before h is
+ * rounded to its dtype.  Each projection is computed as by ss1_forward.
+ *   x    : [M][K]               F32 or BF16 (all tensors share the dtype)
+ *   up   : W_c [N1][K/c1], plan of a K -> N1 layer
+ *   down : W_c [N2][N1/c2], plan of an N1 -> N2 layer
+ *   h    : [R][N1] workspace, 1 <= R (R = h->rows; any R when M == 0): the
+ *          rows of x are processed in chunks of R, each chunk's h written
+ *          here and read back by the down-projection.  A chunk of a few
+ *          thousand rows keeps h inside the device's last-level cache
+ *          instead of a full [M][N1] round trip through HBM; with R >= M, h
+ *          holds GELU(SS1_up(x)) for every row when the call completes.
+ *   y    : [M][N2], written
+ * Requirements: each layer as for ss1_forward (chunking, alignment of x, h, y
+ * and both W_c to 16 bytes, hash 4-byte aligned, balanced plans); x, h and y
+ * must not overlap.  M == 0 enqueues nothing.
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (every
+ * check runs for both layers before any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
+                           ss1_tensor* h, ss1_tensor* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,10 +14,11 @@ from ._lib import (  # noqa: F401
     forward,
     forward_idx,
     load,
+    mlp_forward,
     plan,
     plan_index,
-    select_algo,
     project,
+    select_algo,
     sketch,
     version,
 )

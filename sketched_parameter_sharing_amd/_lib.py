@@ -28,7 +28,7 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
-           "ss1_project")
+           "ss1_project", "ss1_mlp_forward")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -42,6 +42,12 @@ class SS1Error(RuntimeError):
 class Tensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("W_c", Tensor), ("hash", ctypes.c_void_p), ("sign", ctypes.c_void_p),
+                ("c", ctypes.c_int32), ("BK", ctypes.c_int32), ("BN", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -78,6 +84,8 @@ def load():
     lib.ss1_sketch.argtypes = [tp, vp, vp, i32, i32, i32, i64, tp, vp]
     lib.ss1_project.restype = i32
     lib.ss1_project.argtypes = [tp, vp, vp, i32, i32, i32, tp, vp]
+    lib.ss1_mlp_forward.restype = i32
+    lib.ss1_mlp_forward.argtypes = [tp, ctypes.POINTER(Layer), ctypes.POINTER(Layer), tp, tp, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     _LIB = lib
@@ -195,6 +203,30 @@ def forward_idx(x, W_c, idx, isign, c: int, BK: int, BN: int, y=None, algo: str 
                                       c, BK, BN, ctypes.byref(dy), ALGOS[algo], _stream(stream))
     _check(st, "ss1_forward_idx")
     return y
+
+
+def mlp_forward(x, up, down, h=None, y=None, row_chunk: int | None = None, stream=None):
+    """SS1 MLP pair on the GPU (ss1_mlp_forward): y = SS1_down(GELU(SS1_up(x))).
+    ``up`` and ``down`` are (W_c, hash, sign, c, BK, BN) tuples of device
+    tensors and ints.  ``h`` is the [R][N1] workspace (allocated with
+    R = row_chunk, default all rows, when None); returns (h, y)."""
+    import torch
+    Wu, hu, su, cu, BKu, BNu = up
+    Wd, hd, sd, cd, BKd, BNd = down
+    _check_device(x, Wu, hu, su, Wd, hd, sd)
+    M = x.shape[0]
+    if h is None:
+        R = max(1, min(M, row_chunk or M))
+        h = torch.empty((R, Wu.shape[0]), dtype=x.dtype, device=x.device)
+    if y is None:
+        y = torch.empty((M, Wd.shape[0]), dtype=x.dtype, device=x.device)
+    lu = Layer(_desc(Wu), hu.data_ptr(), su.data_ptr(), cu, BKu, BNu, 0)
+    ld = Layer(_desc(Wd), hd.data_ptr(), sd.data_ptr(), cd, BKd, BNd, 0)
+    dx, dh, dy = _desc(x), _desc(h), _desc(y)
+    st = load().ss1_mlp_forward(ctypes.byref(dx), ctypes.byref(lu), ctypes.byref(ld), ctypes.byref(dh),
+                                ctypes.byref(dy), _stream(stream))
+    _check(st, "ss1_mlp_forward")
+    return h, y
 
 
 def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16") -> str:

@@ -210,3 +210,48 @@ extern "C" ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, cons
     if (!aligned(hash, 4)) return SS1_ERR_ALIGN;
     return ss1::launch_project(W->data, W->dtype, hash, sign, d, W_c->data, stream);
 }
+
+extern "C" ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
+                                      ss1_tensor* h, ss1_tensor* y, void* stream) {
+    if (!x || !up || !down || !h || !y) return SS1_ERR_NULL;
+    if (up->reserved != 0 || down->reserved != 0 || h->reserved != 0) return SS1_ERR_SHAPE;
+    const int64_t M = x->rows;
+    const int64_t R = h->rows;
+    if (M < 0) return SS1_ERR_SHAPE;
+    if (M > 0 && R < 1) return SS1_ERR_SHAPE;
+    const int64_t RC = M > 0 ? (R < M ? R : M) : 0;  // rows per chunk
+    // whole-call checks: the up layer maps x to h's columns, the down layer
+    // h's columns to y, on descriptors of the first chunk's shape
+    ss1_tensor xc = *x, hc = *h, yc = *y;
+    xc.rows = RC;
+    hc.rows = RC;
+    yc.rows = RC;
+    ForwardArgs au, ad;
+    ss1_status st = check_forward(&xc, &up->W_c, up->hash, up->sign, up->c, up->BK, up->BN, &hc, PlanForm::Hash,
+                                  stream, &au);
+    if (st != SS1_OK) return st;
+    st = check_forward(&hc, &down->W_c, down->hash, down->sign, down->c, down->BK, down->BN, &yc, PlanForm::Hash,
+                       stream, &ad);
+    if (st != SS1_OK) return st;
+    // the full-size x and y, and the workspace's own shape
+    if (y->rows != M || y->cols != down->W_c.rows) return SS1_ERR_SHAPE;
+    if (h->cols != up->W_c.rows || h->dtype != x->dtype) return SS1_ERR_SHAPE;
+    if (M > 0 && x->cols > (int64_t(1) << 40) / M) return SS1_ERR_SHAPE;
+    if (M > 0 && y->cols > (int64_t(1) << 40) / M) return SS1_ERR_SHAPE;
+    if (M > (int64_t(1) << 31) - 1) return SS1_ERR_SHAPE;
+    if (M == 0) return SS1_OK;
+    const size_t e = x->dtype == SS1_BF16 ? 2 : 4;
+    au.act = ss1::kActGelu;
+    for (int64_t r0 = 0; r0 < M; r0 += RC) {
+        const int64_t rows = (M - r0 < RC) ? (M - r0) : RC;
+        au.x = static_cast<const char*>(x->data) + static_cast<size_t>(r0) * x->cols * e;
+        au.M = rows;
+        ad.y = static_cast<char*>(y->data) + static_cast<size_t>(r0) * y->cols * e;
+        ad.M = rows;
+        st = launch_algo(au, auto_algo(au));
+        if (st != SS1_OK) return st;
+        st = launch_algo(ad, auto_algo(ad));
+        if (st != SS1_OK) return st;
+    }
+    return SS1_OK;
+}

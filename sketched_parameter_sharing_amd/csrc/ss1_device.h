@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include "ss1_internal.h"
+
 namespace ss1 {
 namespace dev {
 
@@ -243,6 +245,15 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
     const int per = n / 8;
     if (b >= per * 8) return b;
     return (b % 8) * per + b / 8;
+}
+
+// Output activation applied in the epilogues, on the float32 accumulator
+// before the output rounding: kActNone, or kActGelu for GELU in its erf
+// form, v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))) (erff: the device math
+// library's single-precision error function).
+__device__ __forceinline__ float apply_act(float v, int act) {
+    if (act == kActGelu) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+    return v;
 }
 
 }  // namespace dev

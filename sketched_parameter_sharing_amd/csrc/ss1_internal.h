@@ -31,7 +31,12 @@ struct ForwardArgs {
     Dims d;
     int32_t dtype;  // ss1_dtype
     void* stream;
+    int32_t act = 0;  // epilogue activation: kActNone or kActGelu (erf form)
 };
+
+// Epilogue activation codes (ForwardArgs::act; applied by dev::apply_act).
+constexpr int32_t kActNone = 0;
+constexpr int32_t kActGelu = 1;
 
 // Which kernels can run a call (host-side checks only).
 bool fused_supported(const ForwardArgs& a);

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void generic_kernel(const TIn* __restrict__ x,
                                                       const int8_t* __restrict__ ps,
                                                       void* __restrict__ y, int M, int K, int N,
                                                       int J, int Jc, int c, int BK, int BN,
-                                                      int KW, int n_sub) {
+                                                      int KW, int n_sub, int act) {
     constexpr int TM = 64, TN = 64, KWMAX = 32;
     __shared__ float zs[KWMAX][TM + 4];
     __shared__ float ws[KWMAX][TN + 4];
@@ -191,9 +191,9 @@ __global__ __launch_bounds__(256) void generic_kernel(const TIn* __restrict__ x,
             if (cc >= width) continue;
             const size_t o = static_cast<size_t>(m) * N + n0 + cc;
             if (BF16_SKETCH_AND_OUT)
-                static_cast<uint16_t*>(y)[o] = to_bf16_bits(acc[i][j]);
+                static_cast<uint16_t*>(y)[o] = to_bf16_bits(apply_act(acc[i][j], act));
             else
-                static_cast<float*>(y)[o] = acc[i][j];
+                static_cast<float*>(y)[o] = apply_act(acc[i][j], act);
         }
     }
 }
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ pi,
                                                     const int8_t* __restrict__ ps,
                                                     uint16_t* __restrict__ y, int M, int K, int N,
-                                                    int J, int Jc, int c_rt, int BK, int n_mt) {
+                                                    int J, int Jc, int c_rt, int BK, int n_mt, int act) {
     static_assert(WM * WN == 4, "four waves");
     constexpr int TMW = MT / WM, TNW = BN / WN;  // wave tile
     constexpr int FM = TMW / 16, FN = TNW / 16;  // 16x16 MFMA blocks per wave
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int m = m0 + wm * TMW + i * 16 + (lane >> 4) * 4 + q;
-                if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(acc[i][j][q]);
+                if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(acc[i][j][q], act));
             }
         }
     }
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
                                                          const int8_t* __restrict__ ps,
                                                          uint16_t* __restrict__ y, int M, int K,
                                                          int N, int J, int Jc, int c_rt, int BK,
-                                                         int BN) {
+                                                         int BN, int act) {
     extern __shared__ uint32_t smem[];
     f32x4* red = reinterpret_cast<f32x4*>(smem);                  // [NW][64]
     uint32_t* s_src = smem + NW * 64 * 4;
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = (lane >> 4) * 4 + q;
-            if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(sum[q]);
+            if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(sum[q], act));
         }
     }
 }
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
                                                        const int32_t* __restrict__ pi,
                                                        const int8_t* __restrict__ ps,
                                                        uint16_t* __restrict__ y, int M, int K, int N,
-                                                       int J, int Jc, int c_rt, int BK, int gsplit) {
+                                                       int J, int Jc, int c_rt, int BK, int gsplit, int act) {
     constexpr int RB = MT / 16;  // 16-row blocks of the band
     constexpr int NB = BN / 16;  // 16-neuron blocks of a group
     static_assert(RB * 16 == MT && NB * 16 == BN && NB % 2 == 0, "tile sizes");
@@ -674,10 +674,10 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
 #pragma unroll
             for (int h = 0; h < NB / 2; ++h) {
                 uint4 o;
-                o.x = pack_bf16(acc[rb][2 * h][0], acc[rb][2 * h][1]);
-                o.y = pack_bf16(acc[rb][2 * h][2], acc[rb][2 * h][3]);
-                o.z = pack_bf16(acc[rb][2 * h + 1][0], acc[rb][2 * h + 1][1]);
-                o.w = pack_bf16(acc[rb][2 * h + 1][2], acc[rb][2 * h + 1][3]);
+                o.x = pack_bf16(apply_act(acc[rb][2 * h][0], act), apply_act(acc[rb][2 * h][1], act));
+                o.y = pack_bf16(apply_act(acc[rb][2 * h][2], act), apply_act(acc[rb][2 * h][3], act));
+                o.z = pack_bf16(apply_act(acc[rb][2 * h + 1][0], act), apply_act(acc[rb][2 * h + 1][1], act));
+                o.w = pack_bf16(apply_act(acc[rb][2 * h + 1][2], act), apply_act(acc[rb][2 * h + 1][3], act));
                 *reinterpret_cast<uint4*>(yr + h * 8) = o;
             }
         }
@@ -866,12 +866,12 @@ ss1_status launch_generic_t(const ForwardArgs& a) {
         hipLaunchKernelGGL((generic_kernel<float, false, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
                            dim3(256), lds, st, static_cast<const float*>(a.x),
                            static_cast<const float*>(a.w), a.plan_i, a.plan_s, a.y, (int)a.M,
-                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub);
+                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub, a.act);
     } else {
         hipLaunchKernelGGL((generic_kernel<uint16_t, true, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
                            dim3(256), lds, st, static_cast<const uint16_t*>(a.x),
                            static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, a.y, (int)a.M,
-                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub);
+                           (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, KW, n_sub, a.act);
     }
     return launch_status();
 }
@@ -894,7 +894,7 @@ ss1_status launch_fused_cfg(const ForwardArgs& a) {
                        static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s,
                        static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K, (int)d.N, (int)d.J,
-                       (int)d.Jc, d.c, d.BK, n_mt);
+                       (int)d.Jc, d.c, d.BK, n_mt, a.act);
     return launch_status();
 }
 
@@ -936,7 +936,7 @@ ss1_status launch_smallm_cfg(const ForwardArgs& a) {
                        dim3(NW * 64), lds, static_cast<hipStream_t>(a.stream),
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w),
                        a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K,
-                       (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN);
+                       (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, a.act);
     return launch_status();
 }
 
@@ -1025,7 +1025,7 @@ ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
                        dim3(static_cast<unsigned>(nbands * cfg.gsplit)), dim3(NW * 64), cfg.lds,
                        static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
-                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, cfg.gsplit);
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, cfg.gsplit, a.act);
     return launch_status();
 }
 

@@ -211,6 +211,40 @@ def test_project_argument_checks():
     assert lib.ss1_project(ctypes.byref(T(128, 256)), A, A, 2, 64, 64, None, None) == _lib.ERR_NULL
 
 
+def _layer(rows, cols, c=2, BK=64, BN=64, h=A, s=A, dtype=_lib.BF16, reserved=0):
+    return _lib.Layer(T(rows, cols, dtype), h, s, c, BK, BN, reserved)
+
+
+def _mlp(x, up, down, h, y):
+    lib = _lib.load()
+    return lib.ss1_mlp_forward(ctypes.byref(x), ctypes.byref(up), ctypes.byref(down), ctypes.byref(h),
+                               ctypes.byref(y), None)
+
+
+def test_mlp_forward_argument_checks():
+    up, down = _layer(512, 128), _layer(256, 256)          # 256 -> 512 -> 256, c = 2
+    x, h, y = T(64, 256), T(32, 512), T(64, 256)
+    assert _mlp(T(64, 250), up, down, h, y) == _lib.ERR_SHAPE        # x cols vs up K
+    assert _mlp(x, _layer(512, 100), down, h, y) == _lib.ERR_SHAPE   # up W_c cols != K/c
+    assert _mlp(x, up, _layer(256, 128), h, y) == _lib.ERR_SHAPE     # down K != up N
+    assert _mlp(x, up, down, T(32, 500), y) == _lib.ERR_SHAPE        # h cols != up N
+    assert _mlp(x, up, down, h, T(63, 256)) == _lib.ERR_SHAPE        # y rows != M
+    assert _mlp(x, up, down, h, T(64, 255)) == _lib.ERR_SHAPE        # y cols != down N
+    assert _mlp(x, up, down, T(0, 512), y) == _lib.ERR_SHAPE         # no workspace rows
+    assert _mlp(x, _layer(512, 128, reserved=1), down, h, y) == _lib.ERR_SHAPE
+    assert _mlp(x, up, down, T(32, 512, _lib.F32), y) == _lib.ERR_DTYPE
+    assert _mlp(x, _layer(512, 128, dtype=_lib.F32), down, h, y) == _lib.ERR_DTYPE
+    assert _mlp(x, _layer(512, 128, h=None), down, h, y) == _lib.ERR_NULL
+    assert _mlp(x, up, _layer(256, 256, s=None), h, y) == _lib.ERR_NULL
+    assert _mlp(T(64, 256, data=None), up, down, h, y) == _lib.ERR_NULL
+    assert _mlp(x, up, down, T(32, 512, data=A + 2), y) == _lib.ERR_ALIGN
+    assert _mlp(x, up, down, h, T(64, 256, data=A + 4)) == _lib.ERR_ALIGN
+    assert _mlp(T(0, 256, data=None), up, down, T(0, 512, data=None), T(0, 256, data=None)) == _lib.OK
+    lib = _lib.load()
+    assert lib.ss1_mlp_forward(None, ctypes.byref(up), ctypes.byref(down), ctypes.byref(h),
+                               ctypes.byref(y), None) == _lib.ERR_NULL
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 256, dtype=torch.bfloat16)
