@@ -8,7 +8,11 @@ from .ss1_oracle import (  # noqa: F401
     SplitMix64,
     bf16_bits_to_f64,
     check_plan,
+    E4M3_MAX,
     dense_expand,
+    dequantize_fp8_rows,
+    e4m3_decode,
+    e4m3_encode,
     dims,
     flops,
     forward,
@@ -20,6 +24,7 @@ from .ss1_oracle import (  # noqa: F401
     plan_index,
     project,
     project_rounded,
+    quantize_fp8_rows,
     sketch,
     sketch_rounded,
 )

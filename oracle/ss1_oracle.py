@@ -397,6 +397,82 @@ def mlp_forward(x, up: dict, down: dict, round_h_to_bf16: bool = False):
     return h, y
 
 
+# ------------------------------------------------------------- fp8 weights
+# OCP 8-bit floating point, E4M3 ("FN": no infinities): 1 sign bit, 4
+# exponent bits (bias 7), 3 mantissa bits; exponent field 0 holds subnormals
+# m * 2^-9; S.1111.111 is NaN, so the largest finite magnitude is
+# 1.75 * 2^8 = 448.  (OCP "OFP8 Formats for Deep Learning", v1.0.)
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """Value of each E4M3 code (uint8), float64; NaN for the two NaN codes."""
+    code = np.asarray(code, dtype=np.int64)
+    sgn = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sgn * mag
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Nearest E4M3 code of each finite value, ties to the even mantissa,
+    magnitudes beyond 448 saturated to 448 (uint8).  Walks the value's
+    binade: the quantum is 2^(e-3) for |v| in [2^e, 2^(e+1)), e >= -6, and
+    2^-9 below 2^-6 (subnormals)."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    for idx, x in np.ndenumerate(v):
+        neg = x < 0 or (x == 0 and math.copysign(1.0, x) < 0)
+        a = abs(float(x))
+        if a == 0.0:
+            out[idx] = 0x80 if neg else 0
+            continue
+        e = max(math.floor(math.log2(a)), -6)
+        if 2.0 ** e > a:               # log2 rounding at binade edges
+            e -= 1
+        elif 2.0 ** (e + 1) <= a:
+            e += 1
+        e = max(e, -6)
+        q = 2.0 ** (e - 3)
+        n = a / q                      # exact: a power-of-two scaling
+        r = math.floor(n)
+        frac = n - r
+        if frac > 0.5 or (frac == 0.5 and r % 2 == 1):
+            r += 1
+        mag = r * q
+        if mag > E4M3_MAX:
+            mag = E4M3_MAX
+        if mag < 2.0 ** -6:            # subnormal (or rounded up to 2^-6)
+            code = int(round(mag / 2.0 ** -9))
+            code = 0x08 if code == 8 else code
+        else:
+            ee = math.floor(math.log2(mag))
+            mm = int(round((mag / 2.0 ** ee - 1.0) * 8))
+            code = ((ee + 7) << 3) | mm
+        out[idx] = code | (0x80 if neg else 0)
+    return out
+
+
+def quantize_fp8_rows(Wc):
+    """Per-row E4M3 quantization of a compressed weight, as float32 device
+    arithmetic does it: scale[n] = max_k |Wc[n, k]| / 448 (float32 division,
+    nearest; 1.0 for an all-zero row), q = Wc / scale (float32 division), then
+    the nearest E4M3 code.  Returns (codes uint8 [N][Kc], scale float32 [N])."""
+    W32 = np.asarray(Wc, dtype=np.float32)
+    amax = np.max(np.abs(W32), axis=1).astype(np.float32)
+    scale = np.where(amax > 0, (amax / np.float32(E4M3_MAX)).astype(np.float32), np.float32(1.0))
+    scale = scale.astype(np.float32)
+    q = (W32 / scale[:, None]).astype(np.float32)
+    return e4m3_encode(q.astype(np.float64)), scale
+
+
+def dequantize_fp8_rows(codes, scale) -> np.ndarray:
+    """Float64 weight that a quantized layer stands for: code value * scale."""
+    return e4m3_decode(codes) * np.asarray(scale, dtype=np.float64)[:, None]
+
+
 def flops(M: int, K: int, N: int, c: int) -> dict:
     """Work of one forward: the compressed contraction does 2*M*N*K/c FLOPs
     (the reduction by c the method claims); the dense layer it replaces does

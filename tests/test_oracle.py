@@ -497,3 +497,53 @@ def test_mlp_rounded_h_is_bf16():
     assert np.array_equal(bf16_bits_to_f32(bits).astype(np.float64), h)
     h0, _ = oracle.mlp_forward(x, up, down)
     assert np.all(np.abs(h - h0) <= 2.0 ** -8 * np.abs(h0))
+
+
+# ---------------------------------------------------------------- fp8 pins
+# The E4M3 codec is pinned against torch's float8_e4m3fn (an independent
+# implementation of the same OCP format) on every code and on random values,
+# and on exact midpoints (ties to even) and saturation.
+def test_e4m3_decode_matches_torch_on_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.nanmax(got) == oracle.E4M3_MAX and got[1] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_and_rounds_ties_to_even():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(20)
+    v = np.concatenate([g.standard_normal(4000) * 50, g.standard_normal(2000) * 0.01,
+                        g.uniform(-448, 448, 2000), [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10]])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(v.astype(np.float32).astype(np.float64)), ref)
+    # every midpoint between neighbouring finite positive codes goes to the even code
+    vals = oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    codes = oracle.e4m3_encode(mids)
+    lo = np.arange(0, 0x7E)
+    assert np.array_equal(codes, np.where(lo % 2 == 0, lo, lo + 1))
+    # saturation instead of NaN past the largest finite value
+    assert list(oracle.e4m3_encode([1000.0, -1e9, 464.0])) == [0x7E, 0xFE, 0x7E]
+
+
+def test_quantize_fp8_rows():
+    g = np.random.default_rng(21)
+    W = (g.standard_normal((6, 96)) * 0.02).astype(np.float32)
+    W[3] = 0.0
+    codes, scale = oracle.quantize_fp8_rows(W)
+    assert scale.dtype == np.float32 and scale[3] == 1.0 and not codes[3].any()
+    deq = oracle.dequantize_fp8_rows(codes, scale)
+    for n in (0, 1, 2, 4, 5):
+        assert scale[n] == np.float32(np.max(np.abs(W[n])) / np.float32(448.0))
+        assert np.max(np.abs(oracle.e4m3_decode(codes[n]))) == 448.0      # the row maximum maps to 448
+        # nearest-code error: half a quantum, at most 2^-4 of the value for normals
+        q = W[n].astype(np.float64) / scale[n]
+        err = np.abs(oracle.e4m3_decode(codes[n]) - q)
+        assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) + 1e-12)
+    np.testing.assert_allclose(deq[0], W[0], rtol=2 ** -4, atol=scale[0] * 2.0 ** -10)
