@@ -21,6 +21,9 @@ oracle timed on a bounded sample of the same workload.
         # ss1_mlp_forward: the GPT-2 L MLP pair (8192 x 1280 -> 5120 -> 1280,
         # GELU between) at compression c, with a c sweep against the dense
         # pair (torch bf16 matmuls and GELU at the same shapes)
+    python bench.py --op fp8 [--workload llama_gateup_m1]
+        # ss1_forward_fp8w: the layer with per-row fp8 (E4M3) compressed
+        # weights, against the HBM / MFMA roofline on its own bytes
     python bench.py --op project [--workload llama_gateup_m1]
         # ss1_project instead: least-squares projection of the layer's dense
         # [N][K] weight onto its sharing pattern, GB/s against the HBM roofline
@@ -182,6 +185,50 @@ def project_work(wl):
     e = 2 if wl.dtype == "bf16" else 4
     return {"bytes": e * (wl.N * wl.K + wl.N * wl.Kc) + wl.G * wl.J * 5,
             "adds": wl.N * wl.Kc * (wl.c - 1)}
+
+
+def fp8_work(wl):
+    return {"dense_flops": 2 * wl.M * wl.N * wl.K, "compressed_flops": 2 * wl.M * wl.N * wl.K // wl.c,
+            "bytes": 2 * wl.M * wl.K + wl.N * wl.Kc + 4 * wl.N + 2 * wl.M * wl.N + wl.G * wl.J * 5}
+
+
+def time_fp8(wl, steps, warmup, warm):
+    """ss1_forward_fp8w over rotating buffer sets: (seconds per call, sets)."""
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    from ss1_inputs import make_inputs
+
+    inp = make_inputs(wl)
+    plan = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    Q0, s0 = ss1.quantize_fp8(to_dev(inp.w_bits, "bf16"))
+    set_bytes = fp8_work(wl)["bytes"]
+    nsets = 1 if warm else min(64, max(2, int(np.ceil(512e6 / set_bytes)) + 1))
+    x0 = to_dev(inp.x_bits, "bf16")
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    Qs = [Q0] + [Q0.clone() for _ in range(nsets - 1)]
+    Ss = [s0] + [s0.clone() for _ in range(nsets - 1)]
+    ys = [torch.empty((wl.M, wl.N), dtype=x0.dtype, device="cuda") for _ in range(nsets)]
+
+    def step(i):
+        k = i % nsets
+        ss1.forward_fp8w(xs[k], Qs[k], Ss[k], plan.hash, plan.sign, wl.c, wl.BK, wl.BN, y=ys[k])
+
+    return time_events_i(step, steps, warmup), nsets
+
+
+def time_events_i(fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
 
 
 def time_project(wl, steps, warmup, warm):
@@ -398,7 +445,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help=f"default: {HEADLINE} (forward), {PROJECT_HEADLINE} (project)")
-    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp"])
+    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band"])
@@ -531,6 +578,45 @@ def main():
             "roofline": roof,
         }
         rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mlp(c)
+        print(json.dumps(rec), flush=True)
+        return
+
+    if args.op == "fp8":
+        name = args.workload or "llama_gateup_m1"
+        wl = WORKLOADS[name]
+        t, nsets = time_fp8(wl, args.steps, args.warmup, args.warm)
+        t16, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, args.warm)
+        wk = fp8_work(wl)
+        t_f = wk["compressed_flops"] / PEAK_MFMA_BF16
+        t_b = wk["bytes"] / PEAK_HBM
+        mf = {"bound": "mfma", "achieved": wk["compressed_flops"] / t / 1e12, "peak": PEAK_MFMA_BF16 / 1e12,
+              "unit": "TFLOP/s"}
+        hb = {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        for r in (mf, hb):
+            r["frac"] = r["achieved"] / r["peak"]
+        roof = dict(mf if t_f >= t_b else hb)
+        roof["other"] = hb if t_f >= t_b else mf
+        traffic = recorded_traffic("fp8:" + name)
+        roof.update({"traffic": traffic, "t_lower_us": max(t_f, t_b) * 1e6,
+                     "traffic_vs_algorithmic": (traffic / wk["bytes"]) if traffic else None})
+        rec = {
+            "metric": "SS1 layer with fp8 (E4M3) weights: dense-equiv TFLOP/s + % of MFMA/HBM roofline",
+            "value": wk["dense_flops"] / t / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16 activations, fp8 e4m3 weights",
+            "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) compressed weights quantized per row, "
+                    "seeded balanced plan)",
+            "config": {"workload": name + "_fp8w", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c, "BK": wl.BK,
+                       "BN": wl.BN, "kernel": "smallm" if wl.M <= 16 else "fused",
+                       "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
+                       "bf16_weights_ms": t16 * 1e3, "speedup_vs_bf16_weights": t16 / t},
+            "roofline": roof,
+        }
+        if args.no_cpu_baseline:
+            rec["cpu_baseline"] = None
+        else:
+            rec["cpu_baseline"] = cpu_baseline(wl)
+            rec["cpu_baseline"]["sample"] += " (bf16-weight oracle: the fp8 layer's arithmetic is the same)"
         print(json.dumps(rec), flush=True)
         return
 

@@ -62,7 +62,10 @@ typedef enum {
     SS1_ERR_ALGO = 7       /* the requested kernel cannot run this shape          */
 } ss1_status;
 
-typedef enum { SS1_F32 = 0, SS1_BF16 = 1 } ss1_dtype;
+/* Element types.  SS1_FP8_E4M3 (OCP 8-bit float E4M3, one byte per element)
+   is only for quantized compressed weights (ss1_quantize_fp8,
+   ss1_forward_fp8w). */
+typedef enum { SS1_F32 = 0, SS1_BF16 = 1, SS1_FP8_E4M3 = 2 } ss1_dtype;
 
 /* Kernel choice for ss1_forward_algo / ss1_forward_idx_algo. */
 typedef enum {
@@ -264,6 +267,47 @@ ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* s
  */
 ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
                            ss1_tensor* h, ss1_tensor* y, void* stream);
+
+/*
+ * ss1_quantize_fp8 -- DEVICE, asynchronous on `stream`.  Per-row fp8
+ * quantization of a compressed weight, for ss1_forward_fp8w.  The SS1
+ * summary page ("Measured effects") quantizes SS1 models after training and
+ * finds quality unchanged; its "Limitations" say quantized SS1 kernels were
+ * not implemented.  This library's scheme (a reading; the pages fix none):
+ *   scale[n] = max_k |W_c[n][k]| / 448   (float32 IEEE division; 1 when the
+ *                                         row is all zero)
+ *   Q[n][k]  = the OCP E4M3 code nearest to W_c[n][k] / scale[n]
+ *              (float32 division, ties to even; 448 is E4M3's largest value)
+ * so that W_c[n][k] ~= e4m3(Q[n][k]) * scale[n].
+ *   W_c   : [N][Kc] BF16 or F32, read
+ *   Q     : [N][Kc] SS1_FP8_E4M3, written
+ *   scale : DEVICE float[N], written
+ * Requirements: Kc even, W_c and Q 16-byte aligned, scale 4-byte aligned;
+ * finite inputs.  N == 0 enqueues nothing.
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (before
+ * any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_quantize_fp8(const ss1_tensor* W_c, ss1_tensor* Q, float* scale, void* stream);
+
+/*
+ * ss1_forward_fp8w -- DEVICE, asynchronous on `stream`.  ss1_forward with the
+ * compressed weight in fp8 (ss1_quantize_fp8's Q and scale): the layer
+ * computed is SS1 with W_c[n][k'] = e4m3(Q[n][k']) * scale[n].  The sketch is
+ * formed as in ss1_forward (float32 sum rounded to bf16); each E4M3 weight is
+ * converted to bf16 exactly, the products are accumulated in float32 by the
+ * bf16 MFMA, and the row's scale multiplies the float32 sum before the bf16
+ * rounding of y.  Halves the weight bytes each call reads, which is what
+ * bounds small-M (decode) calls.
+ *   x : [M][K] BF16;  Q : [N][K/c] SS1_FP8_E4M3;  scale : DEVICE float[N];
+ *   hash, sign : as ss1_forward;  y : [M][N] BF16, written
+ * Requirements: as ss1_forward, plus BK % 32 == 0 and either M <= 16 with
+ * BN % 16 == 0, or BN in {32, 64, 128}; scale 4-byte aligned.
+ * Errors: as ss1_forward (SS1_ERR_SHAPE for a shape no fp8 kernel takes).
+ */
+ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q, const float* scale,
+                            const int32_t* hash, const int8_t* sign,
+                            int32_t c, int32_t BK, int32_t BN,
+                            ss1_tensor* y, void* stream);
 
 #ifdef __cplusplus
 }

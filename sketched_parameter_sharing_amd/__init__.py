@@ -12,12 +12,14 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     SS1Error,
     forward,
+    forward_fp8w,
     forward_idx,
     load,
     mlp_forward,
     plan,
     plan_index,
     project,
+    quantize_fp8,
     select_algo,
     sketch,
     version,

@@ -20,7 +20,7 @@ LIB_PATH = os.environ.get("SS1_LIBRARY") or os.path.join(HERE, "libss1.so")
 # status codes (ss1_status)
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = range(8)
 # dtypes (ss1_dtype)
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 # kernel choice (ss1_algo)
 ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND = range(5)
 ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC,
@@ -28,7 +28,7 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
-           "ss1_project", "ss1_mlp_forward")
+           "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -86,6 +86,10 @@ def load():
     lib.ss1_project.argtypes = [tp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_mlp_forward.restype = i32
     lib.ss1_mlp_forward.argtypes = [tp, ctypes.POINTER(Layer), ctypes.POINTER(Layer), tp, tp, vp]
+    lib.ss1_quantize_fp8.restype = i32
+    lib.ss1_quantize_fp8.argtypes = [tp, tp, vp, vp]
+    lib.ss1_forward_fp8w.restype = i32
+    lib.ss1_forward_fp8w.argtypes = [tp, tp, vp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     _LIB = lib
@@ -145,7 +149,9 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        return FP8_E4M3  # OCP E4M3 codes (quantized weights only)
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float32, or uint8 / float8_e4m3fn codes)")
 
 
 def _desc(t) -> Tensor:
@@ -227,6 +233,34 @@ def mlp_forward(x, up, down, h=None, y=None, row_chunk: int | None = None, strea
                                 ctypes.byref(dy), _stream(stream))
     _check(st, "ss1_mlp_forward")
     return h, y
+
+
+def quantize_fp8(W_c, Q=None, scale=None, stream=None):
+    """Per-row E4M3 quantization on the GPU (ss1_quantize_fp8): returns
+    (Q as uint8 codes [N][Kc], scale float32 [N])."""
+    import torch
+    _check_device(W_c)
+    if Q is None:
+        Q = torch.empty(W_c.shape, dtype=torch.uint8, device=W_c.device)
+    if scale is None:
+        scale = torch.empty((W_c.shape[0],), dtype=torch.float32, device=W_c.device)
+    dw, dq = _desc(W_c), _desc(Q)
+    st = load().ss1_quantize_fp8(ctypes.byref(dw), ctypes.byref(dq), scale.data_ptr(), _stream(stream))
+    _check(st, "ss1_quantize_fp8")
+    return Q, scale
+
+
+def forward_fp8w(x, Q, scale, hash_, sign, c: int, BK: int, BN: int, y=None, stream=None):
+    """y = SS1(x) with fp8 compressed weights on the GPU (ss1_forward_fp8w)."""
+    import torch
+    _check_device(x, Q, scale, hash_, sign)
+    if y is None:
+        y = torch.empty((x.shape[0], Q.shape[0]), dtype=x.dtype, device=x.device)
+    dx, dq, dy = _desc(x), _desc(Q), _desc(y)
+    st = load().ss1_forward_fp8w(ctypes.byref(dx), ctypes.byref(dq), scale.data_ptr(), hash_.data_ptr(),
+                                 sign.data_ptr(), c, BK, BN, ctypes.byref(dy), _stream(stream))
+    _check(st, "ss1_forward_fp8w")
+    return y
 
 
 def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16") -> str:

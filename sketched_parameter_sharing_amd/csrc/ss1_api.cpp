@@ -255,3 +255,40 @@ extern "C" ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, 
     }
     return SS1_OK;
 }
+
+extern "C" ss1_status ss1_quantize_fp8(const ss1_tensor* W_c, ss1_tensor* Q, float* scale, void* stream) {
+    if (!W_c || !Q) return SS1_ERR_NULL;
+    if (W_c->reserved != 0 || Q->reserved != 0) return SS1_ERR_SHAPE;
+    if (!valid_dtype(W_c->dtype) || Q->dtype != SS1_FP8_E4M3) return SS1_ERR_DTYPE;
+    const int64_t N = W_c->rows;
+    const int64_t Kc = W_c->cols;
+    if (N < 0 || Kc < 2 || Kc % 2 != 0 || Kc >= (int64_t(1) << 30) || N >= (int64_t(1) << 31)) return SS1_ERR_SHAPE;
+    if (Q->rows != N || Q->cols != Kc) return SS1_ERR_SHAPE;
+    if (N > (int64_t(1) << 40) / Kc) return SS1_ERR_SHAPE;
+    if (N == 0) return SS1_OK;
+    if (!W_c->data || !Q->data || !scale) return SS1_ERR_NULL;
+    if (!aligned(W_c->data, 16) || !aligned(Q->data, 16) || !aligned(scale, 4)) return SS1_ERR_ALIGN;
+    return ss1::launch_quantize_fp8(W_c->data, W_c->dtype, N, Kc, Q->data, scale, stream);
+}
+
+extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q, const float* scale,
+                                       const int32_t* hash, const int8_t* sign, int32_t c, int32_t BK,
+                                       int32_t BN, ss1_tensor* y, void* stream) {
+    if (!x || !Q || !y) return SS1_ERR_NULL;
+    if (Q->dtype != SS1_FP8_E4M3) return SS1_ERR_DTYPE;
+    if (x->dtype != SS1_BF16) return SS1_ERR_DTYPE;
+    // the forward's own checks, on a descriptor of W_c's shape in x's dtype
+    ss1_tensor wq = *Q;
+    wq.dtype = x->dtype;
+    ForwardArgs a;
+    ss1_status st = check_forward(x, &wq, hash, sign, c, BK, BN, y, PlanForm::Hash, stream, &a);
+    if (st != SS1_OK) return st;
+    if (!scale) return SS1_ERR_NULL;
+    if (!aligned(scale, 4)) return SS1_ERR_ALIGN;
+    a.w_fp8 = true;
+    a.wscale = scale;
+    const bool small = ss1::smallm_supported(a);
+    if (!small && !ss1::fused_supported(a)) return SS1_ERR_SHAPE;
+    if (a.M == 0) return SS1_OK;
+    return small ? ss1::launch_smallm(a) : ss1::launch_fused(a);
+}

@@ -247,6 +247,37 @@ __device__ __forceinline__ int xcd_tile(int b, int n) {
     return (b % 8) * per + b / 8;
 }
 
+// ------------------------------------------------------------ fp8 weights
+// Eight OCP E4M3 values (bytes, element 0 lowest) to eight bf16 values in the
+// uint4 layout of a bf16 row: every E4M3 value (subnormals included) is a
+// bf16 value, so the conversion (v_cvt_scalef32_pk_bf16_fp8, scale 1) is exact.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 r) {
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, false));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.x, 1.0f, true));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, false));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r.y, 1.0f, true));
+    return o;
+}
+
+// Raw storage of 8 consecutive weights: 16 bytes of bf16, or 8 bytes of E4M3.
+template <bool W8>
+struct WRaw {
+    uint4 v;
+    __device__ __forceinline__ void load(const uint16_t* w, size_t elem) {
+        v = *reinterpret_cast<const uint4*>(w + elem);
+    }
+    __device__ __forceinline__ uint4 bf16() const { return v; }
+};
+template <>
+struct WRaw<true> {
+    uint2 v;
+    __device__ __forceinline__ void load(const uint16_t* w, size_t elem) {
+        v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(w) + elem);
+    }
+    __device__ __forceinline__ uint4 bf16() const { return fp8x8_to_bf16x8(v); }
+};
+
 // Output activation applied in the epilogues, on the float32 accumulator
 // before the output rounding: kActNone, or kActGelu for GELU in its erf
 // form, v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))) (erff: the device math

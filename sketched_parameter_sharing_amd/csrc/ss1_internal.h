@@ -32,6 +32,9 @@ struct ForwardArgs {
     int32_t dtype;  // ss1_dtype
     void* stream;
     int32_t act = 0;  // epilogue activation: kActNone or kActGelu (erf form)
+    // fp8 weights: w holds OCP E4M3 codes and wscale one float per row
+    bool w_fp8 = false;
+    const float* wscale = nullptr;
 };
 
 // Epilogue activation codes (ForwardArgs::act; applied by dev::apply_act).
@@ -52,6 +55,9 @@ ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
                          int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
+// Per-row E4M3 quantization of a compressed weight (ss1_quant.hip).
+ss1_status launch_quantize_fp8(const void* W, int32_t dtype, int64_t N, int64_t Kc, void* Q, float* scale,
+                               void* stream);
 // Projection of a dense [N][K] weight onto the sharing pattern (ss1_project.hip).
 ss1_status launch_project(const void* W, int32_t dtype, const int32_t* hash, const int8_t* sign, const Dims& d,
                           void* Wc, void* stream);

@@ -204,13 +204,14 @@ __global__ __launch_bounds__(256) void generic_kernel(const TIn* __restrict__ x,
 // t = s*KS / BK (KS divides BK).  LDS rows are padded by 8 bf16 (16 bytes).
 // The sketch tile of a stage is summed in registers (sign flip + FMA, float32)
 // and written to LDS as bf16 next to the W_c tile; both are double-buffered.
-template <int MT, int BN, int WM, int WN, int KS, int C_T, bool FROM_HASH>
+template <int MT, int BN, int WM, int WN, int KS, int C_T, bool W8, bool FROM_HASH>
 __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ w,
                                                     const int32_t* __restrict__ pi,
                                                     const int8_t* __restrict__ ps,
                                                     uint16_t* __restrict__ y, int M, int K, int N,
-                                                    int J, int Jc, int c_rt, int BK, int n_mt, int act) {
+                                                    int J, int Jc, int c_rt, int BK, int n_mt, int act,
+                                                    const float* __restrict__ wscale) {
     static_assert(WM * WN == 4, "four waves");
     constexpr int TMW = MT / WM, TNW = BN / WN;  // wave tile
     constexpr int FM = TMW / 16, FN = TNW / 16;  // 16x16 MFMA blocks per wave
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
             uint4 a[AV][CR];
             float sg[CR];
             uint32_t sx[CR];
-            uint4 b[BV];
+            WRaw<W8> b[BV];
         };
         auto issue = [&](int s, Regs& R) {
             s = min(s, nstage - 1);
@@ -330,8 +331,7 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
                 for (int i = 0; i < AV; ++i) R.a[i][r] = *reinterpret_cast<const uint4*>(src + a_src[i]);
             }
 #pragma unroll
-            for (int i = 0; i < BV; ++i)
-                R.b[i] = *reinterpret_cast<const uint4*>(w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
+            for (int i = 0; i < BV; ++i) R.b[i].load(w, static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
         };
         auto commit = [&](const Regs& R, int buf) {
             uint16_t* A = As + buf * MT * LDP;
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
             }
 #pragma unroll
             for (int i = 0; i < BV; ++i)
-                if (b_ok[i]) *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = R.b[i];
+                if (b_ok[i]) *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = R.b[i].bf16();
         };
 
         if constexpr (DEEP) {
@@ -412,9 +412,11 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
             }
 #pragma unroll
             for (int i = 0; i < BV; ++i)
-                if (b_ok[i])
-                    *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = *reinterpret_cast<const uint4*>(
-                        w + static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
+                if (b_ok[i]) {
+                    WRaw<W8> r;
+                    r.load(w, static_cast<size_t>(n0 + b_row[i]) * Kc + k0 + b_col[i]);
+                    *reinterpret_cast<uint4*>(B + b_row[i] * LDP + b_col[i]) = r.bf16();
+                }
         };
         build(0, 0);
         __syncthreads();
@@ -431,10 +433,11 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int col = n0 + wn * TNW + j * 16 + fr;
+            const float ws = W8 ? wscale[col] : 1.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int m = m0 + wm * TMW + i * 16 + (lane >> 4) * 4 + q;
-                if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(acc[i][j][q], act));
+                if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(acc[i][j][q] * ws, act));
             }
         }
     }
@@ -447,14 +450,14 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 // weights of neuron (lane % 16); one 16x16x32 MFMA per step.  Tokens >= M are
 // zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.  W_c is
 // read coalesced and permuted into the operand pattern across lanes.
-template <int NW, int C_T, bool FROM_HASH>
+template <int NW, int C_T, bool W8, bool FROM_HASH>
 __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w,
                                                          const int32_t* __restrict__ pi,
                                                          const int8_t* __restrict__ ps,
                                                          uint16_t* __restrict__ y, int M, int K,
                                                          int N, int J, int Jc, int c_rt, int BK,
-                                                         int BN, int act) {
+                                                         int BN, int act, const float* __restrict__ wscale) {
     extern __shared__ uint32_t smem[];
     f32x4* red = reinterpret_cast<f32x4*>(smem);                  // [NW][64]
     uint32_t* s_src = smem + NW * 64 * 4;
@@ -480,16 +483,16 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
     // W_c is read coalesced (this lane: neuron lane/4 of the block, k-chunk
     // lane%4) and permuted into the MFMA operand pattern before use
     const int n = g * BN + nb * 16 + (lane >> 2);
-    const uint16_t* wrow = w + static_cast<size_t>(n) * Kc + (lane & 3) * 8;
+    const size_t wrow = static_cast<size_t>(n) * Kc + (lane & 3) * 8;  // element offset
     const int perm_src = coalesced_src_lane_bytes(lane);
 
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int U = 4;  // steps in flight per wave
     int s = s_begin;
     for (; s + U <= s_end; s += U) {
-        uint4 wr[U];
+        WRaw<W8> wr[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) wr[u] = *reinterpret_cast<const uint4*>(wrow + (s + u) * 32);
+        for (int u = 0; u < U; ++u) wr[u].load(w, wrow + (s + u) * 32);
         uint4 xr[U][(C_T > 0) ? C_T : 1];
         float sg[U][(C_T > 0) ? C_T : 1];
         if constexpr (C_T > 0) {
@@ -525,13 +528,14 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
                 }
             }
             const uint4 ap = pack_bf16x8(a);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
-                                                          __builtin_bit_cast(bf16x8, to_operand_layout(wr[u], perm_src)),
-                                                          acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, to_operand_layout(wr[u].bf16(), perm_src)),
+                acc, 0, 0, 0);
         }
     }
     for (; s < s_end; ++s) {
-        const uint4 wr = *reinterpret_cast<const uint4*>(wrow + s * 32);
+        WRaw<W8> wr;
+        wr.load(w, wrow + s * 32);
         const int k0 = s * 32;
         const int t = k0 / BK;
         const int u0 = k0 - t * BK;
@@ -543,9 +547,9 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
             acc_bf16x8(a, raw, entry_sign(e), r == 0);
         }
         const uint4 ap = pack_bf16x8(a);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap),
-                                                      __builtin_bit_cast(bf16x8, to_operand_layout(wr, perm_src)),
-                                                      acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, to_operand_layout(wr.bf16(), perm_src)), acc,
+            0, 0, 0);
     }
 
     red[wave * 64 + lane] = acc;
@@ -560,10 +564,11 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
             sum[3] += p[3];
         }
         const int col = g * BN + nb * 16 + (lane & 15);
+        const float ws = W8 ? wscale[col] : 1.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = (lane >> 4) * 4 + q;
-            if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(sum[q], act));
+            if (m < M) y[static_cast<size_t>(m) * N + col] = to_bf16_bits(apply_act(sum[q] * ws, act));
         }
     }
 }
@@ -876,7 +881,7 @@ ss1_status launch_generic_t(const ForwardArgs& a) {
     return launch_status();
 }
 
-template <int MT, int BN, int WM, int WN, int KS, int C_T, bool FROM_HASH>
+template <int MT, int BN, int WM, int WN, int KS, int C_T, bool W8, bool FROM_HASH>
 ss1_status launch_fused_cfg(const ForwardArgs& a) {
     const Dims& d = a.d;
     const int n_mt = static_cast<int>((a.M + MT - 1) / MT);
@@ -884,70 +889,69 @@ ss1_status launch_fused_cfg(const ForwardArgs& a) {
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
     constexpr int LDP = KS + 8;
     const size_t lds = static_cast<size_t>(2) * (MT + BN) * LDP * 2 + plan_lds_bytes(d);
+    auto kern = &fused_kernel<MT, BN, WM, WN, KS, C_T, W8, FROM_HASH>;
     if (lds > 64 * 1024) {
-        if (hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&fused_kernel<MT, BN, WM, WN, KS, C_T, FROM_HASH>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds)) != hipSuccess)
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds)) != hipSuccess)
             return SS1_ERR_HIP;
     }
-    hipLaunchKernelGGL((fused_kernel<MT, BN, WM, WN, KS, C_T, FROM_HASH>), dim3(static_cast<unsigned>(blocks)), dim3(256), lds,
-                       static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
-                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s,
-                       static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K, (int)d.N, (int)d.J,
-                       (int)d.Jc, d.c, d.BK, n_mt, a.act);
+    hipLaunchKernelGGL((fused_kernel<MT, BN, WM, WN, KS, C_T, W8, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, n_mt, a.act, a.wscale);
     return launch_status();
 }
 
-template <int BN, int WM, int WN, int KS, bool FROM_HASH>
+template <int BN, int WM, int WN, int KS, bool W8, bool FROM_HASH>
 ss1_status launch_fused_c(const ForwardArgs& a) {
     switch (a.d.c) {
-        case 1: return launch_fused_cfg<128, BN, WM, WN, KS, 1, FROM_HASH>(a);
-        case 2: return launch_fused_cfg<128, BN, WM, WN, KS, 2, FROM_HASH>(a);
-        case 4: return launch_fused_cfg<128, BN, WM, WN, KS, 4, FROM_HASH>(a);
-        case 8: return launch_fused_cfg<128, BN, WM, WN, KS, 8, FROM_HASH>(a);
-        default: return launch_fused_cfg<128, BN, WM, WN, KS, 0, FROM_HASH>(a);
+        case 1: return launch_fused_cfg<128, BN, WM, WN, KS, 1, W8, FROM_HASH>(a);
+        case 2: return launch_fused_cfg<128, BN, WM, WN, KS, 2, W8, FROM_HASH>(a);
+        case 4: return launch_fused_cfg<128, BN, WM, WN, KS, 4, W8, FROM_HASH>(a);
+        case 8: return launch_fused_cfg<128, BN, WM, WN, KS, 8, W8, FROM_HASH>(a);
+        default: return launch_fused_cfg<128, BN, WM, WN, KS, 0, W8, FROM_HASH>(a);
     }
 }
 
-template <int KS, bool FROM_HASH>
+template <int KS, bool W8, bool FROM_HASH>
 ss1_status launch_fused_bn(const ForwardArgs& a) {
     switch (a.d.BN) {
-        case 32: return launch_fused_c<32, 4, 1, KS, FROM_HASH>(a);
-        case 64: return launch_fused_c<64, 2, 2, KS, FROM_HASH>(a);
-        case 128: return launch_fused_c<128, 2, 2, KS, FROM_HASH>(a);
+        case 32: return launch_fused_c<32, 4, 1, KS, W8, FROM_HASH>(a);
+        case 64: return launch_fused_c<64, 2, 2, KS, W8, FROM_HASH>(a);
+        case 128: return launch_fused_c<128, 2, 2, KS, W8, FROM_HASH>(a);
         default: return SS1_ERR_ALGO;
     }
 }
 
-template <bool FROM_HASH>
+template <bool W8, bool FROM_HASH>
 ss1_status launch_fused_t(const ForwardArgs& a) {
-    if (a.d.BK % 64 == 0) return launch_fused_bn<64, FROM_HASH>(a);
-    return launch_fused_bn<32, FROM_HASH>(a);
+    if (a.d.BK % 64 == 0) return launch_fused_bn<64, W8, FROM_HASH>(a);
+    return launch_fused_bn<32, W8, FROM_HASH>(a);
 }
 
-template <int C_T, bool FROM_HASH>
+template <int C_T, bool W8, bool FROM_HASH>
 ss1_status launch_smallm_cfg(const ForwardArgs& a) {
     const Dims& d = a.d;
     constexpr int NW = 8;
     const long long blocks = d.G * (d.BN / 16);
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
     const size_t lds = static_cast<size_t>(NW) * 64 * 16 + plan_lds_bytes(d);
-    hipLaunchKernelGGL((smallm_kernel<NW, C_T, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((smallm_kernel<NW, C_T, W8, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NW * 64), lds, static_cast<hipStream_t>(a.stream),
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w),
                        a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K,
-                       (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, a.act);
+                       (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, a.act, a.wscale);
     return launch_status();
 }
 
-template <bool FROM_HASH>
+template <bool W8, bool FROM_HASH>
 ss1_status launch_smallm_t(const ForwardArgs& a) {
     switch (a.d.c) {
-        case 1: return launch_smallm_cfg<1, FROM_HASH>(a);
-        case 2: return launch_smallm_cfg<2, FROM_HASH>(a);
-        case 4: return launch_smallm_cfg<4, FROM_HASH>(a);
-        case 8: return launch_smallm_cfg<8, FROM_HASH>(a);
-        default: return launch_smallm_cfg<0, FROM_HASH>(a);
+        case 1: return launch_smallm_cfg<1, W8, FROM_HASH>(a);
+        case 2: return launch_smallm_cfg<2, W8, FROM_HASH>(a);
+        case 4: return launch_smallm_cfg<4, W8, FROM_HASH>(a);
+        case 8: return launch_smallm_cfg<8, W8, FROM_HASH>(a);
+        default: return launch_smallm_cfg<0, W8, FROM_HASH>(a);
     }
 }
 
@@ -1091,11 +1095,14 @@ ss1_status launch_generic(const ForwardArgs& a) {
 }
 
 ss1_status launch_fused(const ForwardArgs& a) {
-    return a.form == PlanForm::Hash ? launch_fused_t<true>(a) : launch_fused_t<false>(a);
+    // fp8 weights come with the forward hash only
+    if (a.w_fp8) return a.form == PlanForm::Hash ? launch_fused_t<true, true>(a) : SS1_ERR_ALGO;
+    return a.form == PlanForm::Hash ? launch_fused_t<false, true>(a) : launch_fused_t<false, false>(a);
 }
 
 ss1_status launch_smallm(const ForwardArgs& a) {
-    return a.form == PlanForm::Hash ? launch_smallm_t<true>(a) : launch_smallm_t<false>(a);
+    if (a.w_fp8) return a.form == PlanForm::Hash ? launch_smallm_t<true, true>(a) : SS1_ERR_ALGO;
+    return a.form == PlanForm::Hash ? launch_smallm_t<false, true>(a) : launch_smallm_t<false, false>(a);
 }
 
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i,

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     text = open(os.path.join(ROOT, "include", "ss1.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ss1_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ss1_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_function():
@@ -243,6 +243,41 @@ def test_mlp_forward_argument_checks():
     lib = _lib.load()
     assert lib.ss1_mlp_forward(None, ctypes.byref(up), ctypes.byref(down), ctypes.byref(h),
                                ctypes.byref(y), None) == _lib.ERR_NULL
+
+
+def test_quantize_fp8_argument_checks():
+    lib = _lib.load()
+    F8 = _lib.FP8_E4M3
+
+    def q(W, Q, sc=A):
+        return lib.ss1_quantize_fp8(ctypes.byref(W), ctypes.byref(Q), sc, None)
+
+    assert q(T(64, 128), T(64, 127, F8)) == _lib.ERR_SHAPE
+    assert q(T(64, 127), T(64, 127, F8)) == _lib.ERR_SHAPE          # odd Kc
+    assert q(T(64, 128), T(64, 128)) == _lib.ERR_DTYPE              # Q not FP8
+    assert q(T(64, 128, F8), T(64, 128, F8)) == _lib.ERR_DTYPE      # W_c not BF16/F32
+    assert q(T(64, 128), T(64, 128, F8), sc=None) == _lib.ERR_NULL
+    assert q(T(64, 128), T(64, 128, F8), sc=A + 2) == _lib.ERR_ALIGN
+    assert q(T(64, 128, data=A + 8), T(64, 128, F8)) == _lib.ERR_ALIGN
+    assert q(T(0, 128, data=None), T(0, 128, F8, data=None), sc=None) == _lib.OK
+    assert lib.ss1_quantize_fp8(None, ctypes.byref(T(1, 2, F8)), A, None) == _lib.ERR_NULL
+
+
+def test_forward_fp8w_argument_checks():
+    lib = _lib.load()
+    F8 = _lib.FP8_E4M3
+
+    def f(x, Q, y, sc=A, c=2, BK=64, BN=64):
+        return lib.ss1_forward_fp8w(ctypes.byref(x), ctypes.byref(Q), sc, A, A, c, BK, BN, ctypes.byref(y), None)
+
+    assert f(T(300, 256), T(64, 128), T(300, 64)) == _lib.ERR_DTYPE          # Q not FP8
+    assert f(T(300, 256, _lib.F32), T(64, 128, F8), T(300, 64, _lib.F32)) == _lib.ERR_DTYPE
+    assert f(T(300, 256), T(64, 100, F8), T(300, 64)) == _lib.ERR_SHAPE      # Q cols != K/c
+    assert f(T(300, 240), T(48, 120, F8), T(300, 48), BK=24, BN=48) == _lib.ERR_SHAPE  # no fp8 kernel
+    assert f(T(300, 256), T(96, 128, F8), T(300, 96), BN=48) == _lib.ERR_SHAPE  # BN 48 needs M <= 16
+    assert f(T(300, 256), T(64, 128, F8), T(300, 64), sc=None) == _lib.ERR_NULL
+    assert f(T(300, 256), T(64, 128, F8), T(300, 64), sc=A + 1) == _lib.ERR_ALIGN
+    assert f(T(0, 256, data=None), T(64, 128, F8), T(0, 64, data=None)) == _lib.OK
 
 
 def test_binding_refuses_host_tensors():

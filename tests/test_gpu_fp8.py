@@ -1,0 +1,97 @@
+"""GPU parity of the fp8-weight path (ss1_quantize_fp8, ss1_forward_fp8w)
+against the CPU oracle, through the C ABI.
+
+Bars (written in each test):
+* quantization: codes and float32 scales bit-exact against the oracle's
+  quantize_fp8_rows (which is pinned against torch's float8_e4m3fn);
+* forward: the layer with W_c = e4m3(Q) * scale; against the float64 oracle
+  max|y - y_ref| / max|y_ref| <= 2e-2, and elementwise against the oracle's
+  mirror (bf16 sketch, float64 contraction) |y - y_m| <= 2^-7 |y_m| +
+  1e-5 max|y_m| -- the same bars as the bf16 path, since every E4M3 weight is a
+  bf16 value and only the row scale's float32 product is added.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sketched_parameter_sharing_amd as ss1
+from ss1_inputs import WORKLOADS, Workload, bf16_bits_to_f32, draw, f32_to_bf16_bits, make_inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ss1.load()
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def to_host(t):
+    return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+
+
+@pytest.mark.parametrize("N,Kc,dtype", [(64, 128, "bf16"), (130, 384, "bf16"), (96, 2048, "f32"),
+                                        (3, 2, "bf16"), (14336, 2048, "bf16")])
+def test_quantize_bit_exact(N, Kc, dtype):
+    w = draw("normal002", 0x5800 + N + Kc, (N, Kc))
+    w[min(1, N - 1)] = 0.0                        # an all-zero row
+    if N > 2:
+        w[2, ::7] *= 300.0                        # a row with outliers
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(w)
+        vals = bf16_bits_to_f32(bits)
+        W = bf16_dev(bits)
+    else:
+        vals = w
+        W = torch.from_numpy(w).cuda()
+    Q, scale = ss1.quantize_fp8(W)
+    torch.cuda.synchronize()
+    codes, sc = oracle.quantize_fp8_rows(vals)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), sc.view(np.uint32))
+    assert np.array_equal(Q.cpu().numpy(), codes)
+
+
+def run_case(wl, M, rows=None):
+    inp = make_inputs(wl.with_m(M))
+    p = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    Q, scale = ss1.quantize_fp8(bf16_dev(inp.w_bits))
+    y = ss1.forward_fp8w(bf16_dev(inp.x_bits), Q, scale, p.hash, p.sign, wl.c, wl.BK, wl.BN)
+    torch.cuda.synchronize()
+    y = to_host(y)
+    h, s = oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    Wq = oracle.dequantize_fp8_rows(Q.cpu().numpy(), scale.cpu().numpy())
+    x = inp.x.astype(np.float64)
+    if rows is not None:
+        x, y = x[rows], y[rows]
+    ref = oracle.forward(x, Wq, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.max(np.abs(y - ref)) / np.max(np.abs(ref)) <= 2e-2
+    mir = oracle.forward_mirror(x, Wq, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, True)
+    assert np.all(np.abs(y - mir) <= 2.0 ** -7 * np.abs(mir) + 1e-5 * np.max(np.abs(mir)))
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 300])
+@pytest.mark.parametrize("c,BN", [(1, 64), (2, 64), (4, 32), (8, 128), (3, 64)])
+def test_forward_fp8w_reduced(M, c, BN):
+    K = 96 * 64 if c == 3 else 2048
+    wl = Workload(f"fp8_c{c}_bn{BN}", 8, c, M, K, 4 * BN, c, 64, BN, "bf16")
+    run_case(wl, M)
+
+
+def test_forward_fp8w_decode_bn48_and_ragged():
+    wl = Workload("fp8_bn48", 8, 9, 7, 768, 3 * 48, 2, 32, 48, "bf16")   # small-M kernel only
+    run_case(wl, 7)
+    wl = Workload("fp8_ragged", 8, 10, 333, 768, 6 * 64, 2, 32, 64, "bf16")
+    run_case(wl, 333)
+
+
+@pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_down_m16", "gpt2s_up", "llama_gateup_m4096"])
+def test_forward_fp8w_full_size(name):
+    wl = WORKLOADS[name]
+    rows = None if wl.M <= 16 else np.r_[0:4, wl.M // 2:wl.M // 2 + 4, wl.M - 4:wl.M]
+    run_case(wl, wl.M, rows)
