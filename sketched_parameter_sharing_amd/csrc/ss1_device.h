@@ -53,7 +53,8 @@ __device__ __forceinline__ uint32_t make_entry(int j, int BK, int s) {
 // Fills s_src[t*c + r] (t < Jc, r < c) for group g.  From the forward hash the
 // sources of each compressed chunk are gathered with LDS atomics and then put
 // in ascending chunk order; from the inverse index they are copied.  Needs
-// s_cnt[Jc] scratch for the forward form.  Ends with a barrier.
+// s_cnt[Jc] scratch for the forward form.  Ends with a barrier.  The
+// barriers order LDS only: global loads issued before the call stay in flight.
 template <bool FROM_HASH>
 __device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g,
                            int J, int Jc, int c, int BK, uint32_t* s_src, int* s_cnt) {
@@ -64,7 +65,7 @@ __device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restr
     if (FROM_HASH) {
         for (int e = tid; e < J; e += nt) s_src[e] = kAbsent;
         for (int t = tid; t < Jc; t += nt) s_cnt[t] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int j = tid; j < J; j += nt) {
             const int t = gi[j];
             const int s = gs[j];
@@ -73,7 +74,7 @@ __device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restr
                 if (slot < c) s_src[t * c + slot] = make_entry(j, BK, s);
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int t = tid; t < Jc; t += nt) {
             uint32_t* p = s_src + t * c;
             for (int a = 1; a < c; ++a) {  // insertion sort; absent entries go last
@@ -93,7 +94,7 @@ __device__ void stage_plan(const int32_t* __restrict__ pi, const int8_t* __restr
             s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // ------------------------------------------------------------- bf16 helpers
@@ -185,7 +186,7 @@ __device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __rest
     if (FROM_HASH) {
         for (int e = tid; e < total; e += nt) s_src[e] = kAbsent;
         for (int e = tid; e < count * Jc; e += nt) s_cnt[e] = 0;
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < total; e += nt) {
             const int gl = e / J;
             const int j = e - gl * J;
@@ -196,7 +197,7 @@ __device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __rest
                 if (slot < c) s_src[gl * J + t * c + slot] = make_entry(j, BK, s);
             }
         }
-        __syncthreads();
+        lds_barrier();
         for (int e = tid; e < count * Jc; e += nt) {
             uint32_t* p = s_src + e * c;  // (gl, t) -> row gl*J + t*c
             for (int a = 1; a < c; ++a) {
@@ -216,7 +217,7 @@ __device__ void stage_plans(const int32_t* __restrict__ pi, const int8_t* __rest
             s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // W_c fragments are read from global memory in a coalesced pattern (lane l

@@ -444,8 +444,9 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 }
 
 // ============================================================ small-M kernel
-// Block: NW waves, 16 neurons (rows nb*16 .. +15 of group g).  Wave w takes the
-// 32-wide k-steps [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each
+// Block: NW waves (4, 8 or 16, chosen from S and M), 16 neurons (rows
+// nb*16 .. +15 of group g).  Wave w takes the 32-wide k-steps
+// [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each
 // lane builds 8 sketch values of token (lane % 16) straight from x and loads 8
 // weights of neuron (lane % 16); one 16x16x32 MFMA per step.  Tokens >= M are
 // zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.  W_c is
@@ -929,10 +930,9 @@ ss1_status launch_fused_t(const ForwardArgs& a) {
     return launch_fused_bn<32, W8, FROM_HASH>(a);
 }
 
-template <int C_T, bool W8, bool FROM_HASH>
+template <int NW, int C_T, bool W8, bool FROM_HASH>
 ss1_status launch_smallm_cfg(const ForwardArgs& a) {
     const Dims& d = a.d;
-    constexpr int NW = 8;
     const long long blocks = d.G * (d.BN / 16);
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
     const size_t lds = static_cast<size_t>(NW) * 64 * 16 + plan_lds_bytes(d);
@@ -944,14 +944,28 @@ ss1_status launch_smallm_cfg(const ForwardArgs& a) {
     return launch_status();
 }
 
+// Waves per block: about 16 of the Kc/32 k-steps per wave (measured on the
+// Llama-3-8B decode shapes: 64 steps -> 4 waves best, 224 steps -> 16 waves at
+// M = 1 but 8 at M = 16, where each step also reads 16 tokens); 16 waves only
+// where the kernel fits in 128 registers (c <= 2).
+template <int C_T, bool W8, bool FROM_HASH>
+ss1_status launch_smallm_nw(const ForwardArgs& a) {
+    const long long S = a.d.Kc / 32;
+    if constexpr (C_T > 0 && C_T <= 2) {
+        if (S >= 192 && a.M <= 8) return launch_smallm_cfg<16, C_T, W8, FROM_HASH>(a);
+    }
+    if (S >= 96) return launch_smallm_cfg<8, C_T, W8, FROM_HASH>(a);
+    return launch_smallm_cfg<4, C_T, W8, FROM_HASH>(a);
+}
+
 template <bool W8, bool FROM_HASH>
 ss1_status launch_smallm_t(const ForwardArgs& a) {
     switch (a.d.c) {
-        case 1: return launch_smallm_cfg<1, W8, FROM_HASH>(a);
-        case 2: return launch_smallm_cfg<2, W8, FROM_HASH>(a);
-        case 4: return launch_smallm_cfg<4, W8, FROM_HASH>(a);
-        case 8: return launch_smallm_cfg<8, W8, FROM_HASH>(a);
-        default: return launch_smallm_cfg<0, W8, FROM_HASH>(a);
+        case 1: return launch_smallm_nw<1, W8, FROM_HASH>(a);
+        case 2: return launch_smallm_nw<2, W8, FROM_HASH>(a);
+        case 4: return launch_smallm_nw<4, W8, FROM_HASH>(a);
+        case 8: return launch_smallm_nw<8, W8, FROM_HASH>(a);
+        default: return launch_smallm_nw<0, W8, FROM_HASH>(a);
     }
 }
 
