@@ -6,6 +6,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 from .ss1_oracle import (  # noqa: F401
     SplitMix64,
+    backward,
+    backward_dw_mirror,
     bf16_bits_to_f64,
     check_plan,
     E4M3_MAX,

@@ -397,6 +397,56 @@ def mlp_forward(x, up: dict, down: dict, round_h_to_bf16: bool = False):
     return h, y
 
 
+def backward(x, Wc, dy, hash_, sign, K: int, N: int, c: int, BK: int, BN: int):
+    """Gradients of the SS1 forward, float64, for y = forward(x, Wc) and an
+    upstream gradient dy [M][N].  The summary page's *Limitations* note that
+    the backward pass is not reduced; written out from the forward's two
+    steps:
+
+    * dWc: y[:, g-block] = z_g @ Wc[g-block].T, so
+      dWc[g-block] = dy[:, g-block].T @ z_g (z_g the group's sketch);
+    * dx: dz_g = dy[:, g-block] @ Wc[g-block] is the gradient of the sketch,
+      and the sketch added sign[g][j] * x-chunk j into chunk hash[g][j], so
+      dx-chunk j receives sign[g][j] * dz_g-chunk hash[g][j], summed over
+      the groups.
+
+    Returns (dx [M][K], dWc [N][Kc])."""
+    d = dims(K, N, c, BK, BN)
+    J, Kc, G = d["J"], d["Kc"], d["G"]
+    x = np.asarray(x, dtype=np.float64)
+    Wc = np.asarray(Wc, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    M = x.shape[0]
+    if Wc.shape != (N, Kc) or dy.shape != (M, N):
+        raise ValueError("shape mismatch")
+    z = sketch(x, hash_, sign, K, N, c, BK, BN)
+    dWc = np.empty((N, Kc), dtype=np.float64)
+    dx = np.zeros((M, K), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * BN, (g + 1) * BN)
+        dWc[rows] = dy[:, rows].T @ z[g]
+        dz = dy[:, rows] @ Wc[rows]
+        for j in range(J):
+            t = int(hash_[g, j])
+            dx[:, j * BK:(j + 1) * BK] += float(sign[g, j]) * dz[:, t * BK:(t + 1) * BK]
+    return dx, dWc
+
+
+def backward_dw_mirror(x, dy, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+    """Diagnostic dWc for a device path that rounds the sketch to bf16 (as the
+    forward does) before the float32-accumulated product: dy_g.T @ z_g with z
+    from :func:`sketch_rounded`, in float64."""
+    d = dims(K, N, c, BK, BN)
+    G = d["G"]
+    z = sketch_rounded(x, hash_, sign, K, N, c, BK, BN, True)
+    dy = np.asarray(dy, dtype=np.float64)
+    out = np.empty((N, d["Kc"]), dtype=np.float64)
+    for g in range(G):
+        rows = slice(g * BN, (g + 1) * BN)
+        out[rows] = dy[:, rows].T @ z[g]
+    return out
+
+
 # ------------------------------------------------------------- fp8 weights
 # OCP 8-bit floating point, E4M3 ("FN": no infinities): 1 sign bit, 4
 # exponent bits (bias 7), 3 mantissa bits; exponent field 0 holds subnormals

@@ -547,3 +547,68 @@ def test_quantize_fp8_rows():
         err = np.abs(oracle.e4m3_decode(codes[n]) - q)
         assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(q), 2.0 ** -10) + 1e-12)
     np.testing.assert_allclose(deq[0], W[0], rtol=2 ** -4, atol=scale[0] * 2.0 ** -10)
+
+
+# ----------------------------------------------------------- backward pins
+BWD_SHAPES = [(5, 64, 8, 2, 8, 4), (3, 96, 12, 4, 8, 6), (4, 48, 6, 1, 8, 3), (6, 72, 8, 3, 4, 8)]
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", BWD_SHAPES)
+def test_backward_adjoint_identities_integer_exact(M, K, N, c, BK, BN):
+    """y is linear in x and in Wc: <dy, y> = <dx, x> = <dWc, Wc>, exactly on
+    integer inputs in float64."""
+    g = np.random.default_rng(M * K)
+    h, s = oracle.plan(33, K, N, c, BK, BN)
+    x = g.integers(-4, 5, (M, K)).astype(np.float64)
+    Wc = g.integers(-4, 5, (N, K // c)).astype(np.float64)
+    dy = g.integers(-4, 5, (M, N)).astype(np.float64)
+    y = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    dx, dWc = oracle.backward(x, Wc, dy, h, s, K, N, c, BK, BN)
+    assert np.sum(dy * y) == np.sum(dx * x) == np.sum(dWc * Wc)
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", BWD_SHAPES)
+def test_backward_dx_equals_dense_expansion(M, K, N, c, BK, BN):
+    g = np.random.default_rng(K)
+    h, s = oracle.plan(34, K, N, c, BK, BN)
+    x = g.standard_normal((M, K))
+    Wc = g.standard_normal((N, K // c))
+    dy = g.standard_normal((M, N))
+    dx, _ = oracle.backward(x, Wc, dy, h, s, K, N, c, BK, BN)
+    np.testing.assert_allclose(dx, dy @ oracle.dense_expand(Wc, h, s, K, N, c, BK, BN), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    M, K, N, c, BK, BN = 7, 128, 32, 4, 8, 8
+    h, s = oracle.plan(35, K, N, c, BK, BN)
+    g = np.random.default_rng(36)
+    x = g.standard_normal((M, K))
+    Wc = g.standard_normal((N, K // c))
+    dy = g.standard_normal((M, N))
+    # dense weight built from Wc by torch indexing: W[n, j*BK+u] = sign * Wc[n, hash*BK+u]
+    J = K // BK
+    col = np.empty((N, K), dtype=np.int64)
+    sg = np.empty((N, K))
+    for n in range(N):
+        for j in range(J):
+            col[n, j * BK:(j + 1) * BK] = h[n // BN, j] * BK + np.arange(BK)
+            sg[n, j * BK:(j + 1) * BK] = s[n // BN, j]
+    xt = torch.tensor(x, requires_grad=True)
+    wt = torch.tensor(Wc, requires_grad=True)
+    W = torch.gather(wt, 1, torch.tensor(col)) * torch.tensor(sg)
+    (xt @ W.T).backward(torch.tensor(dy))
+    dx, dWc = oracle.backward(x, Wc, dy, h, s, K, N, c, BK, BN)
+    np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dWc, wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_dw_mirror_rounds_only_the_sketch():
+    M, K, N, c, BK, BN = 6, 64, 8, 2, 8, 4
+    h, s = oracle.plan(37, K, N, c, BK, BN)
+    g = np.random.default_rng(38)
+    x = g.integers(-4, 5, (M, K)).astype(np.float64)     # integer sketch: exact in bf16
+    dy = g.standard_normal((M, N))
+    Wc = np.zeros((N, K // c))
+    _, dWc = oracle.backward(x, Wc, dy, h, s, K, N, c, BK, BN)
+    assert np.array_equal(oracle.backward_dw_mirror(x, dy, h, s, K, N, c, BK, BN), dWc)
