@@ -21,6 +21,9 @@ oracle timed on a bounded sample of the same workload.
         # ss1_mlp_forward: the GPT-2 L MLP pair (8192 x 1280 -> 5120 -> 1280,
         # GELU between) at compression c, with a c sweep against the dense
         # pair (torch bf16 matmuls and GELU at the same shapes)
+    python bench.py --op backward [--workload gpt2s_up]
+        # ss1_backward (dx and dW_c) of the layer, next to the dense layer's
+        # two backward GEMMs (torch bf16) at the same shapes
     python bench.py --op fp8 [--workload llama_gateup_m1]
         # ss1_forward_fp8w: the layer with per-row fp8 (E4M3) compressed
         # weights, against the HBM / MFMA roofline on its own bytes
@@ -229,6 +232,31 @@ def time_events_i(fn, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3 / steps
+
+
+def backward_work(wl):
+    dw = 2 * wl.M * wl.N * wl.Kc          # dy_g^T z_g per group
+    dx = 2 * wl.M * wl.N * wl.K           # dy times the dense expansion
+    return {"flops": dw + dx, "dense_equiv_flops": 2 * 2 * wl.M * wl.N * wl.K,
+            "bytes": 2 * (2 * wl.M * wl.K + 2 * wl.N * wl.Kc + wl.M * wl.N)}
+
+
+def time_backward(wl, steps, warmup):
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    from ss1_inputs import make_inputs, draw, f32_to_bf16_bits
+    inp = make_inputs(wl)
+    p = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    x, w = to_dev(inp.x_bits, "bf16"), to_dev(inp.w_bits, "bf16")
+    dy = to_dev(f32_to_bf16_bits(draw("normal", wl.x_seed + 7, (wl.M, wl.N))), "bf16")
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    t = time_events(lambda: ss1.backward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, dy, dx=dx, dW_c=dw),
+                    steps, warmup)
+    # the dense layer's backward at the same shapes: dx = dy W, dW = dy^T x
+    W = to_dev(f32_to_bf16_bits(draw("normal002", wl.w_seed, (wl.N, wl.K))), "bf16")
+    dyt = dy.t().contiguous()
+    t_dense = time_events(lambda: (torch.matmul(dy, W), torch.matmul(dyt, x)), steps, warmup)
+    return t, t_dense
 
 
 def time_project(wl, steps, warmup, warm):
@@ -445,7 +473,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help=f"default: {HEADLINE} (forward), {PROJECT_HEADLINE} (project)")
-    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8"])
+    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "backward"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band"])
@@ -578,6 +606,51 @@ def main():
             "roofline": roof,
         }
         rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mlp(c)
+        print(json.dumps(rec), flush=True)
+        return
+
+    if args.op == "backward":
+        name = args.workload or HEADLINE
+        wl = WORKLOADS[name]
+        t, t_dense = time_backward(wl, args.steps, args.warmup)
+        wk = backward_work(wl)
+        mf = {"bound": "mfma", "achieved": wk["flops"] / t / 1e12, "peak": PEAK_MFMA_BF16 / 1e12,
+              "unit": "TFLOP/s"}
+        mf["frac"] = mf["achieved"] / mf["peak"]
+        hb = {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        hb["frac"] = hb["achieved"] / hb["peak"]
+        t_f, t_b = wk["flops"] / PEAK_MFMA_BF16, wk["bytes"] / PEAK_HBM
+        roof = dict(mf if t_f >= t_b else hb)
+        roof.update({"other": hb if t_f >= t_b else mf, "traffic": None, "t_lower_us": max(t_f, t_b) * 1e6,
+                     "note": "dx (dense-cost GEMM on the expanded weight) plus dW_c, both kernels per call"})
+        rec = {
+            "metric": "SS1 layer backward (dx + dW_c) TFLOP/s + % of MFMA/HBM roofline",
+            "value": wk["flops"] / t / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) inputs and upstream gradient, N(0,0.02) weights, seeded plan)",
+            "config": {"workload": name + "_backward", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c,
+                       "BK": wl.BK, "BN": wl.BN, "cache": "warm (one buffer set)",
+                       "dense_backward_ms": t_dense * 1e3, "ratio_to_dense": t / t_dense},
+            "roofline": roof,
+        }
+        if args.no_cpu_baseline:
+            rec["cpu_baseline"] = None
+        else:
+            import oracle
+            from ss1_inputs import make_inputs, draw
+            rows = 64
+            sub = wl.with_m(rows)
+            inp = make_inputs(sub)
+            h, sg = oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+            dyh = draw("normal", 1, (rows, wl.N)).astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.backward(inp.x, inp.w, dyh, h, sg, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+            tc = time.perf_counter() - t0
+            rec["cpu_baseline"] = {"value": backward_work(sub)["flops"] / tc / 1e12, "unit": "TFLOP/s",
+                                   "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                   "sample": f"{rows} of {wl.M} rows of {name}, float64 NumPy oracle backward, "
+                                             f"{tc:.3f} s"}
         print(json.dumps(rec), flush=True)
         return
 

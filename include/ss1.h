@@ -309,6 +309,32 @@ ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q, const floa
                             int32_t c, int32_t BK, int32_t BN,
                             ss1_tensor* y, void* stream);
 
+/*
+ * ss1_backward -- DEVICE, asynchronous on `stream`.  Gradients of
+ * y = ss1_forward(x, W_c) for an upstream gradient dy (the SS1 summary page,
+ * "Limitations": the backward pass is not reduced, it costs what a dense
+ * layer's does):
+ *   dW_c[g-block] = dy[:, g-block]^T z_g        (z_g: group g's sketch of x)
+ *   dx[:, j-chunk] = sum over groups g of sign[g][j] *
+ *                    (dy[:, g-block] W_c[g-block])[:, hash[g][j]-chunk]
+ * (dx = dy times the dense weight SS1 stands for).  z_g is formed as in
+ * ss1_forward (float32 sum of the signed sources, rounded to bf16); products
+ * accumulate in float32 on the bf16 MFMA; outputs are rounded to bf16.
+ *   x  : [M][K] BF16;  W_c : [N][K/c] BF16;  hash, sign : as ss1_forward
+ *   dy : [M][N] BF16, read
+ *   dx : [M][K] BF16, written (NULL: not computed)
+ *   dW_c : [N][K/c] BF16, written (NULL: not computed; all zero when M == 0)
+ * Requirements: ss1_forward's, plus BF16 only, BK % 32 == 0, BN % 32 == 0,
+ * G <= 65535.  All buffers 16-byte aligned.  The caller owns every buffer.
+ * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (before
+ * any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c,
+                        const int32_t* hash, const int8_t* sign,
+                        int32_t c, int32_t BK, int32_t BN,
+                        const ss1_tensor* dy, ss1_tensor* dx, ss1_tensor* dW_c,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     ALGOS,
     EXPORTS,
     SS1Error,
+    backward,
     forward,
     forward_fp8w,
     forward_idx,

@@ -28,7 +28,8 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
-           "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w")
+           "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w",
+           "ss1_backward")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -90,6 +91,8 @@ def load():
     lib.ss1_quantize_fp8.argtypes = [tp, tp, vp, vp]
     lib.ss1_forward_fp8w.restype = i32
     lib.ss1_forward_fp8w.argtypes = [tp, tp, vp, vp, vp, i32, i32, i32, tp, vp]
+    lib.ss1_backward.restype = i32
+    lib.ss1_backward.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, tp, tp, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     _LIB = lib
@@ -261,6 +264,24 @@ def forward_fp8w(x, Q, scale, hash_, sign, c: int, BK: int, BN: int, y=None, str
                                  sign.data_ptr(), c, BK, BN, ctypes.byref(dy), _stream(stream))
     _check(st, "ss1_forward_fp8w")
     return y
+
+
+def backward(x, W_c, hash_, sign, c: int, BK: int, BN: int, dy, dx=True, dW_c=True, stream=None):
+    """Gradients of the SS1 forward on the GPU (ss1_backward): returns
+    (dx, dW_c); pass dx=None or dW_c=None to skip one, True to allocate it."""
+    import torch
+    _check_device(x, W_c, hash_, sign, dy)
+    if dx is True:
+        dx = torch.empty_like(x)
+    if dW_c is True:
+        dW_c = torch.empty_like(W_c)
+    ddx = _desc(dx) if dx is not None else None
+    ddw = _desc(dW_c) if dW_c is not None else None
+    st = load().ss1_backward(ctypes.byref(_desc(x)), ctypes.byref(_desc(W_c)), hash_.data_ptr(), sign.data_ptr(),
+                             c, BK, BN, ctypes.byref(_desc(dy)), ctypes.byref(ddx) if ddx else None,
+                             ctypes.byref(ddw) if ddw else None, _stream(stream))
+    _check(st, "ss1_backward")
+    return dx, dW_c
 
 
 def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16") -> str:

@@ -292,3 +292,33 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     if (a.M == 0) return SS1_OK;
     return small ? ss1::launch_smallm(a) : ss1::launch_fused(a);
 }
+
+extern "C" ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash,
+                                   const int8_t* sign, int32_t c, int32_t BK, int32_t BN, const ss1_tensor* dy,
+                                   ss1_tensor* dx, ss1_tensor* dW_c, void* stream) {
+    if (!x || !W_c || !dy) return SS1_ERR_NULL;
+    if (!dx && !dW_c) return SS1_OK;
+    // the forward's checks of x, W_c and the plan, with dy in y's place
+    ForwardArgs a;
+    ss1_status st = check_forward(x, W_c, hash, sign, c, BK, BN, dy, PlanForm::Hash, stream, &a);
+    if (st != SS1_OK) return st;
+    if (x->dtype != SS1_BF16) return SS1_ERR_DTYPE;
+    if (BK % 32 != 0 || BN % 32 != 0) return SS1_ERR_SHAPE;
+    if (a.d.G > 65535 || a.M > (int64_t(1) << 31) - 1) return SS1_ERR_SHAPE;
+    if (dx) {
+        if (dx->reserved != 0) return SS1_ERR_SHAPE;
+        if (dx->dtype != SS1_BF16) return SS1_ERR_DTYPE;
+        if (dx->rows != a.M || dx->cols != a.d.K) return SS1_ERR_SHAPE;
+        if (a.M > 0 && !dx->data) return SS1_ERR_NULL;
+        if (!aligned(dx->data, 16)) return SS1_ERR_ALIGN;
+    }
+    if (dW_c) {
+        if (dW_c->reserved != 0) return SS1_ERR_SHAPE;
+        if (dW_c->dtype != SS1_BF16) return SS1_ERR_DTYPE;
+        if (dW_c->rows != a.d.N || dW_c->cols != a.d.Kc) return SS1_ERR_SHAPE;
+        if (!dW_c->data) return SS1_ERR_NULL;
+        if (!aligned(dW_c->data, 16)) return SS1_ERR_ALIGN;
+    }
+    return ss1::launch_backward(x->data, W_c->data, hash, sign, dy->data, dx ? dx->data : nullptr,
+                                dW_c ? dW_c->data : nullptr, a.M, a.d, stream);
+}

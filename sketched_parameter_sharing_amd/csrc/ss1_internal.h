@@ -55,6 +55,10 @@ ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
                          int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
+// Backward: dW_c (when dW is not null) and dx (when dx is not null), bf16,
+// plan in the forward hash form (ss1_backward.hip).
+ss1_status launch_backward(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign, const void* dy,
+                           void* dx, void* dW, int64_t M, const Dims& d, void* stream);
 // Per-row E4M3 quantization of a compressed weight (ss1_quant.hip).
 ss1_status launch_quantize_fp8(const void* W, int32_t dtype, int64_t N, int64_t Kc, void* Q, float* scale,
                                void* stream);

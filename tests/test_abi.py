@@ -280,6 +280,31 @@ def test_forward_fp8w_argument_checks():
     assert f(T(0, 256, data=None), T(64, 128, F8), T(0, 64, data=None)) == _lib.OK
 
 
+def test_backward_argument_checks():
+    lib = _lib.load()
+
+    def b(x, w, dy, dx, dw, c=2, BK=64, BN=64, h=A, s=A):
+        return lib.ss1_backward(ctypes.byref(x), ctypes.byref(w), h, s, c, BK, BN, ctypes.byref(dy),
+                                ctypes.byref(dx) if dx is not None else None,
+                                ctypes.byref(dw) if dw is not None else None, None)
+
+    x, w, dy, dx, dw = T(96, 512), T(128, 256), T(96, 128), T(96, 512), T(128, 256)
+    assert b(x, w, dy, None, None) == _lib.OK                                   # nothing asked
+    assert b(T(96, 512, _lib.F32), T(128, 256, _lib.F32), T(96, 128, _lib.F32), dx, dw) == _lib.ERR_DTYPE
+    assert b(T(96, 480), T(128, 240), dy, T(96, 480), T(128, 240), BK=48) == _lib.ERR_SHAPE  # BK % 32
+    assert b(x, T(96, 256), T(96, 96), dx, T(96, 256), BN=48) == _lib.ERR_SHAPE            # BN % 32
+    assert b(x, w, T(95, 128), dx, dw) == _lib.ERR_SHAPE                         # dy rows
+    assert b(x, w, dy, T(96, 511), dw) == _lib.ERR_SHAPE                         # dx cols
+    assert b(x, w, dy, dx, T(128, 255)) == _lib.ERR_SHAPE                        # dW_c cols
+    assert b(x, w, dy, T(96, 512, _lib.F32), dw) == _lib.ERR_DTYPE
+    assert b(x, w, dy, dx, T(128, 256, data=None)) == _lib.ERR_NULL
+    assert b(x, w, dy, dx, dw, h=None) == _lib.ERR_NULL
+    assert b(x, w, dy, T(96, 512, data=A + 2), dw) == _lib.ERR_ALIGN
+    assert b(x, w, dy, dx, T(128, 256, data=A + 4)) == _lib.ERR_ALIGN
+    assert lib.ss1_backward(None, ctypes.byref(w), A, A, 2, 64, 64, ctypes.byref(dy), None, None,
+                            None) == _lib.ERR_NULL
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(4, 256, dtype=torch.bfloat16)
