@@ -325,7 +325,7 @@ ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q, const floa
  *   dx : [M][K] BF16, written (NULL: not computed)
  *   dW_c : [N][K/c] BF16, written (NULL: not computed; all zero when M == 0)
  * Requirements: ss1_forward's, plus BF16 only, BK % 32 == 0, BN % 32 == 0,
- * G <= 65535.  All buffers 16-byte aligned.  The caller owns every buffer.
+ * G <= 8192.  All buffers 16-byte aligned.  The caller owns every buffer.
  * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (before
  * any HIP call), SS1_ERR_HIP.
  */

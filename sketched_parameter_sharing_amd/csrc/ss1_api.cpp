@@ -304,7 +304,7 @@ extern "C" ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c, c
     if (st != SS1_OK) return st;
     if (x->dtype != SS1_BF16) return SS1_ERR_DTYPE;
     if (BK % 32 != 0 || BN % 32 != 0) return SS1_ERR_SHAPE;
-    if (a.d.G > 65535 || a.M > (int64_t(1) << 31) - 1) return SS1_ERR_SHAPE;
+    if (a.d.G > 8192 || a.M > (int64_t(1) << 31) - 1) return SS1_ERR_SHAPE;
     if (dx) {
         if (dx->reserved != 0) return SS1_ERR_SHAPE;
         if (dx->dtype != SS1_BF16) return SS1_ERR_DTYPE;

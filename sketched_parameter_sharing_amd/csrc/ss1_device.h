@@ -279,6 +279,28 @@ struct WRaw<true> {
     __device__ __forceinline__ uint4 bf16() const { return fp8x8_to_bf16x8(v); }
 };
 
+// ------------------------------------------------- transposing LDS operand read
+// ds_read_b64_tr_b16 (gfx950), measured lane layout: inside each group of 16
+// lanes, lane l receives element (l % 4) of the 8-byte piece addressed by lane
+// 4i + l/4, for i = 0..3.  So from a row-major LDS tile S (pitch in elements)
+// whose rows run along the MFMA reduction index, the 16x16x32 operand of
+// column block n0 and reduction rows k0..k0+31 -- lane l holds
+// S[k0 + 8*(l/16) + e][n0 + l%16], e = 0..7 -- comes from two such reads:
+// lane l addresses row k0 + 8*(l/16) + 4h + (l%16)/4, column n0 + 4*(l%4), h = 0, 1.
+// Rows must start 8-byte aligned (pitch % 4 == 0, n0 % 4 == 0).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* S, int pitch, int k0, int n0, int lane) {
+    const int q = lane >> 4;
+    const int s = lane & 15;
+    const uint16_t* p = S + (k0 + 8 * q + (s >> 2)) * pitch + n0 + 4 * (s & 3);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * pitch));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Output activation applied in the epilogues, on the float32 accumulator
 // before the output rounding: kActNone, or kActGelu for GELU in its erf
 // form, v * Phi(v) = 0.5 * v * (1 + erf(v / sqrt(2))) (erff: the device math
