@@ -310,10 +310,17 @@ def cpu_baseline_project(wl, budget_s=10.0):
         if t > budget_s / 4 or ng >= wl.G:
             break
         ng = min(wl.G, ng * 4)
+    reps, t0 = 0, time.perf_counter()   # repeat the largest sample to about budget_s
+    while True:
+        oracle.project(vals[:rows], h[:ng], s[:ng], wl.K, rows, wl.c, wl.BK, wl.BN)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= 100:
+            break
+    t = (time.perf_counter() - t0) / reps
     nbytes = e * rows * (wl.K + wl.Kc)
     return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{ng} of {wl.G} groups ({rows} of {wl.N} rows) of the {wl.name} weight, "
-                      f"float64 NumPy oracle (single-threaded loops), {t:.3f} s "
+                      f"float64 NumPy oracle (single-threaded loops), {reps} rep(s) of {t:.3f} s "
                       f"(the sample's algorithmic bytes / time)"}
 
 
@@ -454,10 +461,10 @@ def cpu_baseline(wl, budget_s=10.0):
     inp = make_inputs(wl.with_m(rows))
     reps = 0
     t0 = time.perf_counter()
-    while True:
+    while True:   # whole-workload samples repeat until about budget_s of CPU time
         oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
         reps += 1
-        if time.perf_counter() - t0 > budget_s or reps >= 3:
+        if time.perf_counter() - t0 > budget_s or reps >= 50:
             break
     t = (time.perf_counter() - t0) / reps
     return {"value": 2 * rows * wl.N * wl.K / t / 1e12, "unit": "TFLOP/s", "cores": cores,
