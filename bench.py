@@ -483,7 +483,7 @@ def main():
     ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "backward"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band", "fold"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -533,6 +533,10 @@ def main():
                        "x_l2_gb": wk["x_l2_bytes"] / 1e9},
             "roofline": roofline(wl, t),
         }
+        if rec["config"]["kernel"] == "fold":
+            # the fold kernel multiplies by the expanded weight: its matrix
+            # cores execute the dense FLOP count, c times the algorithmic one
+            rec["config"]["executed_mfma_tflops"] = wk["dense_flops"] / t / 1e12
         return rec, wl
 
     def measure_project(name, steps, warmup):

@@ -73,7 +73,8 @@ typedef enum {
     SS1_ALGO_FUSED = 1,    /* bf16: sketch tile built in LDS, then MFMA (M of any size) */
     SS1_ALGO_SMALLM = 2,   /* bf16: decode shapes, M <= 16, W_c streamed once          */
     SS1_ALGO_GENERIC = 3,  /* any dtype and chunking: LDS-tiled FMA kernel             */
-    SS1_ALGO_BAND = 4      /* bf16, short rows: a band of input rows held in LDS        */
+    SS1_ALGO_BAND = 4,     /* bf16, short rows: a band of input rows held in LDS        */
+    SS1_ALGO_FOLD = 5      /* bf16: W_c expanded on chip, one dense-shaped MFMA GEMM    */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */
@@ -180,6 +181,13 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *   GENERIC: any valid call
  *   BAND   : BF16, BK % 32 == 0, BN in {32, 64, 128}, and 32 input rows of K
  *            bf16 (plus the plan) fit in one block's LDS (K up to about 2400)
+ *   FOLD   : BF16, BK % 64 == 0, and N a multiple of 128 (or 256) that BN
+ *            divides into whole groups; 256*K and 256*Kc under 2^30 elements.
+ *            Multiplies x by the expanded weight W_c S_g (built in LDS from
+ *            W_c, never stored): the same y as the sketch kernels up to
+ *            rounding (no bf16 rounding of a sketch), dense MFMA work.
+ * ss1_forward picks FOLD for large M where its modelled time is below the
+ * sketch kernels' (ss1_select_algo reports the choice).
  */
 ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
                             const int32_t* hash, const int8_t* sign,

@@ -25,6 +25,15 @@ COMMON = [
 ]
 
 
+# Per-source options.  The fold kernels keep 128 float32 accumulators per
+# lane; with MFMA results in ordinary VGPRs they fit beside the operands, while
+# the compiler's default (accumulators in AGPRs, other values spilled there)
+# copies about a hundred registers back and forth on every k-stage.
+EXTRA = {
+    "ss1_fold.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -44,7 +53,8 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *COMMON, f"--offload-arch={ARCH}", "-c", src, "-o", obj]
+        cmd = [hipcc, *COMMON, *EXTRA.get(os.path.basename(src), []), f"--offload-arch={ARCH}", "-c", src,
+               "-o", obj]
         if src.endswith(".cpp"):
             cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)

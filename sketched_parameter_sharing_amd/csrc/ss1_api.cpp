@@ -58,9 +58,25 @@ ss1_status check_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32
     return SS1_OK;
 }
 
-// The kernel ss1_forward picks for a validated call.
+// Estimated time in microseconds of the sketch kernels (band or fused) on a
+// large-M bf16 call, fitted to MI355X measurements: the sketch VALU work,
+// about 0.16 ps per (group, token, input element) and 1.6x that with
+// 128-neuron groups, or the compressed MFMA work at 0.6 PFLOP/s if larger.
+double sketch_estimate_us(const ForwardArgs& a) {
+    const double M = static_cast<double>(a.M), K = static_cast<double>(a.d.K);
+    const double G = static_cast<double>(a.d.G), N = static_cast<double>(a.d.N);
+    const double valu = G * M * K * 0.16e-6 * (a.d.BN >= 128 ? 1.6 : 1.0);
+    const double mfma = 2.0 * M * N * static_cast<double>(a.d.Kc) / 0.6e9;
+    return valu > mfma ? valu : mfma;
+}
+
+// The kernel ss1_forward picks for a validated call: decode shapes go to the
+// small-M kernel; otherwise the fold kernel when its estimate is clearly
+// (10%) below the sketch kernels', else the band kernel where a band of input
+// rows fits in LDS, else the fused kernel.
 int32_t auto_algo(const ForwardArgs& a) {
     if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
+    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return SS1_ALGO_FOLD;
     if (ss1::band_supported(a, 48)) return SS1_ALGO_BAND;
     if (ss1::fused_supported(a)) return SS1_ALGO_FUSED;
     return SS1_ALGO_GENERIC;
@@ -71,6 +87,7 @@ ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
         case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
         case SS1_ALGO_BAND: return ss1::launch_band(a);
         case SS1_ALGO_FUSED: return ss1::launch_fused(a);
+        case SS1_ALGO_FOLD: return ss1::launch_fold(a);
         default: return ss1::launch_generic(a);
     }
 }
@@ -94,6 +111,9 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_BAND:
             if (!ss1::band_supported(a, 32)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_band(a);
+        case SS1_ALGO_FOLD:
+            if (!ss1::fold_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_fold(a);
         case SS1_ALGO_GENERIC:
             return a.M == 0 ? SS1_OK : ss1::launch_generic(a);
         default:

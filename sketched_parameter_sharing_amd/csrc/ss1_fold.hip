@@ -1,0 +1,455 @@
+// The SS1 forward as one dense-shaped contraction: y = x * B^T, where B is the
+// layer's expanded weight, B[n][j*BK + u] = sign_g(j) * W_c[n][h_g(j)*BK + u]
+// for neuron n of group g (the SS1 summary page, "Approach": the sketch is a
+// linear map S_g of x, so W_c * (S_g x) = (W_c S_g) x, and W_c S_g places each
+// compressed chunk of W_c, sign-flipped, at every input chunk that hashes to
+// it).  B is never written to memory: each k-stage loads the W_c chunk that
+// the stage's input chunk maps to straight into the LDS weight tile, and the
+// chunk's sign is applied to the bf16 sign bits as the operand leaves LDS.
+//
+// Why this form on gfx950: the sketch of x costs VALU work (a widen, a signed
+// add and a rounding per element, per group) whose throughput on CDNA4 is about
+// 1/64 of the MFMA rate, so sketching every group's input costs more than the
+// c-fold MFMA work it saves.  Here every multiply runs on the matrix cores
+// (K/Kc = c times the compressed work) and no element of x is gathered per
+// group; what stays compressed is the weight in HBM (N x Kc) and its traffic.
+// The sums also differ from the sketch kernels in rounding only: there the
+// sketch is rounded to bf16 before the MFMA, here nothing is rounded before
+// the float32 accumulators.
+//
+// Block: WM x WN waves (8 or 4), output tile BM tokens x BNB neurons (BNB a
+// multiple of BN, so a tile holds whole groups).  K runs in stages of KS = 64
+// (BK % 64 == 0, so a stage sits inside one input chunk j).  Stages reach LDS
+// by direct buffer-to-LDS loads (no registers, no LDS write instructions),
+// NSTG buffers deep, loaded NSTG-1 stages ahead.  Each
+// 16-byte piece of a tile row sits at a slot XOR-swizzled by the row, which
+// keeps the 16 rows read by one quarter-wave on distinct LDS banks.  A stage's
+// weight rows are the W_c chunk that its input chunk maps to (the load offset
+// carries it; an absent source points past the buffer and loads zeros), and
+// the chunk's sign is applied to the weight operand as it leaves LDS.  The
+// MFMA computes the transposed tile y^T = B x^T with each wave's weight rows
+// placed in a permuted order, so that every lane ends up holding 4*FN
+// consecutive neurons of one token and stores them as 16-byte vectors.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "ss1_device.h"
+#include "ss1_internal.h"
+
+namespace ss1 {
+
+namespace {
+
+using namespace dev;
+
+// Neuron (inside a wave's tile of 16*FN) held by LDS row p of that tile:
+// MFMA row r = 4a + b of neuron block nb = p / 16 holds neuron a*4*FN + nb*4 + b.
+template <int FN>
+__device__ __forceinline__ int fold_neuron(int p) {
+    const int nb = p >> 4;
+    const int r = p & 15;
+    return (r >> 2) * 4 * FN + nb * 4 + (r & 3);
+}
+
+// XOR key of LDS row p for rows of RB bytes: the 16 rows that one quarter-wave
+// reads at a given 16-byte column land on 16 distinct bank groups.
+template <int RB>
+__device__ __forceinline__ int fold_key(int p) {
+    return (p / (256 / RB)) % (RB / 16);
+}
+
+// Plan of the block's groups in LDS, per (group gl of the tile, input chunk j):
+// s_off = byte offset inside a W_c row of the chunk j maps to (t*BK*2), or
+// kFoldAbsent for an absent source; s_sgn = 0x80008000 for a negative sign,
+// else 0.  Hash form: pi/ps are hash/sign [G][J]; index form: idx/isign
+// [G][Jc][c].  Entries out of range leave the source absent.
+constexpr uint32_t kFoldAbsent = 0x7FFFFFFFu;  // plus any in-tile offset: past the extent
+
+template <bool FROM_HASH>
+__device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g0, int ngr,
+                                int J, int Jc, int c, int BK, uint32_t* s_off, uint32_t* s_sgn) {
+    const int tid = threadIdx.x;
+    const int nt = blockDim.x;
+    const int total = ngr * J;
+    if (FROM_HASH) {
+        const int32_t* gi = pi + static_cast<size_t>(g0) * J;
+        const int8_t* gs = ps + static_cast<size_t>(g0) * J;
+        for (int e = tid; e < total; e += nt) {
+            const int t = gi[e];
+            const int s = gs[e];
+            const bool ok = t >= 0 && t < Jc && (s == 1 || s == -1);
+            s_off[e] = ok ? static_cast<uint32_t>(t * BK) * 2u : kFoldAbsent;
+            s_sgn[e] = (ok && s < 0) ? 0x80008000u : 0u;
+        }
+    } else {
+        for (int e = tid; e < total; e += nt) {
+            s_off[e] = kFoldAbsent;
+            s_sgn[e] = 0u;
+        }
+        __syncthreads();
+        const int per = Jc * c;
+        const int32_t* gi = pi + static_cast<size_t>(g0) * per;
+        const int8_t* gs = ps + static_cast<size_t>(g0) * per;
+        for (int e = tid; e < ngr * per; e += nt) {
+            const int gl = e / per;
+            const int t = (e - gl * per) / c;
+            const int j = gi[e];
+            const int s = gs[e];
+            if (j >= 0 && j < J && (s == 1 || s == -1)) {
+                s_off[gl * J + j] = static_cast<uint32_t>(t * BK) * 2u;
+                s_sgn[gl * J + j] = s < 0 ? 0x80008000u : 0u;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Direct buffer-to-LDS load of 16 bytes per lane: lane l writes its 16 bytes
+// at LDS byte address lds + 16*l (an offset past the descriptor's extent
+// writes zeros).  Issued from inline asm: the instruction has no register
+// result, and the compiler, which cannot tell these LDS writes apart from the
+// operand reads of other stages, would otherwise wait for every one in flight
+// before each LDS read.  The stage barriers order them instead; the memory
+// clobber keeps LDS accesses on their side of the issue point.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 fold_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu), static_cast<int>(bytes),
+                 kBufferWord3};
+}
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+// M0 is listed as clobbered for the record; nothing else in these kernels
+// uses it (no LDS DMA builtins, no relative register indexing), and clang's
+// note that a reserved register is not preserved across the statement is
+// silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
+                 "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Waits until at most N of this wave's buffer loads are in flight and its LDS
+// reads are done, then joins the workgroup barrier.  A compiler fence here
+// would wait for every direct-to-LDS load in flight (they count as LDS
+// writes), which would drain the stage pipeline; the memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void fold_stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
+__global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                   const int32_t* __restrict__ pi, const int8_t* __restrict__ ps,
+                                                   uint16_t* __restrict__ y, int M, int K, int N, int J, int Jc,
+                                                   int c, int BK, int BN, int n_mt, int act) {
+    constexpr int NWV = WM * WN;                  // waves per block
+    constexpr int TMW = BM / WM, TNW = BNB / WN;  // wave tile: tokens x neurons
+    constexpr int FM = TMW / 16, FN = TNW / 16;   // 16x16 MFMA blocks per wave
+    static_assert(FM * 16 == TMW && FN * 16 == TNW && FN % 2 == 0, "wave tile");
+    constexpr int RB = KS * 2;                    // bytes per tile row
+    constexpr int CPR = RB / 16;                  // 16-byte pieces per row
+    constexpr int RPI = 1024 / RB;                // rows filled by one wave-wide load
+    constexpr int XI = BM / RPI / NWV;            // x loads per wave per stage
+    constexpr int WI = BNB / RPI / NWV;           // weight loads per wave per stage
+    constexpr int DPW = XI + WI;
+    static_assert(XI * RPI * NWV == BM && WI * RPI * NWV == BNB, "tile rows must split over the waves");
+    static_assert((NWV * RPI) % 16 == 0, "the swizzle key must repeat between a wave's loads");
+    static_assert(NSTG >= 2 && NSTG <= 4, "stage count");
+    static_assert(KS == 32 || KS == 64, "a stage is one or two 32-wide halves");
+    constexpr int HALVES = KS / 32;
+    constexpr int SX = BM * RB, SB = (BM + BNB) * RB;  // x tile bytes, stage bytes
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t fold_smem[];
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(fold_smem + NSTG * SB);
+
+    // Tile order: each XCD takes a contiguous range of tiles (xcd_tile); in
+    // that range tiles go in column-major strips of GM row tiles, so the
+    // blocks running together on one XCD share a few x row tiles and a few
+    // weight column tiles in its L2.
+    constexpr int GM = 4;
+    const int n_nt = N / BNB;
+    const int tile = xcd_tile(blockIdx.x, n_mt * n_nt);
+    const int strip = tile / (GM * n_nt);
+    const int gm = min(GM, n_mt - strip * GM);
+    const int rem = tile - strip * GM * n_nt;
+    const int mt = strip * GM + rem % gm;
+    const int nt = rem / gm;
+    const int m0 = mt * BM;
+    const int n0 = nt * BNB;
+    const int ngr = BNB / BN;
+    uint32_t* s_sgn = s_off + ngr * J;
+    const int Kc = Jc * BK;
+    stage_fold_plan<FROM_HASH>(pi, ps, n0 / BN, ngr, J, Jc, c, BK, s_off, s_sgn);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nstage = K / KS;
+
+    // ---- direct-to-LDS loads.  Wave-wide load i of a tile fills rows
+    // [i*RPI, i*RPI + RPI); lane l writes 16 bytes at row i*RPI + l/CPR, slot
+    // l%CPR, and so reads piece (l%CPR) ^ key(row) of that row.  This wave
+    // does loads wave, wave+NWV, ...; the key repeats every 16 rows, so one
+    // lane offset serves all of them.
+    const i32x4 xr = fold_rsrc(x + static_cast<size_t>(m0) * K,
+                               static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K * 2));
+    const i32x4 wr = fold_rsrc(w + static_cast<size_t>(n0) * Kc, static_cast<uint32_t>(static_cast<size_t>(BNB) * Kc * 2));
+    const int lrow = lane / CPR;
+    const int piece = (lane % CPR) ^ fold_key<RB>(wave * RPI + lrow);
+    const uint32_t x_voff = static_cast<uint32_t>(lrow * K + piece * 8) * 2u;
+    uint32_t w_voff[WI];
+    int w_gl[WI];  // group (inside the tile) of this lane's weight row, per load
+#pragma unroll
+    for (int ii = 0; ii < WI; ++ii) {
+        const int p = (wave + NWV * ii) * RPI + lrow;                 // LDS row in the weight tile
+        const int n = (p / TNW) * TNW + fold_neuron<FN>(p % TNW);    // neuron inside the tile
+        w_voff[ii] = static_cast<uint32_t>(n * Kc + piece * 8) * 2u;
+        w_gl[ii] = n / BN;
+    }
+    const uint32_t lds0 = lds_address(fold_smem);
+    auto dma = [&](int s, int buf) {
+        const int k0 = s * KS;
+        const int j = k0 / BK;
+        const uint32_t u0b = static_cast<uint32_t>(k0 - j * BK) * 2u;
+        const uint32_t base = lds0 + static_cast<uint32_t>(buf * SB);
+        uint32_t off[WI];
+#pragma unroll
+        for (int ii = 0; ii < WI; ++ii) off[ii] = s_off[w_gl[ii] * J + j];
+#pragma unroll
+        for (int ii = 0; ii < XI; ++ii) {
+            const int row0 = (wave + NWV * ii) * RPI;
+            lds_dma16(xr, base + row0 * RB, x_voff, static_cast<uint32_t>((row0 * K + k0) * 2));
+        }
+#pragma unroll
+        for (int ii = 0; ii < WI; ++ii) {
+            const int row0 = (wave + NWV * ii) * RPI;
+            lds_dma16(wr, base + SX + row0 * RB, w_voff[ii] + off[ii] + u0b, 0u);
+        }
+    };
+
+    // ---- operands.  Lane l reads row (block base + l%16) at logical piece
+    // kk/8 + l/16; the key of that row depends on l%16 only.
+    const int fr = lane & 15;
+    const int q = lane >> 4;
+    const int key = fold_key<RB>(fr);
+    // group (inside the tile) of the weight rows this lane feeds to the MFMA
+    const int sg_gl = (wn * TNW + (fr >> 2) * 4 * FN) / BN;
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Operands of one 32-wide half of a stage: FN weight blocks (sign applied)
+    // and FM token blocks.
+    struct Ops {
+        bf16x8 w[FN], x[FM];
+    };
+    auto read_ops = [&](int s, int buf, int half, Ops& o) {
+        const uint32_t sx = s_sgn[sg_gl * J + (s * KS) / BK];
+        const int off = ((half * 4 + q) ^ key) * 16;  // piece half*4 + q of CPR
+        const uint8_t* X = fold_smem + buf * SB + (wm * TMW + fr) * RB + off;
+        const uint8_t* W = fold_smem + buf * SB + SX + (wn * TNW + fr) * RB + off;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            uint4 v = *reinterpret_cast<const uint4*>(W + i * 16 * RB);
+            v.x ^= sx;
+            v.y ^= sx;
+            v.z ^= sx;
+            v.w ^= sx;
+            o.w[i] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj) o.x[jj] = *reinterpret_cast<const bf16x8*>(X + jj * 16 * RB);
+    };
+    auto mma = [&](const Ops& o) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FM; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.w[i], o.x[jj], acc[i][jj], 0, 0, 0);
+    };
+    // wait until stage s's loads (all waves) have landed; `ahead` stages were
+    // issued after it
+    auto wait_stage = [&](int ahead) {
+        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
+        else if (ahead == 1) fold_stage_barrier<DPW>();
+        else fold_stage_barrier<0>();
+    };
+
+    // ---- pipeline.  Stage s lives in buffer s % NSTG.
+    // Loaded NSTG-1 stages ahead.  At the top of stage s a barrier finds
+    // stage s loaded (all waves) and every wave done with stage s-1, whose
+    // buffer the loads of stage s+NSTG-1 then refill.
+#pragma unroll
+    for (int p = 0; p < NSTG - 1; ++p)
+        if (p < nstage) dma(p, p);
+    auto step = [&](int s, int buf) {
+        wait_stage(min(NSTG - 2, nstage - 1 - s));
+        if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        Ops o[HALVES];
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) read_ops(s, buf, h, o[h]);
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) mma(o[h]);
+    };
+    for (int s0 = 0; s0 < nstage; s0 += NSTG) {
+#pragma unroll
+        for (int b = 0; b < NSTG; ++b)
+            if (s0 + b < nstage) step(s0 + b, b);
+    }
+
+    // epilogue: lane holds neurons wn*TNW + (lane/16)*4*FN + nb*4 + i of token
+    // wm*TMW + mb*16 + lane%16
+    const int nbase = n0 + wn * TNW + q * 4 * FN;
+#pragma unroll
+    for (int mb = 0; mb < FM; ++mb) {
+        const int m = m0 + wm * TMW + mb * 16 + fr;
+        if (m >= M) continue;
+        uint16_t* yr = y + static_cast<size_t>(m) * N + nbase;
+#pragma unroll
+        for (int h = 0; h < FN / 2; ++h) {
+            uint4 o;
+            o.x = pack_bf16(apply_act(acc[2 * h][mb][0], act), apply_act(acc[2 * h][mb][1], act));
+            o.y = pack_bf16(apply_act(acc[2 * h][mb][2], act), apply_act(acc[2 * h][mb][3], act));
+            o.z = pack_bf16(apply_act(acc[2 * h + 1][mb][0], act), apply_act(acc[2 * h + 1][mb][1], act));
+            o.w = pack_bf16(apply_act(acc[2 * h + 1][mb][2], act), apply_act(acc[2 * h + 1][mb][3], act));
+            *reinterpret_cast<uint4*>(yr + 8 * h) = o;
+        }
+    }
+}
+
+#ifndef FOLD_BIG_KS
+#define FOLD_BIG_KS 64
+#define FOLD_BIG_NSTG 2
+#endif
+
+struct FoldCfg {
+    int BM, BNB, KS, NSTG;
+    size_t lds;
+};
+
+inline size_t fold_lds(int BM, int BNB, int KS, int NSTG, const Dims& d) {
+    return static_cast<size_t>(NSTG) * (BM + BNB) * KS * 2 + static_cast<size_t>(2) * (BNB / d.BN) * d.J * 4;
+}
+
+int device_attribute(hipDeviceAttribute_t attr, int fallback) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fallback;
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) return fallback;
+    return v;
+}
+
+int max_lds_per_block() { return device_attribute(hipDeviceAttributeMaxSharedMemoryPerBlock, 64 * 1024); }
+
+// Tile choice (tokens x neurons), the neuron tile a whole number of groups
+// that divides N:
+//   256 x 256, 8 waves of 128 x 64, 2 stages (two waves per SIMD: one
+//              multiplies while the other waits on LDS or a barrier);
+//   256 x 128, 4 waves of 128 x 64, 3 stages, when N is not a multiple of 256;
+//   128 x 128, 4 waves of 64 x 64, 4 stages, for M <= 128 or when only 128
+//              divides N and M is small.
+// Buffer offsets are 32-bit: a tile's rows must span less than 2 GiB.
+inline FoldCfg fold_config(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    if (d.BK % 32 != 0) return FoldCfg{0, 0, 0, 0, 0};
+    auto fits = [&](int BNB) { return BNB % d.BN == 0 && d.N % BNB == 0; };
+    int BM = 0, BNB = 0, NSTG = 0, KS = 64;
+    if (fits(256) && a.M > 128) {
+        BM = 256;
+        BNB = 256;
+        NSTG = FOLD_BIG_NSTG;
+        KS = FOLD_BIG_KS;
+    } else if (fits(128) && a.M > 128) {
+        BM = 256;
+        BNB = 128;
+        NSTG = 3;
+    } else if (fits(128)) {
+        BM = 128;
+        BNB = 128;
+        NSTG = 4;
+    }
+    if (d.BK % KS != 0) {  // 32-wide stages, twice as many buffers
+        KS = 32;
+        NSTG = std::min(2 * NSTG, 4);
+    }
+    if (BM == 0) return FoldCfg{0, 0, 0, 0, 0};
+    if (static_cast<double>(std::max(BM * d.K, BNB * d.Kc)) * 2.0 >= 2147483648.0) return FoldCfg{0, 0, 0, 0, 0};
+    const size_t lds = fold_lds(BM, BNB, KS, NSTG, d);
+    if (lds > static_cast<size_t>(max_lds_per_block())) return FoldCfg{0, 0, 0, 0, 0};
+    return FoldCfg{BM, BNB, KS, NSTG, lds};
+}
+
+template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
+ss1_status launch_fold_cfg(const ForwardArgs& a, const FoldCfg& cfg) {
+    const Dims& d = a.d;
+    const int n_mt = static_cast<int>((a.M + BM - 1) / BM);
+    const long long blocks = static_cast<long long>(n_mt) * (d.N / BNB);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    auto kern = &fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(cfg.lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(WM * WN * 64), cfg.lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, n_mt, a.act);
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
+
+template <bool FROM_HASH>
+ss1_status launch_fold_t(const ForwardArgs& a) {
+    const FoldCfg cfg = fold_config(a);
+    if (cfg.BM == 256 && cfg.BNB == 256) {
+        if (cfg.KS == 64 && cfg.NSTG == 2) return launch_fold_cfg<256, 256, 2, 4, 64, 2, FROM_HASH>(a, cfg);
+        if (cfg.KS == 32 && cfg.NSTG == 4) return launch_fold_cfg<256, 256, 2, 4, 32, 4, FROM_HASH>(a, cfg);
+    }
+    if (cfg.BM == 256 && cfg.BNB == 128) {
+        if (cfg.KS == 64) return launch_fold_cfg<256, 128, 2, 2, 64, 3, FROM_HASH>(a, cfg);
+        return launch_fold_cfg<256, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg);
+    }
+    if (cfg.BM == 128 && cfg.BNB == 128) {
+        if (cfg.KS == 64) return launch_fold_cfg<128, 128, 2, 2, 64, 4, FROM_HASH>(a, cfg);
+        return launch_fold_cfg<128, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg);
+    }
+    return SS1_ERR_ALGO;
+}
+
+}  // namespace
+
+bool fold_supported(const ForwardArgs& a) {
+    return a.dtype == SS1_BF16 && fold_config(a).BM > 0;
+}
+
+// Run time model fitted to MI355X measurements of the 256 x 256 tile: per
+// round of tiles (one tile per compute unit) 26.1 ns per input element of K
+// plus 6.2 us; the 4-wave tiles run about 1.3x slower per unit of area.
+double fold_estimate_us(const ForwardArgs& a) {
+    const FoldCfg cfg = fold_config(a);
+    if (a.dtype != SS1_BF16 || cfg.BM == 0 || a.M <= 0) return 1e300;
+    const double cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
+    const double tiles = std::ceil(static_cast<double>(a.M) / cfg.BM) * static_cast<double>(a.d.N / cfg.BNB);
+    const double rounds = std::ceil(tiles / cus);
+    const double area = static_cast<double>(cfg.BM) * cfg.BNB / 65536.0;
+    return rounds * (0.0261 * static_cast<double>(a.d.K) + 6.2) * area * (area < 1.0 ? 1.3 : 1.0);
+}
+
+ss1_status launch_fold(const ForwardArgs& a) {
+    if (a.w_fp8) return SS1_ERR_ALGO;
+    return a.form == PlanForm::Hash ? launch_fold_t<true>(a) : launch_fold_t<false>(a);
+}
+
+}  // namespace ss1

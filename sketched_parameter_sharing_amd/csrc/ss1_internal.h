@@ -47,12 +47,18 @@ bool smallm_supported(const ForwardArgs& a);
 // Band kernel: the layer's rows are short enough for a band of at least
 // min_rows input rows to sit in LDS.
 bool band_supported(const ForwardArgs& a, int min_rows);
+// Fold kernel (ss1_fold.hip): bf16, BK % 32 == 0, a 128- or 256-neuron tile of
+// whole groups that divides N.
+bool fold_supported(const ForwardArgs& a);
+// Estimated fold-kernel time in microseconds (huge when it cannot run).
+double fold_estimate_us(const ForwardArgs& a);
 
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);
 ss1_status launch_smallm(const ForwardArgs& a);
 ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
+ss1_status launch_fold(const ForwardArgs& a);
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
                          int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
 // Backward: dW_c (when dW is not null) and dx (when dx is not null), bf16,

@@ -142,6 +142,9 @@ FORWARD_ERRORS = [
     ("algo fused BN", T(8, 256), T(48, 128), T(8, 48), {"BN": 48, "algo": _lib.ALGO_FUSED}, _lib.ERR_ALGO),
     ("algo smallm M", T(17, 256), T(64, 128), T(17, 64), {"algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
     ("algo smallm BN", T(4, 256), T(40, 128), T(4, 40), {"BN": 40, "algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
+    ("algo fold f32", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32),
+     {"algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
+    ("algo fold BK", T(8, 256), T(64, 128), T(8, 64), {"BK": 32, "algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
     ("algo unknown", T(8, 256), T(64, 128), T(8, 64), {"algo": 9}, _lib.ERR_ALGO),
 ]
 

@@ -8,7 +8,9 @@ Bars (written in each test):
 * bf16 layers: max|y - y_ref| / max|y_ref| <= 2e-2, and elementwise against
   the oracle's mirror (float32 sketch rounded to bf16, float64 contraction):
   |y - y_mirror| <= 2^-7 |y_mirror| + 1e-5 max|y_mirror| (one bf16 ulp plus
-  float32 accumulation-order slack).
+  float32 accumulation-order slack).  The fold kernel multiplies x by the
+  expanded weight and never rounds a sketch, so its mirror is the float64
+  oracle itself, under the same bound.
 * integer-valued inputs: every intermediate is an exact integer, so float32
   output equals the oracle exactly and bf16 output equals the oracle rounded to
   bf16 (nearest, ties to even) bit for bit.
@@ -77,16 +79,25 @@ def rel_err(y, ref):
     return float(np.max(np.abs(y - ref)) / scale) if ref.size else 0.0
 
 
-def check_bf16(wl, inp, y, rows=None):
+def kernel_of(wl, algo):
+    """The kernel a call with this algo runs (auto resolved by the library)."""
+    return ss1.select_algo(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype) if algo == "auto" else algo
+
+
+def check_bf16(wl, inp, y, rows=None, kernel=None):
     """Tolerance gate against the float64 oracle plus the mirror check, on all
-    rows or on the given sample of rows."""
+    rows or on the given sample of rows.  ``kernel`` is the kernel that ran
+    (None: one of the sketch kernels)."""
     h, s = oracle_plan(wl)
     x = inp.x if rows is None else inp.x[rows]
     yg = host(y) if rows is None else host(y)[rows]
     ref = oracle.forward(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
     err = rel_err(yg, ref)
     assert err <= TOL_BF16, f"{wl.name}: normwise error {err:.3e} > {TOL_BF16}"
-    mir = oracle.forward_mirror(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, sketch_bf16=True)
+    if kernel == "fold":
+        mir = ref
+    else:
+        mir = oracle.forward_mirror(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, sketch_bf16=True)
     top = np.max(np.abs(mir)) if mir.size else 0.0
     bad = np.abs(yg - mir) > 2.0 ** -7 * np.abs(mir) + 1e-5 * top
     assert not bad.any(), f"{wl.name}: {int(bad.sum())} outputs off the mirror oracle by more than one bf16 ulp"
@@ -137,9 +148,10 @@ BF16_NAMES = ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m4096", "llama
 
 
 @pytest.mark.parametrize("name", BF16_NAMES)
-@pytest.mark.parametrize("algo", ["auto", "fused", "band", "generic"])
+@pytest.mark.parametrize("algo", ["auto", "fused", "band", "generic", "fold"])
 def test_bf16_reduced_m(name, algo):
-    # M = 300: two full 128-row tiles and a ragged tail (and a ragged band)
+    # M = 300: two full 128-row tiles and a ragged tail (and a ragged band;
+    # for the fold kernel one 256-row tile and a ragged one)
     wl = WORKLOADS[name].with_m(300)
     if algo == "generic" and wl.N * wl.K > 4096 * 4096:
         pytest.skip("generic kernel checked on the smaller layers")
@@ -149,7 +161,8 @@ def test_bf16_reduced_m(name, algo):
     except ss1.SS1Error as e:
         assert e.status == 7 and algo == "band"
         pytest.skip("input rows too long for the band kernel")
-    print(f"{name} algo={algo} err={check_bf16(wl, inp, y):.3e}", flush=True)
+    err = check_bf16(wl, inp, y, kernel=kernel_of(wl, algo))
+    print(f"{name} algo={algo} err={err:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name", BF16_NAMES + ["llama_gateup_m16", "llama_down_m16",
@@ -164,14 +177,17 @@ def test_bf16_full_size_sampled_rows(name):
     else:
         rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, 62, replace=False)]))
     assert np.isfinite(host(y)).all()
-    print(f"{name} full M={wl.M} err={check_bf16(wl, inp, y, rows):.3e}", flush=True)
+    err = check_bf16(wl, inp, y, rows, kernel=kernel_of(wl, "auto"))
+    print(f"{name} full M={wl.M} kernel={kernel_of(wl, 'auto')} err={err:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("gpt2l_down", "fused"),
                                        ("llama_gateup_m16", "smallm"), ("llama_down_m16", "smallm"),
                                        ("square_c8_bn128", "fused"), ("square_c1_bn32", "fused"),
                                        ("gpt2l_up", "generic"), ("gpt2s_up", "band"),
-                                       ("gpt2l_up", "band")])
+                                       ("gpt2l_up", "band"), ("gpt2s_up", "fold"),
+                                       ("llama_down_m4096", "fold"), ("square_c1_bn128", "fold"),
+                                       ("square_c8_bn32", "fold")])
 def test_bf16_integer_bit_exact(name, algo):
     wl = WORKLOADS[name]
     wl = wl.with_m(min(wl.M, 300 if algo != "smallm" else 16))
@@ -211,19 +227,20 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
     inp = make_inputs(wl)
     p = device_plan(wl)
     ys = {}
-    for algo in ("auto", "fused", "smallm", "band", "generic"):
+    for algo in ("auto", "fused", "smallm", "band", "generic", "fold"):
         try:
             ys[algo] = run(wl, inp, p, algo=algo)
         except ss1.SS1Error as e:
             assert e.status == 7  # kernel not applicable to this shape
             continue
-        check_bf16(wl, inp, ys[algo])
+        check_bf16(wl, inp, ys[algo], kernel=kernel_of(wl, algo))
     assert "auto" in ys and "generic" in ys
 
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("llama_down_m16", "smallm"),
                                        ("gpt2l_up", "generic"), ("tiny", "generic"),
-                                       ("gpt2s_up", "band"), ("gpt2l_up", "band")])
+                                       ("gpt2s_up", "band"), ("gpt2l_up", "band"),
+                                       ("gpt2s_up", "fold"), ("llama_gateup_m4096", "fold")])
 def test_hash_and_index_forms_agree(name, algo):
     wl = WORKLOADS[name]
     wl = wl.with_m(min(wl.M, 256))
@@ -242,14 +259,57 @@ def test_m0_is_noop_and_y_fully_written():
     w = torch.zeros((wl.N, wl.Kc), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((0, wl.N), dtype=torch.bfloat16, device="cuda")
     ss1.forward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, y)
+    for algo in ("fold", "band", "fused"):
+        ss1.forward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, y, algo=algo)
     # every output is written: start from NaN
     wl2 = wl.with_m(131)
     inp = make_inputs(wl2)
-    for algo in ("fused", "band", "generic"):
+    for algo in ("fused", "band", "generic", "fold"):
         y = torch.full((131, wl.N), float("nan"), dtype=torch.bfloat16, device="cuda")
         p.forward(dev(inp.x_bits, "bf16"), dev(inp.w_bits, "bf16"), y=y, algo=algo)
         torch.cuda.synchronize()
         assert torch.isfinite(y).all()
+
+
+@pytest.mark.parametrize("name,M", [("gpt2s_up", 1), ("gpt2s_up", 77), ("gpt2s_up", 128), ("gpt2s_up", 129),
+                                    ("gpt2l_down", 300), ("square_c2_bn128", 513), ("llama_down_m4096", 40)])
+def test_fold_tile_shapes(name, M):
+    # 128 x 128 tiles (M <= 128), 256 x 256 tiles with a ragged last row tile,
+    # 128-neuron groups (two per tile), and a 14336-long K
+    wl = WORKLOADS[name].with_m(M)
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    print(f"{name} M={M} fold err={check_bf16(wl, inp, y, kernel='fold'):.3e}", flush=True)
+
+
+def test_fold_neuron_tile_of_128():
+    # N = 384 is not a multiple of 256: 256 x 128 tiles of 4 waves
+    wl = Workload("n384", 9, 1, 300, 512, 384, 2, 64, 64, "bf16")
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    check_bf16(wl, inp, y, kernel="fold")
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [
+    (300, 1536, 512, 2, 32, 64),    # 32-wide stages: 256 x 256 tiles, four buffers
+    (300, 1536, 384, 2, 96, 64),    # 256 x 128 tiles, a stage at offset 32 of a chunk
+    (100, 768, 256, 3, 32, 32),     # 128 x 128 tiles, eight groups per tile
+])
+def test_fold_32_wide_stages(M, K, N, c, BK, BN):
+    wl = Workload("fold32", 9, 2, M, K, N, c, BK, BN, "bf16")
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    check_bf16(wl, inp, y, kernel="fold")
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
 
 
 def test_runs_on_a_side_stream():
