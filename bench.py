@@ -100,29 +100,40 @@ CSRC = os.path.join(ROOT, "sketched_parameter_sharing_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def kernel_source_sha256():
-    """Hash of every device source (kernels and the headers they include)."""
+# Device sources each traffic record depends on (the kernels it measures and
+# the headers they include).
+FORWARD_SOURCES = ("ss1_kernels.hip", "ss1_fold.hip", "ss1_device.h", "ss1_internal.h")
+PROJECT_SOURCES = ("ss1_project.hip", "ss1_device.h", "ss1_internal.h")
+
+
+def record_sources(name):
+    return PROJECT_SOURCES if name.startswith("project:") else FORWARD_SOURCES
+
+
+def kernel_source_sha256(names=None):
+    """Hash of the given device sources (default: every kernel source and
+    header)."""
+    if names is None:
+        names = [n for n in os.listdir(CSRC) if n.endswith((".hip", ".h"))]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(names):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def recorded_traffic(name):
     """Calibrated HBM bytes per launch for record `name` (a workload, or
-    "project:<workload>") from the committed counter record, or None when
-    there is none or the kernels changed since."""
+    "project:<workload>" / "fp8:<workload>") from the committed counter
+    record, or None when there is none or the sources of its kernels changed
+    since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
-        return None
     w = rec.get("workloads", {}).get(name)
-    if not w:
+    if not w or w.get("sources_sha256") != kernel_source_sha256(record_sources(name)):
         return None
     return w.get("hbm_bytes_per_launch")
 

@@ -331,11 +331,6 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     }
 }
 
-#ifndef FOLD_BIG_KS
-#define FOLD_BIG_KS 64
-#define FOLD_BIG_NSTG 2
-#endif
-
 struct FoldCfg {
     int BM, BNB, KS, NSTG;
     size_t lds;
@@ -370,8 +365,7 @@ inline FoldCfg fold_config(const ForwardArgs& a) {
     if (fits(256) && a.M > 128) {
         BM = 256;
         BNB = 256;
-        NSTG = FOLD_BIG_NSTG;
-        KS = FOLD_BIG_KS;
+        NSTG = 2;
     } else if (fits(128) && a.M > 128) {
         BM = 256;
         BNB = 128;
