@@ -13,6 +13,8 @@
 //   into LDS (the sketch summed in float32 over the c sources in
 //   ascending order and rounded to bf16, as in the forward) and runs its
 //   MFMAs on them; the four partial tiles are summed at the end.
+// dx: the fold kernel's dx variant (ss1_fold.hip) when N % 64 == 0, K % 256
+//   == 0 and BK % 64 == 0; otherwise
 // dx_wide_kernel (K % 128 == 0, N % 64 == 0): 128 x 128 dx tiles, see below.
 // dx_kernel (otherwise): block = 4 waves, output tile 128 tokens x 32 columns of one input
 //   chunk j, wave w owning tokens [32w, 32w+32).  Per stage of 128 neurons
@@ -448,6 +450,7 @@ ss1_status launch_backward(const void* x, const void* W_c, const int32_t* hash, 
         if (st != SS1_OK) return st;
     }
     if (dx && M > 0) {
+        if (dx_fold_supported(M, d)) return launch_dx_fold(dy, W_c, hash, sign, dx, M, d, stream);
         const int cpt = static_cast<int>((kDxwT - 32) / d.BK + 2);
         if (d.K % kDxwT == 0 && d.N % kDxwN == 0 && d.G * cpt <= 8192) {
             const dim3 grid(static_cast<unsigned>((M + kDxwT - 1) / kDxwT), static_cast<unsigned>(d.K / kDxwT));

@@ -331,6 +331,216 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     }
 }
 
+// ================================================================ dx kernel
+// dx = dy B, with B the expanded weight of the forward (dx[m][j*BK + u] =
+// sum_n dy[m][n] sign_g(n)(j) W_c[n][h_g(n)(j)*BK + u]): the same contraction
+// with the roles of the two indices swapped.  The kernel computes the
+// transposed tile dx^T = B^T dy^T: the weight operand (16 input features x
+// 32 neurons) comes out of an LDS tile of W_c rows through ds_read_b64_tr_b16,
+// the dy operand (32 neurons x 16 tokens) out of dy rows, so each lane ends
+// up with 4 consecutive input features of one token (8-byte stores).
+//
+// Block: 8 waves (2 x 4), tile BM = 256 or 128 tokens x 256 input features,
+// the four 64-feature sub-tiles each inside one input chunk (BK % 64 == 0).
+// Reduction over N in stages of 64 neurons, NSTG LDS buffers filled by direct
+// loads NSTG-1 stages ahead: the dy tile [256 tokens][64 neurons] and, per sub-tile, the 64
+// W_c rows of the stage, each at the chunk its group maps that input chunk to
+// (a per (group, sub-tile) table in LDS holds the offset and the sign).  The
+// sign goes onto the weight operand as it leaves LDS.
+
+// XOR key (on 16-byte pieces, even values only) of W_c row r in a stage tile:
+// with it the 8-byte transposed reads of one 32-lane pass (rows r0..r0+3 and
+// r0+8..r0+11, 32 bytes each) land on distinct banks.
+__device__ __forceinline__ int dx_tkey(int r) {
+    return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
+
+template <int BM, int BNB, int WM, int WN, int NSTG>
+__global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __restrict__ dy,
+                                                              const uint16_t* __restrict__ w,
+                                                              const int32_t* __restrict__ hash,
+                                                              const int8_t* __restrict__ sign,
+                                                              uint16_t* __restrict__ dx, int M, int K, int N, int J,
+                                                              int Jc, int BK, int BN, int n_mt) {
+    constexpr int NWV = WM * WN;
+    constexpr int TMW = BM / WM, TNW = BNB / WN;  // wave tile: tokens x input features
+    constexpr int FM = TMW / 16, FN = TNW / 16;
+    static_assert(TNW == 64, "one 64-feature sub-tile per wave column");
+    constexpr int KS = 64, RB = 128, RPI = 8;     // stage of 64 neurons, 128-byte rows
+    constexpr int NSUB = BNB / 64;                // 64-feature sub-tiles
+    constexpr int XI = BM / RPI / NWV;            // dy loads per wave per stage
+    constexpr int WI = NSUB * (KS / RPI) / NWV;   // W_c loads per wave per stage
+    constexpr int DPW = XI + WI;
+    static_assert(XI * RPI * NWV == BM && WI * NWV == NSUB * (KS / RPI), "loads must split over the waves");
+    static_assert((NWV * RPI) % 16 == 0, "the dy swizzle key must repeat between a wave's loads");
+    constexpr int SX = BM * RB, SB = SX + NSUB * KS * RB;
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t fold_smem[];
+    const int G = N / BN;
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(fold_smem + NSTG * SB);
+    uint32_t* s_sgn = s_off + G * NSUB;
+
+    constexpr int GM = 4;
+    const int n_nt = K / BNB;
+    const int tile = xcd_tile(blockIdx.x, n_mt * n_nt);
+    const int strip = tile / (GM * n_nt);
+    const int gm = min(GM, n_mt - strip * GM);
+    const int rem = tile - strip * GM * n_nt;
+    const int mt = strip * GM + rem % gm;
+    const int nt = rem / gm;
+    const int m0 = mt * BM;
+    const int k0 = nt * BNB;
+    const int Kc = Jc * BK;
+
+    // table: per group g and sub-tile jj, byte offset of the source columns in
+    // a W_c row (or past the buffer for an absent source) and the sign mask
+    for (int e = threadIdx.x; e < G * NSUB; e += blockDim.x) {
+        const int g = e / NSUB;
+        const int kf = k0 + (e - g * NSUB) * 64;
+        const int j = kf / BK;
+        const int t = hash[static_cast<size_t>(g) * J + j];
+        const int sg = sign[static_cast<size_t>(g) * J + j];
+        const bool ok = t >= 0 && t < Jc && (sg == 1 || sg == -1);
+        s_off[e] = ok ? static_cast<uint32_t>(t * BK + (kf - j * BK)) * 2u : kFoldAbsent;
+        s_sgn[e] = (ok && sg < 0) ? 0x80008000u : 0u;
+    }
+    __syncthreads();
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nstage = N / KS;
+
+    // dy loads: as the x loads of the forward
+    const i32x4 dr = fold_rsrc(dy + static_cast<size_t>(m0) * N,
+                               static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * N * 2));
+    const int lrow = lane / 8;
+    const int dpiece = (lane % 8) ^ fold_key<RB>(wave * RPI + lrow);
+    const uint32_t dy_voff = static_cast<uint32_t>(lrow * N + dpiece * 8) * 2u;
+    // W_c loads: load i = wave + NWV*ii fills rows (i % 8)*8 .. +7 of sub-tile i / 8
+    const i32x4 wr = fold_rsrc(w, static_cast<uint32_t>(static_cast<size_t>(N) * Kc * 2));
+    int w_row[WI], w_sub[WI];
+    uint32_t w_base[WI];
+#pragma unroll
+    for (int ii = 0; ii < WI; ++ii) {
+        const int i = wave + NWV * ii;
+        w_sub[ii] = i / (KS / RPI);
+        w_row[ii] = (i % (KS / RPI)) * RPI + lrow;  // row inside the stage
+        const int piece = (lane % 8) ^ dx_tkey(w_row[ii]);
+        w_base[ii] = static_cast<uint32_t>(w_row[ii] * Kc + piece * 8) * 2u;
+    }
+    const uint32_t lds0 = lds_address(fold_smem);
+    auto dma = [&](int s, int buf) {
+        const int n0 = s * KS;
+        const uint32_t base = lds0 + static_cast<uint32_t>(buf * SB);
+        uint32_t voff[WI];
+#pragma unroll
+        for (int ii = 0; ii < WI; ++ii)
+            voff[ii] = w_base[ii] + static_cast<uint32_t>(n0) * static_cast<uint32_t>(Kc) * 2u +
+                       s_off[((n0 + w_row[ii]) / BN) * NSUB + w_sub[ii]];
+#pragma unroll
+        for (int ii = 0; ii < XI; ++ii) {
+            const int row0 = (wave + NWV * ii) * RPI;
+            lds_dma16(dr, base + row0 * RB, dy_voff, static_cast<uint32_t>((row0 * N + n0) * 2));
+        }
+#pragma unroll
+        for (int ii = 0; ii < WI; ++ii) {
+            const int i = wave + NWV * ii;
+            lds_dma16(wr, base + SX + w_sub[ii] * (KS * RB) + (i % (KS / RPI)) * RPI * RB, voff[ii], 0u);
+        }
+    };
+
+    const int fr = lane & 15;
+    const int q = lane >> 4;
+    const int key = fold_key<RB>(fr);
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    struct Ops {
+        bf16x8 w[FN], d[FM];
+    };
+    // transposed weight operand of feature block nb: lane l gets W[rows
+    // half*32 + 8q + e][feature nb*16 + l%16]; addressing lane s of a 16-lane
+    // group reads row half*32 + 8q + s/4 (+4) at features nb*16 + 4*(s%4)
+    const int tr_s = lane & 15;
+    auto read_ops = [&](int s, int buf, int half, Ops& o) {
+        const int n0 = s * KS;
+        const uint32_t sx = s_sgn[((n0 + half * 32 + 8 * q) / BN) * NSUB + wn];
+        const uint8_t* D = fold_smem + buf * SB + (wm * TMW + fr) * RB + ((half * 4 + q) ^ key) * 16;
+        const uint8_t* W = fold_smem + buf * SB + SX + wn * (KS * RB);
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int byte = i * 32 + 8 * (tr_s & 3);  // within the 128-byte row
+            const int r_lo = half * 32 + 8 * q + (tr_s >> 2);
+            const int r_hi = r_lo + 4;
+            const uint8_t* plo = W + r_lo * RB + ((((byte >> 4) ^ dx_tkey(r_lo)) << 4) | (byte & 8));
+            const uint8_t* phi = W + r_hi * RB + ((((byte >> 4) ^ dx_tkey(r_hi)) << 4) | (byte & 8));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(phi));
+            uint4 v;
+            v.x = (static_cast<uint32_t>(static_cast<uint16_t>(lo[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16)) ^ sx;
+            v.y = (static_cast<uint32_t>(static_cast<uint16_t>(lo[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16)) ^ sx;
+            v.z = (static_cast<uint32_t>(static_cast<uint16_t>(hi[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16)) ^ sx;
+            v.w = (static_cast<uint32_t>(static_cast<uint16_t>(hi[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16)) ^ sx;
+            o.w[i] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj) o.d[jj] = *reinterpret_cast<const bf16x8*>(D + jj * 16 * RB);
+    };
+    auto mma = [&](const Ops& o) {
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FM; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.w[i], o.d[jj], acc[i][jj], 0, 0, 0);
+    };
+    auto wait_stage = [&](int ahead) {
+        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
+        else if (ahead == 1) fold_stage_barrier<DPW>();
+        else fold_stage_barrier<0>();
+    };
+
+#pragma unroll
+    for (int p = 0; p < NSTG - 1; ++p)
+        if (p < nstage) dma(p, p);
+    auto step = [&](int s, int buf) {
+        wait_stage(min(NSTG - 2, nstage - 1 - s));
+        if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        Ops o0, o1;
+        read_ops(s, buf, 0, o0);
+        read_ops(s, buf, 1, o1);
+        mma(o0);
+        mma(o1);
+    };
+    for (int s0 = 0; s0 < nstage; s0 += NSTG) {
+#pragma unroll
+        for (int b = 0; b < NSTG; ++b)
+            if (s0 + b < nstage) step(s0 + b, b);
+    }
+
+    // epilogue: lane holds features wn*64 + nb*16 + 4q + i of token
+    // wm*TMW + mb*16 + lane%16
+#pragma unroll
+    for (int mb = 0; mb < FM; ++mb) {
+        const int m = m0 + wm * TMW + mb * 16 + fr;
+        if (m >= M) continue;
+        uint16_t* dr_ = dx + static_cast<size_t>(m) * K + k0 + wn * TNW + 4 * q;
+#pragma unroll
+        for (int nb = 0; nb < FN; ++nb) {
+            uint2 o;
+            o.x = pack_bf16(acc[nb][mb][0], acc[nb][mb][1]);
+            o.y = pack_bf16(acc[nb][mb][2], acc[nb][mb][3]);
+            *reinterpret_cast<uint2*>(dr_ + nb * 16) = o;
+        }
+    }
+}
+
 struct FoldCfg {
     int BM, BNB, KS, NSTG;
     size_t lds;
@@ -422,6 +632,51 @@ ss1_status launch_fold_t(const ForwardArgs& a) {
     return SS1_ERR_ALGO;
 }
 
+// dx kernel: tiles of BM = 256 tokens (two LDS stages) or 128 (three stages,
+// when 256-token tiles would leave most compute units idle) x 256 input
+// features; N a multiple of the 64-neuron stage, K of 256, BK of 64, and the
+// plan table plus the stages in LDS; 32-bit buffer offsets need the dy rows of
+// a tile and W_c under 2 GiB.
+int dxfold_bm(int64_t M, const Dims& d) {
+    const double cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
+    auto eff = [&](int bm) {
+        const double tiles = std::ceil(static_cast<double>(M) / bm) * static_cast<double>(d.K / 256);
+        return tiles / (std::ceil(tiles / cus) * cus);
+    };
+    // 64 x 64 wave tiles do about 10% less per cycle than 128 x 64 ones
+    return 0.9 * eff(128) > eff(256) ? 128 : 256;
+}
+
+size_t dxfold_lds(int BM, const Dims& d) {
+    const int nstg = BM == 128 ? 3 : 2;
+    return static_cast<size_t>(nstg) * (BM + 4 * 64) * 128 + static_cast<size_t>(d.G) * 4 * 8;
+}
+
+bool dxfold_ok(int64_t M, const Dims& d) {
+    if (M <= 0 || d.N % 64 != 0 || d.K % 256 != 0 || d.BK % 64 != 0) return false;
+    if (static_cast<double>(d.N) * d.Kc * 2.0 >= 2147483648.0) return false;
+    if (256.0 * static_cast<double>(d.N) * 2.0 >= 2147483648.0) return false;
+    return dxfold_lds(dxfold_bm(M, d), d) <= static_cast<size_t>(max_lds_per_block());
+}
+
+template <int BM, int NSTG>
+ss1_status launch_dx_fold_cfg(const void* dy, const void* W_c, const int32_t* hash, const int8_t* sign, void* dx,
+                              int64_t M, const Dims& d, void* stream) {
+    const int n_mt = static_cast<int>((M + BM - 1) / BM);
+    const long long blocks = static_cast<long long>(n_mt) * (d.K / 256);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    const size_t lds = dxfold_lds(BM, d);
+    auto kern = &dxfold_kernel<BM, 256, 2, 4, NSTG>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((dxfold_kernel<BM, 256, 2, 4, NSTG>), dim3(static_cast<unsigned>(blocks)), dim3(512), lds,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(dy),
+                       static_cast<const uint16_t*>(W_c), hash, sign, static_cast<uint16_t*>(dx), (int)M, (int)d.K,
+                       (int)d.N, (int)d.J, (int)d.Jc, d.BK, d.BN, n_mt);
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
 }  // namespace
 
 bool fold_supported(const ForwardArgs& a) {
@@ -431,6 +686,15 @@ bool fold_supported(const ForwardArgs& a) {
 // Run time model fitted to MI355X measurements of the 256 x 256 tile: per
 // round of tiles (one tile per compute unit) 26.1 ns per input element of K
 // plus 6.2 us; the 4-wave tiles run about 1.3x slower per unit of area.
+bool dx_fold_supported(int64_t M, const Dims& d) { return dxfold_ok(M, d); }
+
+ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, const int8_t* sign, void* dx,
+                          int64_t M, const Dims& d, void* stream) {
+    if (!dxfold_ok(M, d)) return SS1_ERR_ALGO;
+    if (dxfold_bm(M, d) == 128) return launch_dx_fold_cfg<128, 3>(dy, W_c, hash, sign, dx, M, d, stream);
+    return launch_dx_fold_cfg<256, 2>(dy, W_c, hash, sign, dx, M, d, stream);
+}
+
 double fold_estimate_us(const ForwardArgs& a) {
     const FoldCfg cfg = fold_config(a);
     if (a.dtype != SS1_BF16 || cfg.BM == 0 || a.M <= 0) return 1e300;

@@ -52,6 +52,11 @@ bool band_supported(const ForwardArgs& a, int min_rows);
 bool fold_supported(const ForwardArgs& a);
 // Estimated fold-kernel time in microseconds (huge when it cannot run).
 double fold_estimate_us(const ForwardArgs& a);
+// Backward dx as the fold contraction (ss1_fold.hip): bf16, hash plan,
+// N % 64 == 0, K % 256 == 0, BK % 64 == 0 and the plan table in LDS.
+bool dx_fold_supported(int64_t M, const Dims& d);
+ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, const int8_t* sign, void* dx,
+                          int64_t M, const Dims& d, void* stream);
 
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);

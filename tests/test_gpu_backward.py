@@ -70,7 +70,9 @@ SHAPES = [  # M, K, N, c, BK, BN
     (300, 768, 192, 2, 64, 64), (100, 512, 128, 1, 64, 32), (257, 1024, 256, 4, 32, 128),
     (64, 576, 96, 3, 64, 32), (130, 2048, 64, 8, 64, 64),
     (200, 4096, 128, 2, 64, 64), (72, 3072, 64, 3, 64, 32),   # Kc >= 1024 (wide dW tiles)
-    (50, 1280, 128, 1, 160, 32), (40, 384, 96, 2, 96, 32)]    # chunks that straddle 128-column dx tiles
+    (50, 1280, 128, 1, 160, 32), (40, 384, 96, 2, 96, 32),    # chunks that straddle 128-column dx tiles
+    (150, 1024, 256, 2, 128, 64), (90, 512, 256, 2, 64, 128),  # dx fold: 64-feature tiles inside 128-wide chunks; BN = 128
+    (4096, 4096, 128, 2, 64, 64)]   # dx fold with 256-token tiles
 
 
 @pytest.mark.parametrize("M,K,N,c,BK,BN", SHAPES)
