@@ -3,7 +3,11 @@
 //   dW_c[g-block] = dy[:, g-block]^T z_g                    (dw_kernel)
 //   dx[:, j-chunk] = sum_g sign[g][j] (dy[:, g-block] W_c[g-block])[:, hash[g][j]-chunk]
 //                  = dy times the dense expansion of W_c          (dx_kernel)
-// Both run on 16x16x32 bf16 MFMA with float32 accumulation.  The operands
+// Both run on 16x16x32 bf16 MFMA with float32 accumulation.  Where their
+// shape conditions hold, both go to the fold kernels of ss1_fold.hip instead
+// (no sketch formed; dense MFMA work): dW_c when BN % 64 == 0, BK % 64 == 0,
+// c in {1, 2, 4} and Kc % 128 == 0; dx when N % 64 == 0, K % 256 == 0 and
+// BK % 64 == 0.  The operands
 // whose stored rows run along the reduction dimension are written to LDS as
 // stored (16-byte stores) and read back transposed with ds_read_b64_tr_b16.
 //
@@ -439,7 +443,10 @@ ss1_status launch_dw_cfg(const void* x, const void* dy, const int32_t* hash, con
 
 ss1_status launch_backward(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign, const void* dy,
                            void* dx, void* dW, int64_t M, const Dims& d, void* stream) {
-    if (dW) {
+    if (dW && dw_fold_supported(M, d)) {
+        const ss1_status st = launch_dw_fold(x, dy, hash, sign, dW, M, d, stream);
+        if (st != SS1_OK) return st;
+    } else if (dW) {
         ss1_status st;
         switch (d.c) {
             case 1: st = launch_dw_cfg<1>(x, dy, hash, sign, dW, M, d, stream); break;

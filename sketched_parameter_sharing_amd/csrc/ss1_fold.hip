@@ -541,6 +541,243 @@ __global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __
     }
 }
 
+// =============================================================== dW kernel
+// dW_c[n][t*BK + u] = sum_m dy[m][n] z_g[m][t*BK + u] with z_g the sketch of x
+// = sum over tokens m and the c sources j_r of chunk t of
+//   sign_g(j_r) x[m][j_r*BK + u] dy[m][n]:
+// a contraction over (m, r) with no sketch formed (the fold of the forward,
+// applied on the reduction side).  The kernel computes the transposed tile
+// dW_c^T[kc][n] = sum x-chunk^T dy; both operands come out of row-major
+// [token][...] LDS tiles through ds_read_b64_tr_b16, and each lane ends with
+// 4 consecutive compressed columns of one neuron (8-byte stores).
+//
+// Block: 8 waves, tile KT compressed columns x 64 neurons inside one group.
+// Waves 0-3 and 4-7 cover the tile the same way (4 x 64 columns x 64 neurons
+// for KT = 256, 2 x 2 of 64 x 32 for KT = 128) and split each 64-token stage
+// into its two 32-token halves; their partial sums meet in LDS at the end.
+// Per stage, direct loads bring the dy tile [64 tokens][64 neurons] and, per
+// 64-column sub-tile st and source r, the x tile [64 tokens][64 columns] at
+// source chunk j_r of that sub-tile's compressed chunk (a table in LDS from
+// the block's group plan; a missing source points past x and loads zeros).
+// The source's sign goes onto the x operand as it leaves LDS.
+template <int KT, int CS, int NSTG>
+__global__ __launch_bounds__(512) void dwfold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
+                                                     const int32_t* __restrict__ hash,
+                                                     const int8_t* __restrict__ sign, uint16_t* __restrict__ dw,
+                                                     int M, int K, int N, int J, int Jc, int BK, int BN) {
+    constexpr int NWV = 8;
+    constexpr int NSUB = KT / 64;                 // 64-column sub-tiles
+    constexpr int WM = NSUB, WN = 4 / WM;         // waves of a half: along columns x neurons
+    static_assert(WM * WN == 4, "four waves per half");
+    constexpr int TNW = 64 / WN;                  // neurons per wave
+    constexpr int FA = 4, FB = TNW / 16;          // 16-blocks: columns (64 per wave) x neurons
+    constexpr int KS = 64, RB = 128, RPI = 8;     // stage of 64 tokens, 128-byte tile rows
+    constexpr int NT = NSUB * CS + 1;             // tiles per stage: x sub-tiles, then dy
+    constexpr int LOADS = NT * (KS / RPI);        // wave-wide loads per stage
+    static_assert(LOADS % NWV == 0, "loads must split over the waves");
+    constexpr int DPW = LOADS / NWV;
+    constexpr int TB = KS * RB;                   // bytes per tile
+    constexpr int SB = NT * TB;                   // bytes per stage
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t fold_smem[];
+    uint32_t* s_xoff = reinterpret_cast<uint32_t*>(fold_smem + NSTG * SB);  // [NSUB][CS]
+    uint32_t* s_xsg = s_xoff + NSUB * CS;
+    int* s_cnt = reinterpret_cast<int*>(s_xsg + NSUB * CS);
+    int* s_j = s_cnt + NSUB;                                                // [NSUB][CS]
+
+    const int Kc = Jc * BK;
+    const int n_ct = Kc / KT;
+    const int nt = blockIdx.x / n_ct;             // 64-neuron tile
+    const int kc0 = (blockIdx.x - nt * n_ct) * KT;
+    const int n0 = nt * 64;
+    const int g = n0 / BN;
+
+    // sources of each sub-tile's compressed chunk, ascending in j
+    const int tid = threadIdx.x;
+    for (int e = tid; e < NSUB * CS; e += blockDim.x) s_j[e] = -1;
+    for (int e = tid; e < NSUB; e += blockDim.x) s_cnt[e] = 0;
+    __syncthreads();
+    for (int j = tid; j < J; j += blockDim.x) {
+        const int t = hash[static_cast<size_t>(g) * J + j];
+        const int sg = sign[static_cast<size_t>(g) * J + j];
+        if (t < 0 || t >= Jc || (sg != 1 && sg != -1)) continue;
+#pragma unroll
+        for (int st = 0; st < NSUB; ++st) {
+            if ((kc0 + 64 * st) / BK != t) continue;
+            const int slot = atomicAdd(&s_cnt[st], 1);
+            if (slot < CS) s_j[st * CS + slot] = sg < 0 ? -(j + 2) : j;  // sign folded into the code
+        }
+    }
+    __syncthreads();
+    if (tid < NSUB) {
+        int* p = s_j + tid * CS;
+        for (int a = 1; a < CS; ++a) {  // insertion sort by chunk; missing sources (-1) go last
+            const int v = p[a];
+            const int kv = v == -1 ? 0x7FFFFFFF : (v < 0 ? -v - 2 : v);
+            int b = a - 1;
+            while (b >= 0) {
+                const int kb = p[b] == -1 ? 0x7FFFFFFF : (p[b] < 0 ? -p[b] - 2 : p[b]);
+                if (kb <= kv) break;
+                p[b + 1] = p[b];
+                --b;
+            }
+            p[b + 1] = v;
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < NSUB * CS; e += blockDim.x) {
+        const int v = s_j[e];
+        const int st = e / CS;
+        const int u0 = (kc0 + 64 * st) % BK;
+        if (v == -1) {
+            s_xoff[e] = kFoldAbsent;
+            s_xsg[e] = 0u;
+        } else {
+            const int j = v < 0 ? -v - 2 : v;
+            s_xoff[e] = static_cast<uint32_t>(j * BK + u0) * 2u;
+            s_xsg[e] = v < 0 ? 0x80008000u : 0u;
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave / 4;                    // which 32 tokens of a stage
+    const int wl = wave % 4;
+    const int wm = wl / WN, wn = wl % WN;
+    const int nstage = (M + KS - 1) / KS;
+
+    // Loads: load i = wave + NWV*ii fills rows (i % 8)*8 .. +7 of tile i / 8
+    // (tiles 0 .. NSUB*CS-1: x sub-tile st = tile / CS, source r = tile % CS;
+    // tile NSUB*CS: dy).  Tokens past M lie past both buffers and load zeros.
+    const i32x4 xr = fold_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(M) * K * 2));
+    const i32x4 dr = fold_rsrc(dy, static_cast<uint32_t>(static_cast<size_t>(M) * N * 2));
+    const int lrow = lane / 8;
+    int l_tile[DPW];
+    uint32_t l_voff[DPW];
+#pragma unroll
+    for (int ii = 0; ii < DPW; ++ii) {
+        const int i = wave + NWV * ii;
+        const int row = (i % (KS / RPI)) * RPI + lrow;
+        const int piece = (lane % 8) ^ dx_tkey(row);
+        l_tile[ii] = i / (KS / RPI);
+        l_voff[ii] = l_tile[ii] < NSUB * CS ? static_cast<uint32_t>(row * K + piece * 8) * 2u
+                                            : static_cast<uint32_t>(row * N + n0 + piece * 8) * 2u;
+    }
+    const uint32_t lds0 = lds_address(fold_smem);
+    auto dma = [&](int s, int buf) {
+        const int m0 = s * KS;
+        const uint32_t base = lds0 + static_cast<uint32_t>(buf * SB);
+#pragma unroll
+        for (int ii = 0; ii < DPW; ++ii) {
+            const int i = wave + NWV * ii;
+            const uint32_t dst = base + static_cast<uint32_t>(l_tile[ii] * TB + (i % (KS / RPI)) * RPI * RB);
+            if (l_tile[ii] < NSUB * CS)
+                lds_dma16(xr, dst, l_voff[ii] + s_xoff[l_tile[ii]], static_cast<uint32_t>(m0) * K * 2u);
+            else
+                lds_dma16(dr, dst, l_voff[ii], static_cast<uint32_t>(m0) * N * 2u);
+        }
+    };
+
+    const int q = lane >> 4;
+    const int tr_s = lane & 15;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    // transposed operand of a 16-wide block at byte `col` of a tile's rows:
+    // lane l gets rows 32*half + 8q + e (e = 0..7) of column (col/2 + l%16)
+    auto read_tr = [&](const uint8_t* T, int col, uint32_t sx) {
+        const int byte = col + 8 * (tr_s & 3);
+        const int r_lo = half * 32 + 8 * q + (tr_s >> 2);
+        const int r_hi = r_lo + 4;
+        const uint8_t* plo = T + r_lo * RB + ((((byte >> 4) ^ dx_tkey(r_lo)) << 4) | (byte & 8));
+        const uint8_t* phi = T + r_hi * RB + ((((byte >> 4) ^ dx_tkey(r_hi)) << 4) | (byte & 8));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(plo));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(phi));
+        uint4 v;
+        v.x = (static_cast<uint32_t>(static_cast<uint16_t>(lo[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[1])) << 16)) ^ sx;
+        v.y = (static_cast<uint32_t>(static_cast<uint16_t>(lo[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(lo[3])) << 16)) ^ sx;
+        v.z = (static_cast<uint32_t>(static_cast<uint16_t>(hi[0])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[1])) << 16)) ^ sx;
+        v.w = (static_cast<uint32_t>(static_cast<uint16_t>(hi[2])) | (static_cast<uint32_t>(static_cast<uint16_t>(hi[3])) << 16)) ^ sx;
+        return __builtin_bit_cast(bf16x8, v);
+    };
+
+    f32x4 acc[FA][FB];
+#pragma unroll
+    for (int i = 0; i < FA; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](int buf) {
+        const uint8_t* S = fold_smem + buf * SB;
+        bf16x8 bo[FB];
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) bo[fb] = read_tr(S + NSUB * CS * TB, (wn * TNW + fb * 16) * 2, 0u);
+#pragma unroll
+        for (int r = 0; r < CS; ++r) {
+            const int tile = wm * CS + r;
+            const uint32_t sx = s_xsg[tile];
+            bf16x8 ao[FA];
+#pragma unroll
+            for (int fa = 0; fa < FA; ++fa) ao[fa] = read_tr(S + tile * TB, fa * 32, sx);
+#pragma unroll
+            for (int fa = 0; fa < FA; ++fa)
+#pragma unroll
+                for (int fb = 0; fb < FB; ++fb)
+                    acc[fa][fb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao[fa], bo[fb], acc[fa][fb], 0, 0, 0);
+        }
+    };
+    auto wait_stage = [&](int ahead) {
+        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
+        else if (ahead == 1) fold_stage_barrier<DPW>();
+        else fold_stage_barrier<0>();
+    };
+
+#pragma unroll
+    for (int p = 0; p < NSTG - 1; ++p)
+        if (p < nstage) dma(p, p);
+    auto step = [&](int s, int buf) {
+        wait_stage(min(NSTG - 2, nstage - 1 - s));
+        if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        compute(buf);
+    };
+    for (int s0 = 0; s0 < nstage; s0 += NSTG) {
+#pragma unroll
+        for (int b = 0; b < NSTG; ++b)
+            if (s0 + b < nstage) step(s0 + b, b);
+    }
+
+    // the two halves' partial tiles meet in LDS (the stage buffers are free
+    // once every wave has passed this barrier)
+    fold_stage_barrier<0>();
+    float* red = reinterpret_cast<float*>(fold_smem);
+    if (half == 1) {
+#pragma unroll
+        for (int fa = 0; fa < FA; ++fa)
+#pragma unroll
+            for (int fb = 0; fb < FB; ++fb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) red[((wl * FA + fa) * FB + fb) * 256 + i * 64 + lane] = acc[fa][fb][i];
+    }
+    __syncthreads();
+    if (half == 0) {
+        // lane holds columns wm*64 + fa*16 + 4q + i of neuron wn*TNW + fb*16 + lane%16
+#pragma unroll
+        for (int fb = 0; fb < FB; ++fb) {
+            const int n = n0 + wn * TNW + fb * 16 + tr_s;
+            uint16_t* dr_ = dw + static_cast<size_t>(n) * Kc + kc0 + wm * 64 + 4 * q;
+#pragma unroll
+            for (int fa = 0; fa < FA; ++fa) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = acc[fa][fb][i] + red[((wl * FA + fa) * FB + fb) * 256 + i * 64 + lane];
+                uint2 o;
+                o.x = pack_bf16(v[0], v[1]);
+                o.y = pack_bf16(v[2], v[3]);
+                *reinterpret_cast<uint2*>(dr_ + fa * 16) = o;
+            }
+        }
+    }
+}
+
 struct FoldCfg {
     int BM, BNB, KS, NSTG;
     size_t lds;
@@ -686,7 +923,76 @@ bool fold_supported(const ForwardArgs& a) {
 // Run time model fitted to MI355X measurements of the 256 x 256 tile: per
 // round of tiles (one tile per compute unit) 26.1 ns per input element of K
 // plus 6.2 us; the 4-wave tiles run about 1.3x slower per unit of area.
+// dW kernel: KT = 256 compressed columns when Kc allows and the c sources fit
+// (4*c sub-tiles of 8 KB per stage), else 128; c in {1, 2, 4}; BN % 64 == 0
+// (a 64-neuron tile inside one group), BK % 64 == 0; 32-bit buffer offsets
+// need x and dy under 2 GiB.
+struct DwCfg {
+    int KT, NSTG;
+    size_t lds;
+};
+
+DwCfg dwfold_config(int64_t M, const Dims& d) {
+    if (M <= 0 || d.BN % 64 != 0 || d.BK % 64 != 0) return DwCfg{0, 0, 0};
+    if (!(d.c == 1 || d.c == 2 || d.c == 4)) return DwCfg{0, 0, 0};
+    if (static_cast<double>(M) * std::max(d.K, d.N) * 2.0 >= 2147483648.0) return DwCfg{0, 0, 0};
+    int KT = 0;
+    if (d.Kc % 256 == 0 && 4 * d.c <= 8) KT = 256;
+    else if (d.Kc % 128 == 0 && 2 * d.c <= 8) KT = 128;
+    if (KT == 0) return DwCfg{0, 0, 0};
+    const size_t stage = static_cast<size_t>(KT / 64 * d.c + 1) * 64 * 128;
+    const size_t table = static_cast<size_t>(KT / 64) * (3 * d.c + 1) * 4;
+    const size_t cap = static_cast<size_t>(max_lds_per_block());
+    int nstg = 3;
+    while (nstg > 2 && nstg * stage + table > cap) --nstg;
+    // after the loop the stage buffers hold the second half's partial tiles:
+    // 4 waves x 16 blocks x 256 floats
+    const size_t lds = std::max(nstg * stage + table, static_cast<size_t>(4 * 16 * 256 * 4));
+    if (lds > cap) return DwCfg{0, 0, 0};
+    return DwCfg{KT, nstg, lds};
+}
+
+template <int KT, int CS, int NSTG>
+ss1_status launch_dw_fold_cfg(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
+                              int64_t M, const Dims& d, const DwCfg& cfg, void* stream) {
+    const long long blocks = static_cast<long long>(d.N / 64) * (d.Kc / KT);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    auto kern = &dwfold_kernel<KT, CS, NSTG>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(cfg.lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((dwfold_kernel<KT, CS, NSTG>), dim3(static_cast<unsigned>(blocks)), dim3(512), cfg.lds,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(dy), hash, sign, static_cast<uint16_t*>(dW), (int)M, (int)d.K,
+                       (int)d.N, (int)d.J, (int)d.Jc, d.BK, d.BN);
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
+template <int KT, int CS>
+ss1_status launch_dw_fold_k(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
+                            int64_t M, const Dims& d, const DwCfg& cfg, void* stream) {
+    if (cfg.NSTG == 3) return launch_dw_fold_cfg<KT, CS, 3>(x, dy, hash, sign, dW, M, d, cfg, stream);
+    return launch_dw_fold_cfg<KT, CS, 2>(x, dy, hash, sign, dW, M, d, cfg, stream);
+}
+
 bool dx_fold_supported(int64_t M, const Dims& d) { return dxfold_ok(M, d); }
+
+bool dw_fold_supported(int64_t M, const Dims& d) { return dwfold_config(M, d).KT > 0; }
+
+ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
+                          int64_t M, const Dims& d, void* stream) {
+    const DwCfg cfg = dwfold_config(M, d);
+    if (cfg.KT == 256) {
+        if (d.c == 1) return launch_dw_fold_k<256, 1>(x, dy, hash, sign, dW, M, d, cfg, stream);
+        if (d.c == 2) return launch_dw_fold_k<256, 2>(x, dy, hash, sign, dW, M, d, cfg, stream);
+    }
+    if (cfg.KT == 128) {
+        if (d.c == 1) return launch_dw_fold_k<128, 1>(x, dy, hash, sign, dW, M, d, cfg, stream);
+        if (d.c == 2) return launch_dw_fold_k<128, 2>(x, dy, hash, sign, dW, M, d, cfg, stream);
+        if (d.c == 4) return launch_dw_fold_k<128, 4>(x, dy, hash, sign, dW, M, d, cfg, stream);
+    }
+    return SS1_ERR_ALGO;
+}
 
 ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, const int8_t* sign, void* dx,
                           int64_t M, const Dims& d, void* stream) {

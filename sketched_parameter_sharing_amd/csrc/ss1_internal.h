@@ -57,6 +57,11 @@ double fold_estimate_us(const ForwardArgs& a);
 bool dx_fold_supported(int64_t M, const Dims& d);
 ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, const int8_t* sign, void* dx,
                           int64_t M, const Dims& d, void* stream);
+// Backward dW_c as the fold contraction over (token, source) (ss1_fold.hip):
+// bf16, hash plan, BN % 64 == 0, BK % 64 == 0, c in {1, 2, 4}, Kc % 128 == 0.
+bool dw_fold_supported(int64_t M, const Dims& d);
+ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
+                          int64_t M, const Dims& d, void* stream);
 
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);

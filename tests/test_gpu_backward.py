@@ -61,9 +61,22 @@ def run(seed, M, K, N, c, BK, BN, want_dx=True, want_dw=True, integer=False):
             host(dx) if dx is not None else None, host(dw) if dw is not None else None)
 
 
+def within_ulp(got, mirror):
+    return np.abs(got - mirror) <= 2.0 ** -7 * np.abs(mirror) + 1e-5 * np.max(np.abs(mirror))
+
+
 def check_close(got, ref, mirror):
+    """Normwise against the float64 oracle, then elementwise within one bf16
+    ulp of the mirror.  For dW_c the library runs either a sketch kernel (the
+    sketch rounded to bf16 first: mirror = backward_dw_mirror) or the fold
+    kernel (no sketch formed: mirror = the exact float64 result); each output
+    must sit within one ulp of one of the two."""
     assert np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30) <= 2e-2
-    assert np.all(np.abs(got - mirror) <= 2.0 ** -7 * np.abs(mirror) + 1e-5 * np.max(np.abs(mirror)))
+    mirrors = mirror if isinstance(mirror, (list, tuple)) else [mirror]
+    ok = np.zeros(got.shape, dtype=bool)
+    for mir in mirrors:
+        ok |= within_ulp(got, mir)
+    assert np.all(ok)
 
 
 SHAPES = [  # M, K, N, c, BK, BN
@@ -88,7 +101,7 @@ def test_backward_random(M, K, N, c, BK, BN):
     x, w, dy, h, s, dx, dw = run(0x4c00 + M, M, K, N, c, BK, BN)
     rdx, rdw = oracle.backward(x, w, dy, h, s, K, N, c, BK, BN)
     check_close(dx, rdx, rdx)
-    check_close(dw, rdw, oracle.backward_dw_mirror(x, dy, h, s, K, N, c, BK, BN))
+    check_close(dw, rdw, [oracle.backward_dw_mirror(x, dy, h, s, K, N, c, BK, BN), rdw])
 
 
 def test_backward_one_output_only_and_empty():
@@ -122,4 +135,4 @@ def test_backward_full_size_sampled():
     mir = oracle.backward_dw_mirror(x, dy[:, cols], hs, ss, K, Ns, c, BK, BN)
     z = oracle.sketch(x, hs, ss, K, Ns, c, BK, BN)
     ref = np.concatenate([dy[:, cols[i * BN:(i + 1) * BN]].T @ z[i] for i in range(len(groups))])
-    check_close(dw[cols], ref, mir)
+    check_close(dw[cols], ref, [mir, ref])
