@@ -74,8 +74,8 @@ def work(wl):
     }
 
 
-def roofline(wl, t):
-    """Roofline record of one launch lasting t seconds."""
+def roofline(wl, t, kernel=None):
+    """Roofline record of one launch lasting t seconds of `kernel`."""
     wk = work(wl)
     peak_f = PEAK_MFMA_BF16 if wl.dtype == "bf16" else PEAK_MFMA_F32
     t_f = wk["compressed_flops"] / peak_f
@@ -89,7 +89,7 @@ def roofline(wl, t):
     else:
         r = {"bound": "hbm", **hb, "other": {"bound": "mfma", **mf}}
     r["t_lower_us"] = max(t_f, t_b) * 1e6
-    traffic = recorded_traffic(wl.name)
+    traffic = recorded_traffic(wl.name, kernel)
     r["traffic"] = traffic
     r["traffic_unit"] = "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)"
     r["traffic_vs_algorithmic"] = (traffic / wk["bytes"]) if traffic else None
@@ -100,14 +100,24 @@ CSRC = os.path.join(ROOT, "sketched_parameter_sharing_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-# Device sources each traffic record depends on (the kernels it measures and
-# the headers they include).
-FORWARD_SOURCES = ("ss1_kernels.hip", "ss1_fold.hip", "ss1_device.h", "ss1_internal.h")
-PROJECT_SOURCES = ("ss1_project.hip", "ss1_device.h", "ss1_internal.h")
+# Device sources of each kernel family (its kernels and the headers they include).
+KERNEL_SOURCES = {
+    "band": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "fused": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "smallm": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "generic": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_internal.h"),
+    "project": ("ss1_project.hip", "ss1_device.h", "ss1_internal.h"),
+}
 
 
-def record_sources(name):
-    return PROJECT_SOURCES if name.startswith("project:") else FORWARD_SOURCES
+def kernel_family(kernel_name):
+    """Family of a kernel from its (demangled or short) name, e.g.
+    'void band_kernel<...>' -> 'band'."""
+    for fam in KERNEL_SOURCES:
+        if f"{fam}_kernel" in kernel_name:
+            return fam
+    return None
 
 
 def kernel_source_sha256(names=None):
@@ -122,18 +132,22 @@ def kernel_source_sha256(names=None):
     return h.hexdigest()
 
 
-def recorded_traffic(name):
+def recorded_traffic(name, kernel=None):
     """Calibrated HBM bytes per launch for record `name` (a workload, or
     "project:<workload>" / "fp8:<workload>") from the committed counter
-    record, or None when there is none or the sources of its kernels changed
-    since."""
+    record, or None when there is none, when it measured another kernel family
+    than `kernel`, or when the sources of its kernel changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     w = rec.get("workloads", {}).get(name)
-    if not w or w.get("sources_sha256") != kernel_source_sha256(record_sources(name)):
+    if not w or "sources" not in w:
+        return None
+    if kernel is not None and kernel_family(w.get("kernel", "")) != kernel:
+        return None
+    if w.get("sources_sha256") != kernel_source_sha256(w["sources"]):
         return None
     return w.get("hbm_bytes_per_launch")
 
@@ -542,8 +556,8 @@ def main():
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
                        "compressed_tflops": wk["compressed_flops"] / t / 1e12,
                        "x_l2_gb": wk["x_l2_bytes"] / 1e9},
-            "roofline": roofline(wl, t),
         }
+        rec["roofline"] = roofline(wl, t, rec["config"]["kernel"])
         if rec["config"]["kernel"] == "fold":
             # the fold kernel multiplies by the expanded weight: its matrix
             # cores execute the dense FLOP count, c times the algorithmic one

@@ -59,13 +59,14 @@ ss1_status check_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32
 }
 
 // Estimated time in microseconds of the sketch kernels (band or fused) on a
-// large-M bf16 call, fitted to MI355X measurements: the sketch VALU work,
-// about 0.16 ps per (group, token, input element) and 1.6x that with
-// 128-neuron groups, or the compressed MFMA work at 0.6 PFLOP/s if larger.
+// large-M bf16 call, fitted to MI355X measurements (inputs not in cache): the
+// sketch VALU work, about 0.17 ps per (group, token, input element) and 2x
+// that with 128-neuron groups, or the compressed MFMA work at 0.6 PFLOP/s if
+// larger.
 double sketch_estimate_us(const ForwardArgs& a) {
     const double M = static_cast<double>(a.M), K = static_cast<double>(a.d.K);
     const double G = static_cast<double>(a.d.G), N = static_cast<double>(a.d.N);
-    const double valu = G * M * K * 0.16e-6 * (a.d.BN >= 128 ? 1.6 : 1.0);
+    const double valu = G * M * K * 0.17e-6 * (a.d.BN >= 128 ? 2.0 : 1.0);
     const double mfma = 2.0 * M * N * static_cast<double>(a.d.Kc) / 0.6e9;
     return valu > mfma ? valu : mfma;
 }

@@ -151,7 +151,8 @@ template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
 __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                    const int32_t* __restrict__ pi, const int8_t* __restrict__ ps,
                                                    uint16_t* __restrict__ y, int M, int K, int N, int J, int Jc,
-                                                   int c, int BK, int BN, int n_mt, int act) {
+                                                   int c, int BK, int BN, int n_mt, int act, int n_base,
+                                                   int n_cols) {
     constexpr int NWV = WM * WN;                  // waves per block
     constexpr int TMW = BM / WM, TNW = BNB / WN;  // wave tile: tokens x neurons
     constexpr int FM = TMW / 16, FN = TNW / 16;   // 16x16 MFMA blocks per wave
@@ -176,8 +177,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     // that range tiles go in column-major strips of GM row tiles, so the
     // blocks running together on one XCD share a few x row tiles and a few
     // weight column tiles in its L2.
+    // (the launch covers neurons [n_base, n_base + n_cols))
     constexpr int GM = 4;
-    const int n_nt = N / BNB;
+    const int n_nt = n_cols / BNB;
     const int tile = xcd_tile(blockIdx.x, n_mt * n_nt);
     const int strip = tile / (GM * n_nt);
     const int gm = min(GM, n_mt - strip * GM);
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     const int mt = strip * GM + rem % gm;
     const int nt = rem / gm;
     const int m0 = mt * BM;
-    const int n0 = nt * BNB;
+    const int n0 = n_base + nt * BNB;
     const int ngr = BNB / BN;
     uint32_t* s_sgn = s_off + ngr * J;
     const int Kc = Jc * BK;
@@ -834,37 +836,67 @@ inline FoldCfg fold_config(const ForwardArgs& a) {
 }
 
 template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
-ss1_status launch_fold_cfg(const ForwardArgs& a, const FoldCfg& cfg) {
+ss1_status launch_fold_cfg(const ForwardArgs& a, size_t lds, int64_t n_base, int64_t n_cols) {
     const Dims& d = a.d;
     const int n_mt = static_cast<int>((a.M + BM - 1) / BM);
-    const long long blocks = static_cast<long long>(n_mt) * (d.N / BNB);
+    const long long blocks = static_cast<long long>(n_mt) * (n_cols / BNB);
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    if (blocks == 0) return SS1_OK;
     auto kern = &fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(cfg.lds)) != hipSuccess)
+                            static_cast<int>(lds)) != hipSuccess)
         return SS1_ERR_HIP;
     hipLaunchKernelGGL((fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(WM * WN * 64), cfg.lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       dim3(WM * WN * 64), lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
-                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, n_mt, a.act);
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, n_mt, a.act, (int)n_base,
+                       (int)n_cols);
     return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
 }
 
+// A 256 x 256 launch whose tiles end in a partial round splits its neurons: the
+// columns [0, main) in 256 x 256 tiles that fill whole rounds of compute units,
+// the rest in 128 x 256 tiles (8 waves of 64 x 64) in a second launch, whose
+// one round of half-size tiles takes about 0.55 of a full round.  Returns the
+// number of neurons of the first launch (N when there is no split).
+int64_t fold_main_cols(const ForwardArgs& a, const FoldCfg& cfg) {
+    const Dims& d = a.d;
+    if (!(cfg.BM == 256 && cfg.BNB == 256 && cfg.KS == 64)) return d.N;
+    if (fold_lds(128, 256, 64, 3, d) > static_cast<size_t>(max_lds_per_block())) return d.N;
+    const long long cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
+    const long long n_mt = (a.M + 255) / 256, n_nt = d.N / 256;
+    const long long tiles = n_mt * n_nt;
+    const long long full = tiles / cus;
+    if (full == 0 || tiles % cus == 0) return d.N;
+    const long long n_main = full * cus / n_mt;
+    if (n_main <= 0 || n_main >= n_nt) return d.N;
+    auto rounds = [&](long long t) { return static_cast<double>((t + cus - 1) / cus); };
+    const double single = rounds(tiles);
+    const double split = rounds(n_mt * n_main) + 0.55 * rounds(((a.M + 127) / 128) * (n_nt - n_main));
+    return split < 0.97 * single ? n_main * 256 : d.N;
+}
 
 template <bool FROM_HASH>
 ss1_status launch_fold_t(const ForwardArgs& a) {
     const FoldCfg cfg = fold_config(a);
+    const int64_t N = a.d.N;
     if (cfg.BM == 256 && cfg.BNB == 256) {
-        if (cfg.KS == 64 && cfg.NSTG == 2) return launch_fold_cfg<256, 256, 2, 4, 64, 2, FROM_HASH>(a, cfg);
-        if (cfg.KS == 32 && cfg.NSTG == 4) return launch_fold_cfg<256, 256, 2, 4, 32, 4, FROM_HASH>(a, cfg);
+        if (cfg.KS == 64 && cfg.NSTG == 2) {
+            const int64_t main = fold_main_cols(a, cfg);
+            ss1_status st = launch_fold_cfg<256, 256, 2, 4, 64, 2, FROM_HASH>(a, cfg.lds, 0, main);
+            if (st != SS1_OK || main == N) return st;
+            return launch_fold_cfg<128, 256, 2, 4, 64, 3, FROM_HASH>(a, fold_lds(128, 256, 64, 3, a.d), main,
+                                                                    N - main);
+        }
+        if (cfg.KS == 32 && cfg.NSTG == 4) return launch_fold_cfg<256, 256, 2, 4, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
     }
     if (cfg.BM == 256 && cfg.BNB == 128) {
-        if (cfg.KS == 64) return launch_fold_cfg<256, 128, 2, 2, 64, 3, FROM_HASH>(a, cfg);
-        return launch_fold_cfg<256, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg);
+        if (cfg.KS == 64) return launch_fold_cfg<256, 128, 2, 2, 64, 3, FROM_HASH>(a, cfg.lds, 0, N);
+        return launch_fold_cfg<256, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
     }
     if (cfg.BM == 128 && cfg.BNB == 128) {
-        if (cfg.KS == 64) return launch_fold_cfg<128, 128, 2, 2, 64, 4, FROM_HASH>(a, cfg);
-        return launch_fold_cfg<128, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg);
+        if (cfg.KS == 64) return launch_fold_cfg<128, 128, 2, 2, 64, 4, FROM_HASH>(a, cfg.lds, 0, N);
+        return launch_fold_cfg<128, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
     }
     return SS1_ERR_ALGO;
 }
@@ -920,9 +952,6 @@ bool fold_supported(const ForwardArgs& a) {
     return a.dtype == SS1_BF16 && fold_config(a).BM > 0;
 }
 
-// Run time model fitted to MI355X measurements of the 256 x 256 tile: per
-// round of tiles (one tile per compute unit) 26.1 ns per input element of K
-// plus 6.2 us; the 4-wave tiles run about 1.3x slower per unit of area.
 // dW kernel: KT = 256 compressed columns when Kc allows and the c sources fit
 // (4*c sub-tiles of 8 KB per stage), else 128; c in {1, 2, 4}; BN % 64 == 0
 // (a 64-neuron tile inside one group), BK % 64 == 0; 32-bit buffer offsets
@@ -1001,14 +1030,28 @@ ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, 
     return launch_dx_fold_cfg<256, 2>(dy, W_c, hash, sign, dx, M, d, stream);
 }
 
+// Run time model fitted to MI355X measurements of the 256 x 256 tile (inputs
+// not in cache): per round of tiles (one tile per compute unit) 31 ns per
+// input element of K plus 10 us; the 4-wave tiles run about 1.3x slower per
+// unit of area, and a round of the 128 x 256 tiles of a split launch takes
+// 0.55 of a full one.
 double fold_estimate_us(const ForwardArgs& a) {
     const FoldCfg cfg = fold_config(a);
     if (a.dtype != SS1_BF16 || cfg.BM == 0 || a.M <= 0) return 1e300;
     const double cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
-    const double tiles = std::ceil(static_cast<double>(a.M) / cfg.BM) * static_cast<double>(a.d.N / cfg.BNB);
+    const double per_round = 0.031 * static_cast<double>(a.d.K) + 10.0;
+    const int64_t main = fold_main_cols(a, cfg);
+    const double n_mt = std::ceil(static_cast<double>(a.M) / cfg.BM);
+    if (main != a.d.N) {
+        const double t_main = std::ceil(n_mt * static_cast<double>(main / 256) / cus);
+        const double t_rest = std::ceil(std::ceil(static_cast<double>(a.M) / 128) *
+                                        static_cast<double>((a.d.N - main) / 256) / cus);
+        return (t_main + 0.55 * t_rest) * per_round;
+    }
+    const double tiles = n_mt * static_cast<double>(a.d.N / cfg.BNB);
     const double rounds = std::ceil(tiles / cus);
     const double area = static_cast<double>(cfg.BM) * cfg.BNB / 65536.0;
-    return rounds * (0.0261 * static_cast<double>(a.d.K) + 6.2) * area * (area < 1.0 ? 1.3 : 1.0);
+    return rounds * per_round * area * (area < 1.0 ? 1.3 : 1.0);
 }
 
 ss1_status launch_fold(const ForwardArgs& a) {

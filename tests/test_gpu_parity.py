@@ -282,6 +282,20 @@ def test_fold_tile_shapes(name, M):
     print(f"{name} M={M} fold err={check_bf16(wl, inp, y, kernel='fold'):.3e}", flush=True)
 
 
+def test_fold_split_launch():
+    # 16 x 20 tiles of 256 x 256 end in a partial round: the first 4096
+    # neurons run as 256 x 256 tiles, the last 1024 as 128 x 256 tiles
+    wl = Workload("split", 9, 3, 4096, 256, 5120, 2, 64, 64, "bf16")
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    check_bf16(wl, inp, y, kernel="fold")
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
+
+
 def test_fold_neuron_tile_of_128():
     # N = 384 is not a multiple of 256: 256 x 128 tiles of 4 waves
     wl = Workload("n384", 9, 1, 300, 512, 384, 2, 64, 64, "bf16")
