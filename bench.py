@@ -454,6 +454,17 @@ def cpu_baseline_mlp(c, budget_s=10.0, m=MLP_SHAPE):
                       f"{t:.3f} s (dense-equivalent FLOPs of the sample / time)"}
 
 
+def fp8_kernel_name(wl):
+    """The kernel ss1_forward_fp8w runs: small-M for M <= 16, else the fold
+    kernel where the bf16 forward would pick it (the same time models; fp8
+    weights need BK % 64 == 0 there), else the fused kernel."""
+    if wl.M <= 16:
+        return "smallm"
+    if wl.BK % 64 == 0 and kernel_name(wl, "auto") == "fold":
+        return "fold"
+    return "fused"
+
+
 def kernel_name(wl, algo):
     """The kernel a call runs: the requested one, or what the library picks."""
     if algo != "auto":
@@ -716,7 +727,7 @@ def main():
             "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) compressed weights quantized per row, "
                     "seeded balanced plan)",
             "config": {"workload": name + "_fp8w", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c, "BK": wl.BK,
-                       "BN": wl.BN, "kernel": "smallm" if wl.M <= 16 else "fused",
+                       "BN": wl.BN, "kernel": fp8_kernel_name(wl),
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
                        "bf16_weights_ms": t16 * 1e3, "speedup_vs_bf16_weights": t16 / t},
             "roofline": roof,

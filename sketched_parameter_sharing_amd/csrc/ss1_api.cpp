@@ -311,7 +311,10 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     const bool small = ss1::smallm_supported(a);
     if (!small && !ss1::fused_supported(a)) return SS1_ERR_SHAPE;
     if (a.M == 0) return SS1_OK;
-    return small ? ss1::launch_smallm(a) : ss1::launch_fused(a);
+    if (small) return ss1::launch_smallm(a);
+    // large M: the fold kernel where the time models put it clearly ahead
+    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return ss1::launch_fold(a);
+    return ss1::launch_fused(a);
 }
 
 extern "C" ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash,

@@ -63,13 +63,14 @@ __device__ __forceinline__ int fold_key(int p) {
 }
 
 // Plan of the block's groups in LDS, per (group gl of the tile, input chunk j):
-// s_off = byte offset inside a W_c row of the chunk j maps to (t*BK*2), or
+// s_off = byte offset inside a W_c row of the chunk j maps to (t*BK*WB, WB
+// bytes per stored weight), or
 // kFoldAbsent for an absent source; s_sgn = 0x80008000 for a negative sign,
 // else 0.  Hash form: pi/ps are hash/sign [G][J]; index form: idx/isign
 // [G][Jc][c].  Entries out of range leave the source absent.
 constexpr uint32_t kFoldAbsent = 0x7FFFFFFFu;  // plus any in-tile offset: past the extent
 
-template <bool FROM_HASH>
+template <bool FROM_HASH, int WB>
 __device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g0, int ngr,
                                 int J, int Jc, int c, int BK, uint32_t* s_off, uint32_t* s_sgn) {
     const int tid = threadIdx.x;
@@ -82,7 +83,7 @@ __device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __
             const int t = gi[e];
             const int s = gs[e];
             const bool ok = t >= 0 && t < Jc && (s == 1 || s == -1);
-            s_off[e] = ok ? static_cast<uint32_t>(t * BK) * 2u : kFoldAbsent;
+            s_off[e] = ok ? static_cast<uint32_t>(t * BK) * WB : kFoldAbsent;
             s_sgn[e] = (ok && s < 0) ? 0x80008000u : 0u;
         }
     } else {
@@ -100,7 +101,7 @@ __device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __
             const int j = gi[e];
             const int s = gs[e];
             if (j >= 0 && j < J && (s == 1 || s == -1)) {
-                s_off[gl * J + j] = static_cast<uint32_t>(t * BK) * 2u;
+                s_off[gl * J + j] = static_cast<uint32_t>(t * BK) * WB;
                 s_sgn[gl * J + j] = s < 0 ? 0x80008000u : 0u;
             }
         }
@@ -147,28 +148,33 @@ __device__ __forceinline__ void fold_stage_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
+template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool W8, bool FROM_HASH>
 __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                    const int32_t* __restrict__ pi, const int8_t* __restrict__ ps,
                                                    uint16_t* __restrict__ y, int M, int K, int N, int J, int Jc,
                                                    int c, int BK, int BN, int n_mt, int act, int n_base,
-                                                   int n_cols) {
+                                                   int n_cols, const float* __restrict__ wscale) {
     constexpr int NWV = WM * WN;                  // waves per block
     constexpr int TMW = BM / WM, TNW = BNB / WN;  // wave tile: tokens x neurons
     constexpr int FM = TMW / 16, FN = TNW / 16;   // 16x16 MFMA blocks per wave
     static_assert(FM * 16 == TMW && FN * 16 == TNW && FN % 2 == 0, "wave tile");
-    constexpr int RB = KS * 2;                    // bytes per tile row
+    constexpr int RB = KS * 2;                    // bytes per x tile row
     constexpr int CPR = RB / 16;                  // 16-byte pieces per row
     constexpr int RPI = 1024 / RB;                // rows filled by one wave-wide load
+    // weight tile rows: KS weights of WB bytes (bf16, or E4M3 codes with W8)
+    constexpr int WB = W8 ? 1 : 2;
+    constexpr int RBW = KS * WB, CPRW = RBW / 16, RPIW = 1024 / RBW;
     constexpr int XI = BM / RPI / NWV;            // x loads per wave per stage
-    constexpr int WI = BNB / RPI / NWV;           // weight loads per wave per stage
+    constexpr int WI = BNB / RPIW / NWV;          // weight loads per wave per stage
     constexpr int DPW = XI + WI;
-    static_assert(XI * RPI * NWV == BM && WI * RPI * NWV == BNB, "tile rows must split over the waves");
-    static_assert((NWV * RPI) % 16 == 0, "the swizzle key must repeat between a wave's loads");
+    static_assert(XI * RPI * NWV == BM && WI * RPIW * NWV == BNB, "tile rows must split over the waves");
+    static_assert((NWV * RPI) % 16 == 0 && (NWV * RPIW) % 16 == 0,
+                  "the swizzle key must repeat between a wave's loads");
+    static_assert(!W8 || KS == 64, "fp8 weights with 64-wide stages");
     static_assert(NSTG >= 2 && NSTG <= 4, "stage count");
     static_assert(KS == 32 || KS == 64, "a stage is one or two 32-wide halves");
     constexpr int HALVES = KS / 32;
-    constexpr int SX = BM * RB, SB = (BM + BNB) * RB;  // x tile bytes, stage bytes
+    constexpr int SX = BM * RB, SB = SX + BNB * RBW;   // x tile bytes, stage bytes
 
     extern __shared__ __attribute__((aligned(16))) uint8_t fold_smem[];
     uint32_t* s_off = reinterpret_cast<uint32_t*>(fold_smem + NSTG * SB);
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     const int ngr = BNB / BN;
     uint32_t* s_sgn = s_off + ngr * J;
     const int Kc = Jc * BK;
-    stage_fold_plan<FROM_HASH>(pi, ps, n0 / BN, ngr, J, Jc, c, BK, s_off, s_sgn);
+    stage_fold_plan<FROM_HASH, WB>(pi, ps, n0 / BN, ngr, J, Jc, c, BK, s_off, s_sgn);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -206,24 +212,27 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     // lane offset serves all of them.
     const i32x4 xr = fold_rsrc(x + static_cast<size_t>(m0) * K,
                                static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K * 2));
-    const i32x4 wr = fold_rsrc(w + static_cast<size_t>(n0) * Kc, static_cast<uint32_t>(static_cast<size_t>(BNB) * Kc * 2));
+    const i32x4 wr = fold_rsrc(reinterpret_cast<const uint8_t*>(w) + static_cast<size_t>(n0) * Kc * WB,
+                               static_cast<uint32_t>(static_cast<size_t>(BNB) * Kc * WB));
     const int lrow = lane / CPR;
     const int piece = (lane % CPR) ^ fold_key<RB>(wave * RPI + lrow);
     const uint32_t x_voff = static_cast<uint32_t>(lrow * K + piece * 8) * 2u;
     uint32_t w_voff[WI];
     int w_gl[WI];  // group (inside the tile) of this lane's weight row, per load
+    const int lroww = lane / CPRW;
+    const int piecew = (lane % CPRW) ^ fold_key<RBW>(wave * RPIW + lroww);
 #pragma unroll
     for (int ii = 0; ii < WI; ++ii) {
-        const int p = (wave + NWV * ii) * RPI + lrow;                 // LDS row in the weight tile
+        const int p = (wave + NWV * ii) * RPIW + lroww;               // LDS row in the weight tile
         const int n = (p / TNW) * TNW + fold_neuron<FN>(p % TNW);    // neuron inside the tile
-        w_voff[ii] = static_cast<uint32_t>(n * Kc + piece * 8) * 2u;
+        w_voff[ii] = static_cast<uint32_t>(n * Kc * WB + piecew * 16);
         w_gl[ii] = n / BN;
     }
     const uint32_t lds0 = lds_address(fold_smem);
     auto dma = [&](int s, int buf) {
         const int k0 = s * KS;
         const int j = k0 / BK;
-        const uint32_t u0b = static_cast<uint32_t>(k0 - j * BK) * 2u;
+        const uint32_t u0w = static_cast<uint32_t>(k0 - j * BK) * WB;  // bytes into the chunk
         const uint32_t base = lds0 + static_cast<uint32_t>(buf * SB);
         uint32_t off[WI];
 #pragma unroll
@@ -235,8 +244,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
         }
 #pragma unroll
         for (int ii = 0; ii < WI; ++ii) {
-            const int row0 = (wave + NWV * ii) * RPI;
-            lds_dma16(wr, base + SX + row0 * RB, w_voff[ii] + off[ii] + u0b, 0u);
+            const int row0 = (wave + NWV * ii) * RPIW;
+            lds_dma16(wr, base + SX + row0 * RBW, w_voff[ii] + off[ii] + u0w, 0u);
         }
     };
 
@@ -259,14 +268,29 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     struct Ops {
         bf16x8 w[FN], x[FM];
     };
+    // piece of the weight row holding this lane's 8 weights (E4M3: 8 bytes, in
+    // half of a 16-byte piece; the key of 64-byte rows depends on l%16 only)
+    auto w_off = [&](int half) {
+        if constexpr (W8) {
+            const int byte = half * 32 + 8 * q;
+            return (((byte >> 4) ^ fold_key<RBW>(fr)) << 4) | (byte & 8);
+        } else {
+            return ((half * 4 + q) ^ key) * 16;
+        }
+    };
     auto read_ops = [&](int s, int buf, int half, Ops& o) {
         const uint32_t sx = s_sgn[sg_gl * J + (s * KS) / BK];
         const int off = ((half * 4 + q) ^ key) * 16;  // piece half*4 + q of CPR
         const uint8_t* X = fold_smem + buf * SB + (wm * TMW + fr) * RB + off;
-        const uint8_t* W = fold_smem + buf * SB + SX + (wn * TNW + fr) * RB + off;
+        const uint8_t* W = fold_smem + buf * SB + SX + (wn * TNW + fr) * RBW + w_off(half);
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            uint4 v = *reinterpret_cast<const uint4*>(W + i * 16 * RB);
+            uint4 v;
+            if constexpr (W8) {
+                v = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(W + i * 16 * RBW));
+            } else {
+                v = *reinterpret_cast<const uint4*>(W + i * 16 * RBW);
+            }
             v.x ^= sx;
             v.y ^= sx;
             v.z ^= sx;
@@ -323,11 +347,21 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
         uint16_t* yr = y + static_cast<size_t>(m) * N + nbase;
 #pragma unroll
         for (int h = 0; h < FN / 2; ++h) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = acc[2 * h][mb][i];
+                v[4 + i] = acc[2 * h + 1][mb][i];
+            }
+            if constexpr (W8) {  // the rows' E4M3 scales
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] *= wscale[nbase + 8 * h + i];
+            }
             uint4 o;
-            o.x = pack_bf16(apply_act(acc[2 * h][mb][0], act), apply_act(acc[2 * h][mb][1], act));
-            o.y = pack_bf16(apply_act(acc[2 * h][mb][2], act), apply_act(acc[2 * h][mb][3], act));
-            o.z = pack_bf16(apply_act(acc[2 * h + 1][mb][0], act), apply_act(acc[2 * h + 1][mb][1], act));
-            o.w = pack_bf16(apply_act(acc[2 * h + 1][mb][2], act), apply_act(acc[2 * h + 1][mb][3], act));
+            o.x = pack_bf16(apply_act(v[0], act), apply_act(v[1], act));
+            o.y = pack_bf16(apply_act(v[2], act), apply_act(v[3], act));
+            o.z = pack_bf16(apply_act(v[4], act), apply_act(v[5], act));
+            o.w = pack_bf16(apply_act(v[6], act), apply_act(v[7], act));
             *reinterpret_cast<uint4*>(yr + 8 * h) = o;
         }
     }
@@ -785,8 +819,11 @@ struct FoldCfg {
     size_t lds;
 };
 
-inline size_t fold_lds(int BM, int BNB, int KS, int NSTG, const Dims& d) {
-    return static_cast<size_t>(NSTG) * (BM + BNB) * KS * 2 + static_cast<size_t>(2) * (BNB / d.BN) * d.J * 4;
+// LDS of a fold launch: NSTG stages of the x tile (BM rows of KS bf16) and the
+// weight tile (BNB rows of KS weights of WB bytes), plus the plan table.
+inline size_t fold_lds(int BM, int BNB, int KS, int NSTG, int WB, const Dims& d) {
+    return static_cast<size_t>(NSTG) * (static_cast<size_t>(BM) * KS * 2 + static_cast<size_t>(BNB) * KS * WB) +
+           static_cast<size_t>(2) * (BNB / d.BN) * d.J * 4;
 }
 
 int device_attribute(hipDeviceAttribute_t attr, int fallback) {
@@ -801,20 +838,23 @@ int max_lds_per_block() { return device_attribute(hipDeviceAttributeMaxSharedMem
 // Tile choice (tokens x neurons), the neuron tile a whole number of groups
 // that divides N:
 //   256 x 256, 8 waves of 128 x 64, 2 stages (two waves per SIMD: one
-//              multiplies while the other waits on LDS or a barrier);
+//              multiplies while the other waits on LDS or a barrier; 3 stages
+//              with E4M3 weights, whose weight tile is half the size);
 //   256 x 128, 4 waves of 128 x 64, 3 stages, when N is not a multiple of 256;
 //   128 x 128, 4 waves of 64 x 64, 4 stages, for M <= 128 or when only 128
 //              divides N and M is small.
+// 32-wide stages (twice the buffers) when BK % 64 != 0, bf16 weights only.
 // Buffer offsets are 32-bit: a tile's rows must span less than 2 GiB.
 inline FoldCfg fold_config(const ForwardArgs& a) {
     const Dims& d = a.d;
-    if (d.BK % 32 != 0) return FoldCfg{0, 0, 0, 0, 0};
+    const int WB = a.w_fp8 ? 1 : 2;
+    if (d.BK % 32 != 0 || (a.w_fp8 && d.BK % 64 != 0)) return FoldCfg{0, 0, 0, 0, 0};
     auto fits = [&](int BNB) { return BNB % d.BN == 0 && d.N % BNB == 0; };
     int BM = 0, BNB = 0, NSTG = 0, KS = 64;
     if (fits(256) && a.M > 128) {
         BM = 256;
         BNB = 256;
-        NSTG = 2;
+        NSTG = a.w_fp8 ? 3 : 2;
     } else if (fits(128) && a.M > 128) {
         BM = 256;
         BNB = 128;
@@ -829,30 +869,33 @@ inline FoldCfg fold_config(const ForwardArgs& a) {
         NSTG = std::min(2 * NSTG, 4);
     }
     if (BM == 0) return FoldCfg{0, 0, 0, 0, 0};
-    if (static_cast<double>(std::max(BM * d.K, BNB * d.Kc)) * 2.0 >= 2147483648.0) return FoldCfg{0, 0, 0, 0, 0};
-    const size_t lds = fold_lds(BM, BNB, KS, NSTG, d);
+    if (static_cast<double>(std::max(BM * d.K * 2, BNB * d.Kc * WB)) >= 2147483648.0) return FoldCfg{0, 0, 0, 0, 0};
+    const size_t lds = fold_lds(BM, BNB, KS, NSTG, WB, d);
     if (lds > static_cast<size_t>(max_lds_per_block())) return FoldCfg{0, 0, 0, 0, 0};
     return FoldCfg{BM, BNB, KS, NSTG, lds};
 }
 
-template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool FROM_HASH>
+template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool W8, bool FROM_HASH>
 ss1_status launch_fold_cfg(const ForwardArgs& a, size_t lds, int64_t n_base, int64_t n_cols) {
     const Dims& d = a.d;
     const int n_mt = static_cast<int>((a.M + BM - 1) / BM);
     const long long blocks = static_cast<long long>(n_mt) * (n_cols / BNB);
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
     if (blocks == 0) return SS1_OK;
-    auto kern = &fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>;
+    auto kern = &fold_kernel<BM, BNB, WM, WN, KS, NSTG, W8, FROM_HASH>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds)) != hipSuccess)
         return SS1_ERR_HIP;
-    hipLaunchKernelGGL((fold_kernel<BM, BNB, WM, WN, KS, NSTG, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((fold_kernel<BM, BNB, WM, WN, KS, NSTG, W8, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
                        dim3(WM * WN * 64), lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
                        (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, n_mt, a.act, (int)n_base,
-                       (int)n_cols);
+                       (int)n_cols, a.wscale);
     return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
 }
+
+// Stages of the 128 x 256 tiles of a split launch's second part.
+inline int fold_rest_nstg(const ForwardArgs& a) { return a.w_fp8 ? 4 : 3; }
 
 // A 256 x 256 launch whose tiles end in a partial round splits its neurons: the
 // columns [0, main) in 256 x 256 tiles that fill whole rounds of compute units,
@@ -862,7 +905,8 @@ ss1_status launch_fold_cfg(const ForwardArgs& a, size_t lds, int64_t n_base, int
 int64_t fold_main_cols(const ForwardArgs& a, const FoldCfg& cfg) {
     const Dims& d = a.d;
     if (!(cfg.BM == 256 && cfg.BNB == 256 && cfg.KS == 64)) return d.N;
-    if (fold_lds(128, 256, 64, 3, d) > static_cast<size_t>(max_lds_per_block())) return d.N;
+    if (fold_lds(128, 256, 64, fold_rest_nstg(a), a.w_fp8 ? 1 : 2, d) > static_cast<size_t>(max_lds_per_block()))
+        return d.N;
     const long long cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
     const long long n_mt = (a.M + 255) / 256, n_nt = d.N / 256;
     const long long tiles = n_mt * n_nt;
@@ -876,27 +920,33 @@ int64_t fold_main_cols(const ForwardArgs& a, const FoldCfg& cfg) {
     return split < 0.97 * single ? n_main * 256 : d.N;
 }
 
-template <bool FROM_HASH>
+template <bool FROM_HASH, bool W8>
 ss1_status launch_fold_t(const ForwardArgs& a) {
     const FoldCfg cfg = fold_config(a);
     const int64_t N = a.d.N;
+    constexpr int WB = W8 ? 1 : 2;
+    constexpr int NB = W8 ? 3 : 2;       // stages of the 256 x 256 tile
+    constexpr int NR = W8 ? 4 : 3;       // stages of the 128 x 256 tile
     if (cfg.BM == 256 && cfg.BNB == 256) {
-        if (cfg.KS == 64 && cfg.NSTG == 2) {
+        if (cfg.KS == 64 && cfg.NSTG == NB) {
             const int64_t main = fold_main_cols(a, cfg);
-            ss1_status st = launch_fold_cfg<256, 256, 2, 4, 64, 2, FROM_HASH>(a, cfg.lds, 0, main);
+            ss1_status st = launch_fold_cfg<256, 256, 2, 4, 64, NB, W8, FROM_HASH>(a, cfg.lds, 0, main);
             if (st != SS1_OK || main == N) return st;
-            return launch_fold_cfg<128, 256, 2, 4, 64, 3, FROM_HASH>(a, fold_lds(128, 256, 64, 3, a.d), main,
-                                                                    N - main);
+            return launch_fold_cfg<128, 256, 2, 4, 64, NR, W8, FROM_HASH>(a, fold_lds(128, 256, 64, NR, WB, a.d),
+                                                                         main, N - main);
         }
-        if (cfg.KS == 32 && cfg.NSTG == 4) return launch_fold_cfg<256, 256, 2, 4, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
+        if constexpr (!W8) {
+            if (cfg.KS == 32 && cfg.NSTG == 4)
+                return launch_fold_cfg<256, 256, 2, 4, 32, 4, W8, FROM_HASH>(a, cfg.lds, 0, N);
+        }
     }
     if (cfg.BM == 256 && cfg.BNB == 128) {
-        if (cfg.KS == 64) return launch_fold_cfg<256, 128, 2, 2, 64, 3, FROM_HASH>(a, cfg.lds, 0, N);
-        return launch_fold_cfg<256, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
+        if (cfg.KS == 64) return launch_fold_cfg<256, 128, 2, 2, 64, 3, W8, FROM_HASH>(a, cfg.lds, 0, N);
+        if constexpr (!W8) return launch_fold_cfg<256, 128, 2, 2, 32, 4, W8, FROM_HASH>(a, cfg.lds, 0, N);
     }
     if (cfg.BM == 128 && cfg.BNB == 128) {
-        if (cfg.KS == 64) return launch_fold_cfg<128, 128, 2, 2, 64, 4, FROM_HASH>(a, cfg.lds, 0, N);
-        return launch_fold_cfg<128, 128, 2, 2, 32, 4, FROM_HASH>(a, cfg.lds, 0, N);
+        if (cfg.KS == 64) return launch_fold_cfg<128, 128, 2, 2, 64, 4, W8, FROM_HASH>(a, cfg.lds, 0, N);
+        if constexpr (!W8) return launch_fold_cfg<128, 128, 2, 2, 32, 4, W8, FROM_HASH>(a, cfg.lds, 0, N);
     }
     return SS1_ERR_ALGO;
 }
@@ -1055,8 +1105,9 @@ double fold_estimate_us(const ForwardArgs& a) {
 }
 
 ss1_status launch_fold(const ForwardArgs& a) {
-    if (a.w_fp8) return SS1_ERR_ALGO;
-    return a.form == PlanForm::Hash ? launch_fold_t<true>(a) : launch_fold_t<false>(a);
+    // fp8 weights come with the forward hash only
+    if (a.w_fp8) return a.form == PlanForm::Hash ? launch_fold_t<true, true>(a) : SS1_ERR_ALGO;
+    return a.form == PlanForm::Hash ? launch_fold_t<true, false>(a) : launch_fold_t<false, false>(a);
 }
 
 }  // namespace ss1
