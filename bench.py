@@ -455,14 +455,9 @@ def cpu_baseline_mlp(c, budget_s=10.0, m=MLP_SHAPE):
 
 
 def fp8_kernel_name(wl):
-    """The kernel ss1_forward_fp8w runs: small-M for M <= 16, else the fold
-    kernel where the bf16 forward would pick it (the same time models; fp8
-    weights need BK % 64 == 0 there), else the fused kernel."""
-    if wl.M <= 16:
-        return "smallm"
-    if wl.BK % 64 == 0 and kernel_name(wl, "auto") == "fold":
-        return "fold"
-    return "fused"
+    """The kernel ss1_forward_fp8w runs for this layer (the library's choice)."""
+    import sketched_parameter_sharing_amd as ss1
+    return ss1.select_algo(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype, weights="fp8")
 
 
 def kernel_name(wl, algo):

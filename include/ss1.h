@@ -201,10 +201,12 @@ ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
 /*
  * ss1_select_algo -- HOST.  The kernel (an ss1_algo value, never AUTO) that
  * ss1_forward would run for a layer with these descriptors; only their
- * dtypes and sizes are read (data may be NULL).  For M == 0 it reports the
- * kernel a non-empty call of the same layer would use.  May query the current
- * HIP device's properties.  Errors: as the shape and dtype checks of
- * ss1_forward.
+ * dtypes and sizes are read (data may be NULL).  With W_c of dtype
+ * FP8_E4M3 (and x BF16) it reports the kernel ss1_forward_fp8w would run
+ * (SMALLM, FOLD or FUSED).  For M == 0 it reports the kernel a non-empty call
+ * of the same layer would use.  May query the current HIP device's
+ * properties.  Errors: as the shape and dtype checks of ss1_forward (of
+ * ss1_forward_fp8w for E4M3 weights).
  */
 ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
                            int32_t BN, int32_t* algo);

@@ -284,12 +284,15 @@ def backward(x, W_c, hash_, sign, c: int, BK: int, BN: int, dy, dx=True, dW_c=Tr
     return dx, dW_c
 
 
-def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16") -> str:
+def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16",
+                weights: str | None = None) -> str:
     """Name of the kernel ss1_forward runs for this layer ("fused", "smallm",
-    "band" or "generic")."""
+    "band", "fold" or "generic"); with weights="fp8", the kernel
+    ss1_forward_fp8w runs (bf16 x)."""
     code = BF16 if dtype == "bf16" else F32
+    wcode = FP8_E4M3 if weights == "fp8" else code
     x = Tensor(None, code, 0, M, K)
-    w = Tensor(None, code, 0, N, K // c if c > 0 else 0)
+    w = Tensor(None, wcode, 0, N, K // c if c > 0 else 0)
     out = ctypes.c_int32(-1)
     _check(load().ss1_select_algo(ctypes.byref(x), ctypes.byref(w), c, BK, BN, ctypes.byref(out)),
            "ss1_select_algo")

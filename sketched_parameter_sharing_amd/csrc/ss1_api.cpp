@@ -83,6 +83,19 @@ int32_t auto_algo(const ForwardArgs& a) {
     return SS1_ALGO_GENERIC;
 }
 
+// The kernel ss1_forward_fp8w runs (a.w_fp8 set), or -1 when none can:
+// small-M for decode shapes; otherwise the fold kernel where the time models
+// put it clearly ahead of the fused kernel, which runs fp8 weights (on layers
+// short enough for the band kernel, which has no fp8 form, the fused kernel
+// measured about 1.6x the band kernel's time); else the fused kernel.
+int32_t fp8_algo(const ForwardArgs& a) {
+    if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
+    if (!ss1::fused_supported(a)) return -1;
+    const double sketch = sketch_estimate_us(a) * (ss1::band_supported(a, 48) ? 1.6 : 1.0);
+    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch) return SS1_ALGO_FOLD;
+    return SS1_ALGO_FUSED;
+}
+
 ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
     switch (algo) {
         case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
@@ -178,9 +191,23 @@ extern "C" ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c
     if (!xs.data) xs.data = dummy;
     if (!ws.data) ws.data = dummy;
     y.data = xs.data;
+    // E4M3 weights: the choice of ss1_forward_fp8w (bf16 x only)
+    const bool fp8 = ws.dtype == SS1_FP8_E4M3;
+    if (fp8) {
+        if (xs.dtype != SS1_BF16) return SS1_ERR_DTYPE;
+        ws.dtype = xs.dtype;
+    }
     ForwardArgs a;
-    ss1_status st = check_forward(&xs, &ws, &plan_i, &plan_s, c, BK, BN, &y, PlanForm::Index, nullptr, &a);
+    ss1_status st = check_forward(&xs, &ws, &plan_i, &plan_s, c, BK, BN, &y, fp8 ? PlanForm::Hash : PlanForm::Index,
+                                  nullptr, &a);
     if (st != SS1_OK) return st;
+    if (fp8) {
+        a.w_fp8 = true;
+        const int32_t k = fp8_algo(a);
+        if (k < 0) return SS1_ERR_SHAPE;
+        *algo = k;
+        return SS1_OK;
+    }
     *algo = auto_algo(a);
     return SS1_OK;
 }
@@ -308,12 +335,11 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     if (!aligned(scale, 4)) return SS1_ERR_ALIGN;
     a.w_fp8 = true;
     a.wscale = scale;
-    const bool small = ss1::smallm_supported(a);
-    if (!small && !ss1::fused_supported(a)) return SS1_ERR_SHAPE;
+    const int32_t algo = fp8_algo(a);
+    if (algo < 0) return SS1_ERR_SHAPE;
     if (a.M == 0) return SS1_OK;
-    if (small) return ss1::launch_smallm(a);
-    // large M: the fold kernel where the time models put it clearly ahead
-    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return ss1::launch_fold(a);
+    if (algo == SS1_ALGO_SMALLM) return ss1::launch_smallm(a);
+    if (algo == SS1_ALGO_FOLD) return ss1::launch_fold(a);
     return ss1::launch_fused(a);
 }
 

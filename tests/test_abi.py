@@ -324,7 +324,16 @@ def test_select_algo_host():
     assert ss1.select_algo(16, 14336, 4096, 2, 64, 64) == "smallm"
     assert ss1.select_algo(64, 256, 256, 2, 32, 32, "f32") == "generic"
     assert ss1.select_algo(300, 240, 96, 2, 24, 48) == "generic"
-    assert ss1.select_algo(4096, 4096, 4096, 2, 64, 64) in ("fused", "band")
+    assert ss1.select_algo(4096, 4096, 4096, 2, 64, 64) in ("fused", "band", "fold")
+    # E4M3 weights: the choice of ss1_forward_fp8w (no band or generic kernel)
+    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64, weights="fp8") == "smallm"
+    assert ss1.select_algo(8192, 768, 3072, 2, 64, 64, weights="fp8") in ("fused", "fold")
+    with pytest.raises(ss1.SS1Error) as e:
+        ss1.select_algo(64, 256, 256, 2, 32, 32, "f32", weights="fp8")
+    assert e.value.status == _lib.ERR_DTYPE
+    with pytest.raises(ss1.SS1Error) as e:   # neither small-M nor fused: BN = 48
+        ss1.select_algo(300, 768, 3 * 48, 2, 32, 48, weights="fp8")
+    assert e.value.status == _lib.ERR_SHAPE
     with pytest.raises(ss1.SS1Error) as e:
         ss1.select_algo(8, 250, 64, 2, 64, 64)
     assert e.value.status == _lib.ERR_SHAPE
