@@ -443,6 +443,8 @@ ss1_status launch_dw_cfg(const void* x, const void* dy, const int32_t* hash, con
 
 ss1_status launch_backward(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign, const void* dy,
                            void* dx, void* dW, int64_t M, const Dims& d, void* stream) {
+    if (dx && dW && M > 0 && bwd_fold_supported(M, d))
+        return launch_bwd_fold(x, W_c, hash, sign, dy, dx, dW, M, d, stream);
     if (dW && dw_fold_supported(M, d)) {
         const ss1_status st = launch_dw_fold(x, dy, hash, sign, dW, M, d, stream);
         if (st != SS1_OK) return st;

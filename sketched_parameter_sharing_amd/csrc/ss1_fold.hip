@@ -392,12 +392,10 @@ __device__ __forceinline__ int dx_tkey(int r) {
 }
 
 template <int BM, int BNB, int WM, int WN, int NSTG>
-__global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __restrict__ dy,
-                                                              const uint16_t* __restrict__ w,
-                                                              const int32_t* __restrict__ hash,
-                                                              const int8_t* __restrict__ sign,
-                                                              uint16_t* __restrict__ dx, int M, int K, int N, int J,
-                                                              int Jc, int BK, int BN, int n_mt) {
+__device__ __forceinline__ void dxfold_body(int bid, const uint16_t* __restrict__ dy,
+                                            const uint16_t* __restrict__ w, const int32_t* __restrict__ hash,
+                                            const int8_t* __restrict__ sign, uint16_t* __restrict__ dx, int M,
+                                            int K, int N, int J, int Jc, int BK, int BN, int n_mt) {
     constexpr int NWV = WM * WN;
     constexpr int TMW = BM / WM, TNW = BNB / WN;  // wave tile: tokens x input features
     constexpr int FM = TMW / 16, FN = TNW / 16;
@@ -418,7 +416,7 @@ __global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __
 
     constexpr int GM = 4;
     const int n_nt = K / BNB;
-    const int tile = xcd_tile(blockIdx.x, n_mt * n_nt);
+    const int tile = xcd_tile(bid, n_mt * n_nt);
     const int strip = tile / (GM * n_nt);
     const int gm = min(GM, n_mt - strip * GM);
     const int rem = tile - strip * GM * n_nt;
@@ -597,10 +595,10 @@ __global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __
 // the block's group plan; a missing source points past x and loads zeros).
 // The source's sign goes onto the x operand as it leaves LDS.
 template <int KT, int CS, int NSTG>
-__global__ __launch_bounds__(512) void dwfold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
-                                                     const int32_t* __restrict__ hash,
-                                                     const int8_t* __restrict__ sign, uint16_t* __restrict__ dw,
-                                                     int M, int K, int N, int J, int Jc, int BK, int BN) {
+__device__ __forceinline__ void dwfold_body(int bid, const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
+                                            const int32_t* __restrict__ hash, const int8_t* __restrict__ sign,
+                                            uint16_t* __restrict__ dw, int M, int K, int N, int J, int Jc, int BK,
+                                            int BN) {
     constexpr int NWV = 8;
     constexpr int NSUB = KT / 64;                 // 64-column sub-tiles
     constexpr int WM = NSUB, WN = 4 / WM;         // waves of a half: along columns x neurons
@@ -623,8 +621,8 @@ __global__ __launch_bounds__(512) void dwfold_kernel(const uint16_t* __restrict_
 
     const int Kc = Jc * BK;
     const int n_ct = Kc / KT;
-    const int nt = blockIdx.x / n_ct;             // 64-neuron tile
-    const int kc0 = (blockIdx.x - nt * n_ct) * KT;
+    const int nt = bid / n_ct;                    // 64-neuron tile
+    const int kc0 = (bid - nt * n_ct) * KT;
     const int n0 = nt * 64;
     const int g = n0 / BN;
 
@@ -812,6 +810,42 @@ __global__ __launch_bounds__(512) void dwfold_kernel(const uint16_t* __restrict_
             }
         }
     }
+}
+
+template <int BM, int BNB, int WM, int WN, int NSTG>
+__global__ __launch_bounds__(WM * WN * 64) void dxfold_kernel(const uint16_t* __restrict__ dy,
+                                                              const uint16_t* __restrict__ w,
+                                                              const int32_t* __restrict__ hash,
+                                                              const int8_t* __restrict__ sign,
+                                                              uint16_t* __restrict__ dx, int M, int K, int N, int J,
+                                                              int Jc, int BK, int BN, int n_mt) {
+    dxfold_body<BM, BNB, WM, WN, NSTG>(blockIdx.x, dy, w, hash, sign, dx, M, K, N, J, Jc, BK, BN, n_mt);
+}
+
+template <int KT, int CS, int NSTG>
+__global__ __launch_bounds__(512) void dwfold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ dy,
+                                                     const int32_t* __restrict__ hash,
+                                                     const int8_t* __restrict__ sign, uint16_t* __restrict__ dw,
+                                                     int M, int K, int N, int J, int Jc, int BK, int BN) {
+    dwfold_body<KT, CS, NSTG>(blockIdx.x, x, dy, hash, sign, dw, M, K, N, J, Jc, BK, BN);
+}
+
+// Both gradients in one launch: blocks [0, n_dw) are dW_c tiles, the rest dx
+// tiles.  The two are independent; sharing the grid lets dx tiles fill the
+// compute units that a layer's few dW_c tiles leave idle (GPT-2 S: 144 dW_c
+// tiles for 256 compute units), and the longer dW_c tiles are dispatched first.
+template <int DXBM, int DXNSTG, int KT, int CS, int DWNSTG>
+__global__ __launch_bounds__(512) void bwdfold_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+                                                      const int32_t* __restrict__ hash,
+                                                      const int8_t* __restrict__ sign,
+                                                      const uint16_t* __restrict__ dy, uint16_t* __restrict__ dx,
+                                                      uint16_t* __restrict__ dw, int M, int K, int N, int J, int Jc,
+                                                      int BK, int BN, int n_mt, int n_dw) {
+    if (static_cast<int>(blockIdx.x) < n_dw)
+        dwfold_body<KT, CS, DWNSTG>(blockIdx.x, x, dy, hash, sign, dw, M, K, N, J, Jc, BK, BN);
+    else
+        dxfold_body<DXBM, 256, 2, 4, DXNSTG>(blockIdx.x - n_dw, dy, w, hash, sign, dx, M, K, N, J, Jc, BK, BN,
+                                             n_mt);
 }
 
 struct FoldCfg {
@@ -1057,6 +1091,66 @@ ss1_status launch_dw_fold_k(const void* x, const void* dy, const int32_t* hash, 
 bool dx_fold_supported(int64_t M, const Dims& d) { return dxfold_ok(M, d); }
 
 bool dw_fold_supported(int64_t M, const Dims& d) { return dwfold_config(M, d).KT > 0; }
+
+template <int DXBM, int DXNSTG, int KT, int CS, int DWNSTG>
+ss1_status launch_bwd_fold_cfg(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign,
+                               const void* dy, void* dx, void* dW, int64_t M, const Dims& d, size_t lds,
+                               void* stream) {
+    const int n_mt = static_cast<int>((M + DXBM - 1) / DXBM);
+    const long long n_dw = static_cast<long long>(d.N / 64) * (d.Kc / KT);
+    const long long blocks = n_dw + static_cast<long long>(n_mt) * (d.K / 256);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    auto kern = &bwdfold_kernel<DXBM, DXNSTG, KT, CS, DWNSTG>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((bwdfold_kernel<DXBM, DXNSTG, KT, CS, DWNSTG>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(512), lds, static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(W_c), hash, sign, static_cast<const uint16_t*>(dy),
+                       static_cast<uint16_t*>(dx), static_cast<uint16_t*>(dW), (int)M, (int)d.K, (int)d.N, (int)d.J,
+                       (int)d.Jc, d.BK, d.BN, n_mt, static_cast<int>(n_dw));
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
+template <int DXBM, int DXNSTG>
+ss1_status launch_bwd_fold_dw(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign,
+                              const void* dy, void* dx, void* dW, int64_t M, const Dims& d, const DwCfg& cfg,
+                              size_t lds, void* stream) {
+    // the (KT, c) pairs and the stage counts dwfold_config gives them
+    if (cfg.KT == 256 && d.c == 1 && cfg.NSTG == 3)
+        return launch_bwd_fold_cfg<DXBM, DXNSTG, 256, 1, 3>(x, W_c, hash, sign, dy, dx, dW, M, d, lds, stream);
+    if (cfg.KT == 256 && d.c == 2 && cfg.NSTG == 2)
+        return launch_bwd_fold_cfg<DXBM, DXNSTG, 256, 2, 2>(x, W_c, hash, sign, dy, dx, dW, M, d, lds, stream);
+    if (cfg.KT == 128 && d.c == 1 && cfg.NSTG == 3)
+        return launch_bwd_fold_cfg<DXBM, DXNSTG, 128, 1, 3>(x, W_c, hash, sign, dy, dx, dW, M, d, lds, stream);
+    if (cfg.KT == 128 && d.c == 2 && cfg.NSTG == 3)
+        return launch_bwd_fold_cfg<DXBM, DXNSTG, 128, 2, 3>(x, W_c, hash, sign, dy, dx, dW, M, d, lds, stream);
+    if (cfg.KT == 128 && d.c == 4 && cfg.NSTG == 2)
+        return launch_bwd_fold_cfg<DXBM, DXNSTG, 128, 4, 2>(x, W_c, hash, sign, dy, dx, dW, M, d, lds, stream);
+    return SS1_ERR_ALGO;
+}
+
+bool bwd_fold_supported(int64_t M, const Dims& d) {
+    if (!dxfold_ok(M, d)) return false;
+    const DwCfg cfg = dwfold_config(M, d);
+    if (cfg.KT == 0) return false;
+    const size_t lds = std::max(dxfold_lds(dxfold_bm(M, d), d), cfg.lds);
+    if (lds > static_cast<size_t>(max_lds_per_block())) return false;
+    const bool known = (cfg.KT == 256 && ((d.c == 1 && cfg.NSTG == 3) || (d.c == 2 && cfg.NSTG == 2))) ||
+                       (cfg.KT == 128 && ((d.c == 1 && cfg.NSTG == 3) || (d.c == 2 && cfg.NSTG == 3) ||
+                                          (d.c == 4 && cfg.NSTG == 2)));
+    return known;
+}
+
+ss1_status launch_bwd_fold(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign, const void* dy,
+                           void* dx, void* dW, int64_t M, const Dims& d, void* stream) {
+    if (!bwd_fold_supported(M, d)) return SS1_ERR_ALGO;
+    const DwCfg cfg = dwfold_config(M, d);
+    const int bm = dxfold_bm(M, d);
+    const size_t lds = std::max(dxfold_lds(bm, d), cfg.lds);
+    if (bm == 128) return launch_bwd_fold_dw<128, 3>(x, W_c, hash, sign, dy, dx, dW, M, d, cfg, lds, stream);
+    return launch_bwd_fold_dw<256, 2>(x, W_c, hash, sign, dy, dx, dW, M, d, cfg, lds, stream);
+}
 
 ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
                           int64_t M, const Dims& d, void* stream) {

@@ -60,6 +60,11 @@ ss1_status launch_dx_fold(const void* dy, const void* W_c, const int32_t* hash, 
 // Backward dW_c as the fold contraction over (token, source) (ss1_fold.hip):
 // bf16, hash plan, BN % 64 == 0, BK % 64 == 0, c in {1, 2, 4}, Kc % 128 == 0.
 bool dw_fold_supported(int64_t M, const Dims& d);
+// Both gradients in one fold launch (dW_c tiles and dx tiles share the grid)
+// where both fold kernels apply and their configurations pair up.
+bool bwd_fold_supported(int64_t M, const Dims& d);
+ss1_status launch_bwd_fold(const void* x, const void* W_c, const int32_t* hash, const int8_t* sign, const void* dy,
+                           void* dx, void* dW, int64_t M, const Dims& d, void* stream);
 ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
                           int64_t M, const Dims& d, void* stream);
 
