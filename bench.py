@@ -105,6 +105,7 @@ KERNEL_SOURCES = {
     "band": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "fused": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "smallm": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "gemv": ("ss1_gemv.hip", "ss1_device.h", "ss1_internal.h"),
     "generic": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_internal.h"),
     "project": ("ss1_project.hip", "ss1_device.h", "ss1_internal.h"),
@@ -514,7 +515,7 @@ def main():
     ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "backward"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "generic", "band", "fold"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "generic", "band", "fold"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

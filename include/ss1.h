@@ -74,7 +74,8 @@ typedef enum {
     SS1_ALGO_SMALLM = 2,   /* bf16: decode shapes, M <= 16, W_c streamed once          */
     SS1_ALGO_GENERIC = 3,  /* any dtype and chunking: LDS-tiled FMA kernel             */
     SS1_ALGO_BAND = 4,     /* bf16, short rows: a band of input rows held in LDS        */
-    SS1_ALGO_FOLD = 5      /* bf16: W_c expanded on chip, one dense-shaped MFMA GEMM    */
+    SS1_ALGO_FOLD = 5,     /* bf16: W_c expanded on chip, one dense-shaped MFMA GEMM    */
+    SS1_ALGO_GEMV = 6      /* bf16: M <= 4, matrix-vector kernel, W_c streamed once     */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */
@@ -178,6 +179,11 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  * HIP call, when that kernel cannot run the given dtype or shape:
  *   FUSED  : BF16, BK % 32 == 0, BN in {32, 64, 128}
  *   SMALLM : BF16, M <= 16, BK % 32 == 0, BN % 16 == 0
+ *   GEMV   : BF16, M <= 4, BN % 16 == 0, 512 <= Kc = K/c <= 65536 (32768
+ *            for M = 2, 16384 for M = 3 or 4), and K/BK <= 2 T, where
+ *            T = 64 ceil(Kc / (512 Q)) threads take Q = 1 (Kc <= 8192), 2, 4
+ *            or 8 slices of 8 compressed columns each.  Each block's weight
+ *            loads are all issued before it waits for anything.
  *   GENERIC: any valid call
  *   BAND   : BF16, BK % 32 == 0, BN in {32, 64, 128}, and 32 input rows of K
  *            bf16 (plus the plan) fit in one block's LDS (K up to about 2400)
@@ -186,8 +192,9 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *            Multiplies x by the expanded weight W_c S_g (built in LDS from
  *            W_c, never stored): the same y as the sketch kernels up to
  *            rounding (no bf16 rounding of a sketch), dense MFMA work.
- * ss1_forward picks FOLD for large M where its modelled time is below the
- * sketch kernels' (ss1_select_algo reports the choice).
+ * ss1_forward picks GEMV for M <= 4 where it applies, else SMALLM for
+ * M <= 16, and FOLD for large M where its modelled time is below the sketch
+ * kernels' (ss1_select_algo reports the choice).
  */
 ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
                             const int32_t* hash, const int8_t* sign,
@@ -203,7 +210,7 @@ ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
  * ss1_forward would run for a layer with these descriptors; only their
  * dtypes and sizes are read (data may be NULL).  With W_c of dtype
  * FP8_E4M3 (and x BF16) it reports the kernel ss1_forward_fp8w would run
- * (SMALLM, FOLD or FUSED).  For M == 0 it reports the kernel a non-empty call
+ * (GEMV, SMALLM, FOLD or FUSED).  For M == 0 it reports the kernel a non-empty call
  * of the same layer would use.  May query the current HIP device's
  * properties.  Errors: as the shape and dtype checks of ss1_forward (of
  * ss1_forward_fp8w for E4M3 weights).

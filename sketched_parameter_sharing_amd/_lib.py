@@ -22,9 +22,9 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = ran
 # dtypes (ss1_dtype)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 # kernel choice (ss1_algo)
-ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD = range(6)
+ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD, ALGO_GEMV = range(7)
 ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC,
-         "band": ALGO_BAND, "fold": ALGO_FOLD}
+         "band": ALGO_BAND, "fold": ALGO_FOLD, "gemv": ALGO_GEMV}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
@@ -287,7 +287,7 @@ def backward(x, W_c, hash_, sign, c: int, BK: int, BN: int, dy, dx=True, dW_c=Tr
 def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "bf16",
                 weights: str | None = None) -> str:
     """Name of the kernel ss1_forward runs for this layer ("fused", "smallm",
-    "band", "fold" or "generic"); with weights="fp8", the kernel
+    "gemv", "band", "fold" or "generic"); with weights="fp8", the kernel
     ss1_forward_fp8w runs (bf16 x)."""
     code = BF16 if dtype == "bf16" else F32
     wcode = FP8_E4M3 if weights == "fp8" else code

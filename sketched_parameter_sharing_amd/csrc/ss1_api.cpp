@@ -72,10 +72,11 @@ double sketch_estimate_us(const ForwardArgs& a) {
 }
 
 // The kernel ss1_forward picks for a validated call: decode shapes go to the
-// small-M kernel; otherwise the fold kernel when its estimate is clearly
+// matrix-vector kernel (M <= 4) or the small-M kernel; otherwise the fold kernel when its estimate is clearly
 // (10%) below the sketch kernels', else the band kernel where a band of input
 // rows fits in LDS, else the fused kernel.
 int32_t auto_algo(const ForwardArgs& a) {
+    if (ss1::gemv_supported(a)) return SS1_ALGO_GEMV;
     if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
     if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return SS1_ALGO_FOLD;
     if (ss1::band_supported(a, 48)) return SS1_ALGO_BAND;
@@ -84,11 +85,12 @@ int32_t auto_algo(const ForwardArgs& a) {
 }
 
 // The kernel ss1_forward_fp8w runs (a.w_fp8 set), or -1 when none can:
-// small-M for decode shapes; otherwise the fold kernel where the time models
+// matrix-vector or small-M for decode shapes; otherwise the fold kernel where the time models
 // put it clearly ahead of the fused kernel, which runs fp8 weights (on layers
 // short enough for the band kernel, which has no fp8 form, the fused kernel
 // measured about 1.6x the band kernel's time); else the fused kernel.
 int32_t fp8_algo(const ForwardArgs& a) {
+    if (ss1::gemv_supported(a)) return SS1_ALGO_GEMV;
     if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
     if (!ss1::fused_supported(a)) return -1;
     const double sketch = sketch_estimate_us(a) * (ss1::band_supported(a, 48) ? 1.6 : 1.0);
@@ -99,6 +101,7 @@ int32_t fp8_algo(const ForwardArgs& a) {
 ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
     switch (algo) {
         case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
+        case SS1_ALGO_GEMV: return ss1::launch_gemv(a);
         case SS1_ALGO_BAND: return ss1::launch_band(a);
         case SS1_ALGO_FUSED: return ss1::launch_fused(a);
         case SS1_ALGO_FOLD: return ss1::launch_fold(a);
@@ -122,6 +125,9 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_SMALLM:
             if (!ss1::smallm_supported(a)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_smallm(a);
+        case SS1_ALGO_GEMV:
+            if (!ss1::gemv_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_gemv(a);
         case SS1_ALGO_BAND:
             if (!ss1::band_supported(a, 32)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_band(a);
@@ -338,6 +344,7 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     const int32_t algo = fp8_algo(a);
     if (algo < 0) return SS1_ERR_SHAPE;
     if (a.M == 0) return SS1_OK;
+    if (algo == SS1_ALGO_GEMV) return ss1::launch_gemv(a);
     if (algo == SS1_ALGO_SMALLM) return ss1::launch_smallm(a);
     if (algo == SS1_ALGO_FOLD) return ss1::launch_fold(a);
     return ss1::launch_fused(a);

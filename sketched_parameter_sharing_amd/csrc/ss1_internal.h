@@ -44,6 +44,9 @@ constexpr int32_t kActGelu = 1;
 // Which kernels can run a call (host-side checks only).
 bool fused_supported(const ForwardArgs& a);
 bool smallm_supported(const ForwardArgs& a);
+// Matrix-vector kernel (ss1_gemv.hip): bf16, M <= 4, BN % 16 == 0, 512 to
+// 65536 compressed columns (fewer for M > 1) and J within twice the block.
+bool gemv_supported(const ForwardArgs& a);
 // Band kernel: the layer's rows are short enough for a band of at least
 // min_rows input rows to sit in LDS.
 bool band_supported(const ForwardArgs& a, int min_rows);
@@ -71,6 +74,7 @@ ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, co
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);
 ss1_status launch_smallm(const ForwardArgs& a);
+ss1_status launch_gemv(const ForwardArgs& a);
 ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_fold(const ForwardArgs& a);

@@ -142,6 +142,10 @@ FORWARD_ERRORS = [
     ("algo fused BN", T(8, 256), T(48, 128), T(8, 48), {"BN": 48, "algo": _lib.ALGO_FUSED}, _lib.ERR_ALGO),
     ("algo smallm M", T(17, 256), T(64, 128), T(17, 64), {"algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
     ("algo smallm BN", T(4, 256), T(40, 128), T(4, 40), {"BN": 40, "algo": _lib.ALGO_SMALLM}, _lib.ERR_ALGO),
+    ("algo gemv M", T(5, 2048), T(64, 1024), T(5, 64), {"algo": _lib.ALGO_GEMV}, _lib.ERR_ALGO),
+    ("algo gemv Kc", T(1, 512), T(64, 256), T(1, 64), {"algo": _lib.ALGO_GEMV}, _lib.ERR_ALGO),
+    ("algo gemv f32", T(1, 2048, _lib.F32), T(64, 1024, _lib.F32), T(1, 64, _lib.F32),
+     {"algo": _lib.ALGO_GEMV}, _lib.ERR_ALGO),
     ("algo fold f32", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32),
      {"algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
     ("algo fold BK", T(8, 256), T(64, 128), T(8, 64), {"BK": 32, "algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
@@ -318,15 +322,23 @@ def test_binding_refuses_host_tensors():
 
 
 def test_select_algo_host():
-    # decode shapes take the small-M kernel, float32 the generic one; invalid
-    # shapes give the forward's own status codes
-    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64) == "smallm"
+    # decode shapes take the matrix-vector kernel (M <= 4) or the small-M
+    # kernel, float32 the generic one; invalid shapes give the forward's own
+    # status codes
+    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64) == "gemv"
+    assert ss1.select_algo(2, 14336, 4096, 2, 64, 64) == "gemv"
+    assert ss1.select_algo(4, 4096, 14336, 2, 64, 64) == "gemv"
+    assert ss1.select_algo(4, 14336, 4096, 2, 64, 64) == "gemv"
+    assert ss1.select_algo(3, 65536, 1024, 2, 64, 64) == "smallm"  # Kc = 32768 > 16384 at 4 token slots
+    assert ss1.select_algo(5, 4096, 14336, 2, 64, 64) == "smallm"
     assert ss1.select_algo(16, 14336, 4096, 2, 64, 64) == "smallm"
+    assert ss1.select_algo(1, 768, 3072, 2, 64, 64) == "smallm"   # Kc = 384: under one wave of slices
     assert ss1.select_algo(64, 256, 256, 2, 32, 32, "f32") == "generic"
     assert ss1.select_algo(300, 240, 96, 2, 24, 48) == "generic"
     assert ss1.select_algo(4096, 4096, 4096, 2, 64, 64) in ("fused", "band", "fold")
     # E4M3 weights: the choice of ss1_forward_fp8w (no band or generic kernel)
-    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64, weights="fp8") == "smallm"
+    assert ss1.select_algo(1, 4096, 14336, 2, 64, 64, weights="fp8") == "gemv"
+    assert ss1.select_algo(8, 4096, 14336, 2, 64, 64, weights="fp8") == "smallm"
     assert ss1.select_algo(8192, 768, 3072, 2, 64, 64, weights="fp8") in ("fused", "fold")
     with pytest.raises(ss1.SS1Error) as e:
         ss1.select_algo(64, 256, 256, 2, 32, 32, "f32", weights="fp8")

@@ -81,7 +81,7 @@ def run_case(wl, M, rows=None):
     assert np.all(ok)
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 300])
+@pytest.mark.parametrize("M", [1, 3, 5, 16, 300])
 @pytest.mark.parametrize("c,BN", [(1, 64), (2, 64), (4, 32), (8, 128), (3, 64)])
 def test_forward_fp8w_reduced(M, c, BN):
     K = 96 * 64 if c == 3 else 2048

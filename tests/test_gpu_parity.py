@@ -183,6 +183,7 @@ def test_bf16_full_size_sampled_rows(name):
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("gpt2l_down", "fused"),
                                        ("llama_gateup_m16", "smallm"), ("llama_down_m16", "smallm"),
+                                       ("llama_gateup_m1", "gemv"), ("llama_down_m1", "gemv"),
                                        ("square_c8_bn128", "fused"), ("square_c1_bn32", "fused"),
                                        ("gpt2l_up", "generic"), ("gpt2s_up", "band"),
                                        ("gpt2l_up", "band"), ("gpt2s_up", "fold"),
@@ -190,7 +191,7 @@ def test_bf16_full_size_sampled_rows(name):
                                        ("square_c8_bn32", "fold")])
 def test_bf16_integer_bit_exact(name, algo):
     wl = WORKLOADS[name]
-    wl = wl.with_m(min(wl.M, 300 if algo != "smallm" else 16))
+    wl = wl.with_m(min(wl.M, {"smallm": 16, "gemv": 4}.get(algo, 300)))
     inp = make_inputs(wl, integer=True)
     y = run(wl, inp, device_plan(wl), algo=algo)
     h, s = oracle_plan(wl)
@@ -208,8 +209,55 @@ def test_smallm_parity(name, M):
     p = device_plan(wl)
     y = run(wl, inp, p, algo="smallm")
     check_bf16(wl, inp, y)
-    ya = run(wl, inp, p)  # auto picks the same kernel at M <= 16
-    assert torch.equal(y, ya)
+    if M > 4:
+        ya = run(wl, inp, p)  # auto picks the same kernel for 4 < M <= 16
+        assert torch.equal(y, ya)
+
+
+@pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_down_m1"])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_gemv_parity(name, M):
+    # one, two or four token slots (M = 3: a zero fourth token); 256 threads
+    # per block for Llama gate/up, 896 for down (one 8-column slice each)
+    wl = WORKLOADS[name].with_m(M)
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="gemv")
+    err = check_bf16(wl, inp, y, kernel="gemv")
+    print(f"{name} M={M} gemv err={err:.3e}", flush=True)
+    assert torch.equal(y, run(wl, inp, p))  # auto picks the same kernel at M <= 4
+    assert torch.equal(y, run(wl, inp, p, algo="gemv", use_index=True))
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [
+    (1, 1024, 128, 1, 64, 64),      # c = 1: the dense layer
+    (3, 2400, 64, 2, 40, 32),       # 150 slices: 192 threads, BK = 40
+    (2, 6144, 96, 3, 64, 48),       # c at run time, 48-neuron groups
+    (4, 16384, 64, 4, 64, 16),      # four token slots, 512 threads
+    (1, 1024, 32, 2, 8, 16),        # 64 threads; J = 128, twice the block
+    (1, 32768, 32, 2, 64, 16),      # two slices per thread
+    (2, 65536, 32, 2, 64, 32),      # four slices per thread with two tokens
+    (1, 131072, 16, 2, 64, 16),     # eight slices per thread, J = 2048 (twice the block)
+])
+def test_gemv_shapes(M, K, N, c, BK, BN):
+    wl = Workload("gemv", 9, 4, M, K, N, c, BK, BN, "bf16")
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="gemv")
+    check_bf16(wl, inp, y, kernel="gemv")
+    assert torch.equal(y, run(wl, inp, p, algo="gemv", use_index=True))
+    # integer-valued inputs: every partial sum is an exact integer
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, p, algo="gemv")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.max(np.abs(ref)) < 2 ** 24
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
+    # every output is written
+    yn = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    p.forward(dev(inp.x_bits, "bf16"), dev(inp.w_bits, "bf16"), y=yn, algo="gemv")
+    torch.cuda.synchronize()
+    assert torch.equal(yn, y)
 
 
 @pytest.mark.parametrize("M,K,N,c,BK,BN", [
@@ -227,7 +275,7 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
     inp = make_inputs(wl)
     p = device_plan(wl)
     ys = {}
-    for algo in ("auto", "fused", "smallm", "band", "generic", "fold"):
+    for algo in ("auto", "fused", "smallm", "gemv", "band", "generic", "fold"):
         try:
             ys[algo] = run(wl, inp, p, algo=algo)
         except ss1.SS1Error as e:
