@@ -28,91 +28,24 @@ namespace {
 using namespace dev;
 
 constexpr int kGemvMaxThreads = 1024;
-constexpr int kGemvPlanPerThread = 2;  // plan entries per thread: J <= 2 NT
-
-// Workgroup barrier for LDS only: waits for this wave's LDS accesses, not for
-// its global loads.  (A compiler fence here waits for every load in flight,
-// the weights included.)  The memory clobber keeps the compiler from moving
-// LDS accesses across it.
-__device__ __forceinline__ void gemv_lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Buffer loads with the hardware range check: an offset at or past the
-// descriptor's extent reads zeros and moves no data, so the loads need no
-// branches (a branch around a load makes the compiler wait for it at the join).
-__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
-}
-__device__ __forceinline__ int8_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, voff, 0, 0));
-}
-__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
-}
-constexpr uint32_t kOutOfRange = 0x80000000u;  // past every extent used here
 
 // Eight consecutive weights of one row: 16 bytes of bf16 or 8 of E4M3.
 template <bool W8>
 struct WSlice {
     uint4 v;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t s) { v = buf_load16(r, 16 * s, 0); }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t s) {
+        v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * s, 0, kNonTemporal));
+    }
     __device__ __forceinline__ uint4 bf16() const { return v; }
 };
 template <>
 struct WSlice<true> {
     uint2 v;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t s) { v = buf_load8(r, 8 * s); }
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t s) {
+        v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * s, 0, kNonTemporal));
+    }
     __device__ __forceinline__ uint4 bf16() const { return fp8x8_to_bf16x8(v); }
 };
-
-// Stages the plan of group g (as stage_plan does) from entries that each
-// thread has already read into registers: entry j = tid + p * nt is iv[p],
-// sv[p] (entries at j >= J are ignored).  Ends with a barrier that orders LDS
-// only.
-template <bool FROM_HASH, int PJ>
-__device__ void stage_plan_regs(const int32_t (&iv)[PJ], const int8_t (&sv)[PJ], int J, int Jc, int c, int BK,
-                                uint32_t* s_src, int* s_cnt) {
-    const int tid = threadIdx.x;
-    const int NT = blockDim.x;
-    if (FROM_HASH) {
-        for (int e = tid; e < J; e += NT) s_src[e] = kAbsent;
-        for (int t = tid; t < Jc; t += NT) s_cnt[t] = 0;
-        gemv_lds_barrier();
-#pragma unroll
-        for (int p = 0; p < PJ; ++p) {
-            const int j = tid + p * NT;
-            const int t = iv[p];
-            const int s = sv[p];
-            if (j < J && t >= 0 && t < Jc && (s == 1 || s == -1)) {
-                const int slot = atomicAdd(&s_cnt[t], 1);
-                if (slot < c) s_src[t * c + slot] = make_entry(j, BK, s);
-            }
-        }
-        gemv_lds_barrier();
-        for (int t = tid; t < Jc; t += NT) {
-            uint32_t* p = s_src + t * c;
-            for (int a = 1; a < c; ++a) {  // ascending source chunk; absent entries last
-                const uint32_t v = p[a];
-                int b = a - 1;
-                while (b >= 0 && (p[b] & ~kNeg) > (v & ~kNeg)) {
-                    p[b + 1] = p[b];
-                    --b;
-                }
-                p[b + 1] = v;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int p = 0; p < PJ; ++p) {
-            const int e = tid + p * NT;
-            const int j = iv[p];
-            const int s = sv[p];
-            if (e < J) s_src[e] = (j >= 0 && j < J && (s == 1 || s == -1)) ? make_entry(j, BK, s) : kAbsent;
-        }
-    }
-    gemv_lds_barrier();
-}
 
 // Lane exchange partner^off inside a row of 16 lanes with DPP moves (no LDS
 // round trip): xor 1 and 2 are quad permutes; xor 4 and 8 take the value
@@ -174,7 +107,7 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(const uint16_t* _
     const int NW = NT / 64;
     constexpr int V = R * MT;  // partial sums per thread, value i = r * MT + m
     static_assert((V & (V - 1)) == 0 && V <= 32, "V is a power of two, at most 32");
-    constexpr int PJ = kGemvPlanPerThread;
+    constexpr int PJ = kPlanPerThread;
     extern __shared__ uint32_t smem[];
     float* red = reinterpret_cast<float*>(smem);  // [NW][V]
     uint32_t* s_src = smem + NW * V;
@@ -190,16 +123,9 @@ __global__ __launch_bounds__(kGemvMaxThreads) void gemv_kernel(const uint16_t* _
     const int S8 = Kc >> 3;
 
     // 1. this thread's plan entries
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(pi + static_cast<size_t>(g) * J, static_cast<uint32_t>(J) * 4);
-    const __amdgpu_buffer_rsrc_t srs = make_rsrc(ps + static_cast<size_t>(g) * J, static_cast<uint32_t>(J));
     int32_t iv[PJ];
     int8_t sv[PJ];
-#pragma unroll
-    for (int p = 0; p < PJ; ++p) {
-        const uint32_t j = static_cast<uint32_t>(tid + p * NT);
-        iv[p] = static_cast<int32_t>(buf_load4(prs, 4 * j));
-        sv[p] = buf_load1(srs, j);
-    }
+    fetch_plan_regs<PJ>(pi, ps, g, J, iv, sv);
 
     // 2. all of this thread's weight slices (slices past the row read zeros)
     constexpr int WB = W8 ? 1 : 2;
@@ -337,7 +263,7 @@ inline GemvCfg gemv_config(const ForwardArgs& a) {
     if (MT * Q > 8) return cfg;
     const int64_t per_thread = (s8 + Q - 1) / Q;
     const int NT = static_cast<int>((per_thread + 63) / 64 * 64);
-    if (d.J > static_cast<int64_t>(NT) * kGemvPlanPerThread) return cfg;
+    if (d.J > static_cast<int64_t>(NT) * kPlanPerThread) return cfg;
     int R = std::min((a.w_fp8 ? 16 : 8) / Q, 32 / MT);
     if (R < 1) R = 1;
     if (d.BN % R) return cfg;
