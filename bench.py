@@ -601,10 +601,17 @@ def main():
         }
         return rec, wl
 
+    def sweep_steps(wl):
+        # at least ~2 ms of timed work (the roofline time taken twice), so the
+        # start of the timed region does not weigh on microsecond layers
+        wk = work(wl)
+        t_low = max(wk["compressed_flops"] / PEAK_MFMA_BF16, wk["bytes"] / PEAK_HBM)
+        return max(20, args.steps // 4, min(1000, int(np.ceil(2e-3 / (2 * t_low)))))
+
     if args.sweep:
         with open(args.sweep, "w") as f:
             for name in SWEEP:
-                rec, _ = measure(name, max(20, args.steps // 4), max(5, args.warmup // 4))
+                rec, _ = measure(name, sweep_steps(WORKLOADS[name]), max(5, args.warmup // 4))
                 f.write(json.dumps(rec) + "\n")
                 print(f"sweep {name}: {rec['ms_per_step'] * 1e3:.1f} us, "
                       f"{rec['roofline']['bound']} frac {rec['roofline']['frac']:.3f}",
