@@ -180,7 +180,7 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *   FUSED  : BF16, BK % 32 == 0, BN in {32, 64, 128}
  *   SMALLM : BF16, M <= 16, BK % 32 == 0, BN % 16 == 0
  *   GEMV   : BF16, M <= 4, BN % 16 == 0, 512 <= Kc = K/c <= 65536 (32768
- *            for M = 2, 16384 for M = 3 or 4), and K/BK <= 2 T, where
+ *            for M = 2, 4096 for M = 3 or 4), and K/BK <= 2 T, where
  *            T = 64 ceil(Kc / (512 Q)) threads take Q = 1 (Kc <= 8192), 2, 4
  *            or 8 slices of 8 compressed columns each.  Each block's weight
  *            loads are all issued before it waits for anything.

@@ -328,7 +328,7 @@ def test_select_algo_host():
     assert ss1.select_algo(1, 4096, 14336, 2, 64, 64) == "gemv"
     assert ss1.select_algo(2, 14336, 4096, 2, 64, 64) == "gemv"
     assert ss1.select_algo(4, 4096, 14336, 2, 64, 64) == "gemv"
-    assert ss1.select_algo(4, 14336, 4096, 2, 64, 64) == "gemv"
+    assert ss1.select_algo(4, 14336, 4096, 2, 64, 64) == "smallm"  # 896-thread blocks at 4 token slots
     assert ss1.select_algo(3, 65536, 1024, 2, 64, 64) == "smallm"  # Kc = 32768 > 16384 at 4 token slots
     assert ss1.select_algo(5, 4096, 14336, 2, 64, 64) == "smallm"
     assert ss1.select_algo(16, 14336, 4096, 2, 64, 64) == "smallm"

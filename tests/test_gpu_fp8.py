@@ -96,6 +96,17 @@ def test_forward_fp8w_decode_bn48_and_ragged():
     run_case(wl, 333)
 
 
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [
+    (1, 32768, 32, 2, 64, 16),      # two 8-weight slices per thread, 1024 threads
+    (2, 65536, 32, 2, 64, 32),      # four slices per thread, two tokens
+    (4, 16384, 64, 4, 64, 16),      # four token slots, 512 threads
+    (3, 6144, 96, 3, 64, 48),       # c at run time
+])
+def test_forward_fp8w_matrix_vector(M, K, N, c, BK, BN):
+    assert ss1.select_algo(M, K, N, c, BK, BN, weights="fp8") == "gemv"
+    run_case(Workload("fp8_gemv", 8, 12, M, K, N, c, BK, BN, "bf16"), M)
+
+
 def test_forward_fp8w_fold_shape():
     # a large-M layer that the library runs on the fold kernel (E4M3 weight
     # tile widened to bf16 as it leaves LDS), with a ragged last row tile

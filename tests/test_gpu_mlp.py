@@ -130,6 +130,17 @@ def test_mlp_small_m_and_odd_shapes():
     P.check(to_host(h), to_host(y))
 
 
+def test_mlp_decode_matrix_vector():
+    # M <= 4 with compressed rows of 1024: both layers run the matrix-vector
+    # kernel, the up-projection with GELU in its epilogue
+    for M in (1, 3):
+        P = Pair(0x5e60 + M, M, 2048, 1024, 512, 2, 1, 64, 64, "bf16")
+        assert ss1.select_algo(M, 2048, 1024, 2, 64, 64) == "gemv"
+        assert ss1.select_algo(M, 1024, 512, 1, 64, 64) == "gemv"
+        h, y = P.run()
+        P.check(to_host(h), to_host(y))
+
+
 def test_mlp_float32_tiny():
     P = Pair(0x5e50, 64, 256, 256, 128, 2, 2, 32, 32, "f32")
     h, y = P.run()

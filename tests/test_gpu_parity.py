@@ -214,11 +214,12 @@ def test_smallm_parity(name, M):
         assert torch.equal(y, ya)
 
 
-@pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_down_m1"])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("name,M", [("llama_gateup_m1", 1), ("llama_gateup_m1", 2), ("llama_gateup_m1", 3),
+                                    ("llama_gateup_m1", 4), ("llama_down_m1", 1), ("llama_down_m1", 2)])
 def test_gemv_parity(name, M):
     # one, two or four token slots (M = 3: a zero fourth token); 256 threads
-    # per block for Llama gate/up, 896 for down (one 8-column slice each)
+    # per block for Llama gate/up, 896 for down (one 8-column slice each;
+    # down takes the small-M kernel at four token slots)
     wl = WORKLOADS[name].with_m(M)
     inp = make_inputs(wl)
     p = device_plan(wl)
@@ -233,7 +234,7 @@ def test_gemv_parity(name, M):
     (1, 1024, 128, 1, 64, 64),      # c = 1: the dense layer
     (3, 2400, 64, 2, 40, 32),       # 150 slices: 192 threads, BK = 40
     (2, 6144, 96, 3, 64, 48),       # c at run time, 48-neuron groups
-    (4, 16384, 64, 4, 64, 16),      # four token slots, 512 threads
+    (4, 16384, 64, 4, 64, 16),      # four token slots, 512 threads (the limit for four)
     (1, 1024, 32, 2, 8, 16),        # 64 threads; J = 128, twice the block
     (1, 32768, 32, 2, 64, 16),      # two slices per thread
     (2, 65536, 32, 2, 64, 32),      # four slices per thread with two tokens
