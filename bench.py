@@ -14,8 +14,11 @@ e*(M*K + N*K/c + M*N), whichever bound is the larger lower time), and the CPU
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload gpt2s_up]
-                    [--algo auto] [--index] [--warm] [--no-cpu-baseline]
+                    [--algo auto] [--index] [--warm] [--graph] [--no-cpu-baseline]
                     [--sweep FILE]   # one extra JSON line per workload into FILE
+        # --graph: the timed calls captured in one HIP graph and replayed
+        # (forward and fp8 ops), so no host launch cost falls in the timed
+        # region; the microsecond decode layers otherwise time the host too
     python bench.py --copy-calibration   # a plain 256 MiB device copy, for counters
     python bench.py --op mlp [--mlp-c 4] [--row-chunk 8192]
         # ss1_mlp_forward: the GPT-2 L MLP pair (8192 x 1280 -> 5120 -> 1280,
@@ -173,8 +176,34 @@ def to_dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def time_gpu(wl, steps, warmup, algo, use_index, warm):
-    """Returns (seconds per step, kernel name, number of buffer sets)."""
+def time_graph(fn, steps, warmup):
+    """Seconds per call of fn(i), i < steps, captured in one HIP graph and
+    replayed: the launches cost no host time in the timed region."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(warmup):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def time_gpu(wl, steps, warmup, algo, use_index, warm, graph=False):
+    """Returns (seconds per step, number of buffer sets)."""
     import torch
     import sketched_parameter_sharing_amd as ss1
     from ss1_inputs import make_inputs
@@ -195,6 +224,8 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm):
         k = i % nsets
         plan.forward(xs[k], ws[k], y=ys[k], algo=algo, use_index=use_index)
 
+    if graph:
+        return time_graph(step, steps, warmup), nsets
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -221,7 +252,7 @@ def fp8_work(wl):
             "bytes": 2 * wl.M * wl.K + wl.N * wl.Kc + 4 * wl.N + 2 * wl.M * wl.N + wl.G * wl.J * 5}
 
 
-def time_fp8(wl, steps, warmup, warm):
+def time_fp8(wl, steps, warmup, warm, graph=False):
     """ss1_forward_fp8w over rotating buffer sets: (seconds per call, sets)."""
     import torch
     import sketched_parameter_sharing_amd as ss1
@@ -242,6 +273,8 @@ def time_fp8(wl, steps, warmup, warm):
         k = i % nsets
         ss1.forward_fp8w(xs[k], Qs[k], Ss[k], plan.hash, plan.sign, wl.c, wl.BK, wl.BN, y=ys[k])
 
+    if graph:
+        return time_graph(step, steps, warmup), nsets
     return time_events_i(step, steps, warmup), nsets
 
 
@@ -518,6 +551,9 @@ def main():
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "generic", "band", "fold"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed calls in one HIP graph (forward and fp8 ops): no host launch "
+                         "cost in the timed region, for microsecond decode layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default=None, help="also time every workload, JSON lines into this file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -542,7 +578,7 @@ def main():
 
     def measure(name, steps, warmup):
         wl = WORKLOADS[name]
-        t, nsets = time_gpu(wl, steps, warmup, args.algo, args.index, args.warm)
+        t, nsets = time_gpu(wl, steps, warmup, args.algo, args.index, args.warm, args.graph)
         wk = work(wl)
         rec = {
             "metric": METRIC,
@@ -561,6 +597,7 @@ def main():
                        "BN": wl.BN, "kernel": kernel_name(wl, args.algo),
                        "plan": "inverse index" if args.index else "hash",
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
+                       "launch": "one HIP graph of the timed calls" if args.graph else "eager",
                        "compressed_tflops": wk["compressed_flops"] / t / 1e12,
                        "x_l2_gb": wk["x_l2_bytes"] / 1e9},
         }
@@ -707,8 +744,9 @@ def main():
     if args.op == "fp8":
         name = args.workload or "llama_gateup_m1"
         wl = WORKLOADS[name]
-        t, nsets = time_fp8(wl, args.steps, args.warmup, args.warm)
-        t16, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, args.warm)
+        t, nsets = time_fp8(wl, args.steps, args.warmup, args.warm, args.graph)
+        t16, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, args.warm,
+                          args.graph)
         wk = fp8_work(wl)
         t_f = wk["compressed_flops"] / PEAK_MFMA_BF16
         t_b = wk["bytes"] / PEAK_HBM
@@ -732,6 +770,7 @@ def main():
             "config": {"workload": name + "_fp8w", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c, "BK": wl.BK,
                        "BN": wl.BN, "kernel": fp8_kernel_name(wl),
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
+                       "launch": "one HIP graph of the timed calls" if args.graph else "eager",
                        "bf16_weights_ms": t16 * 1e3, "speedup_vs_bf16_weights": t16 / t},
             "roofline": roof,
         }
