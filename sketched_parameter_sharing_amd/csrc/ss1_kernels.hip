@@ -444,14 +444,15 @@ __global__ __launch_bounds__(256) void fused_kernel(const uint16_t* __restrict__
 }
 
 // ============================================================ small-M kernel
-// Block: NW waves (4, 8 or 16, chosen from S and M), 16 neurons (rows
-// nb*16 .. +15 of group g).  Wave w takes the 32-wide k-steps
-// [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each
-// lane builds 8 sketch values of token (lane % 16) straight from x and loads 8
-// weights of neuron (lane % 16); one 16x16x32 MFMA per step.  Tokens >= M are
-// zero rows.  BK % 32 == 0 keeps a step inside one compressed chunk.  W_c is
-// read coalesced and permuted into the operand pattern across lanes.
-template <int NW, int C_T, bool W8, bool FROM_HASH>
+// Block: NW waves (4, 8 or 16, chosen from S and M), NB column blocks of 16
+// neurons (rows nb*16*NB .. +16*NB-1 of group g).  Wave w takes the 32-wide
+// k-steps [w*S/NW, (w+1)*S/NW) of the S = Kc/32 steps.  Per step each lane
+// builds 8 sketch values of token (lane % 16) straight from x, once for all
+// NB column blocks, and loads 8 weights of neuron (lane % 16) of each; one
+// 16x16x32 MFMA per column block and step.  Tokens >= M are zero rows.
+// BK % 32 == 0 keeps a step inside one compressed chunk.  W_c is read
+// coalesced and permuted into the operand pattern across lanes.
+template <int NW, int C_T, bool W8, bool FROM_HASH, int NB>
 __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ w,
                                                          const int32_t* __restrict__ pi,
@@ -460,12 +461,12 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
                                                          int N, int J, int Jc, int c_rt, int BK,
                                                          int BN, int act, const float* __restrict__ wscale) {
     extern __shared__ uint32_t smem[];
-    f32x4* red = reinterpret_cast<f32x4*>(smem);                  // [NW][64]
-    uint32_t* s_src = smem + NW * 64 * 4;
+    f32x4* red = reinterpret_cast<f32x4*>(smem);                  // [NB][NW][64]
+    uint32_t* s_src = smem + NB * NW * 64 * 4;
     int* s_cnt = reinterpret_cast<int*>(s_src + J);
 
     const int c = (C_T > 0) ? C_T : c_rt;
-    const int nblk = BN / 16;
+    const int nblk = BN / (16 * NB);
     const int g = blockIdx.x / nblk;
     const int nb = blockIdx.x % nblk;
     stage_plan<FROM_HASH>(pi, ps, g, J, Jc, c, BK, s_src, s_cnt);
@@ -483,17 +484,23 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
     const uint16_t* xrow = x + static_cast<size_t>(tok_ok ? tok : 0) * K + kq;
     // W_c is read coalesced (this lane: neuron lane/4 of the block, k-chunk
     // lane%4) and permuted into the MFMA operand pattern before use
-    const int n = g * BN + nb * 16 + (lane >> 2);
+    // (column block b: the next 16 rows, 16 * Kc elements on)
+    const int n = g * BN + nb * 16 * NB + (lane >> 2);
     const size_t wrow = static_cast<size_t>(n) * Kc + (lane & 3) * 8;  // element offset
+    const size_t wblk = static_cast<size_t>(16) * Kc;
     const int perm_src = coalesced_src_lane_bytes(lane);
 
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     constexpr int U = 4;  // steps in flight per wave
     int s = s_begin;
     for (; s + U <= s_end; s += U) {
-        WRaw<W8> wr[U];
+        WRaw<W8> wr[U][NB];
 #pragma unroll
-        for (int u = 0; u < U; ++u) wr[u].load(w, wrow + (s + u) * 32);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) wr[u][b].load(w, wrow + b * wblk + (s + u) * 32);
         uint4 xr[U][(C_T > 0) ? C_T : 1];
         float sg[U][(C_T > 0) ? C_T : 1];
         if constexpr (C_T > 0) {
@@ -529,14 +536,17 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
                 }
             }
             const uint4 ap = pack_bf16x8(a);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, to_operand_layout(wr[u].bf16(), perm_src)),
-                acc, 0, 0, 0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, ap),
+                    __builtin_bit_cast(bf16x8, to_operand_layout(wr[u][b].bf16(), perm_src)), acc[b], 0, 0, 0);
         }
     }
     for (; s < s_end; ++s) {
-        WRaw<W8> wr;
-        wr.load(w, wrow + s * 32);
+        WRaw<W8> wr[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wr[b].load(w, wrow + b * wblk + s * 32);
         const int k0 = s * 32;
         const int t = k0 / BK;
         const int u0 = k0 - t * BK;
@@ -548,23 +558,28 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
             acc_bf16x8(a, raw, entry_sign(e), r == 0);
         }
         const uint4 ap = pack_bf16x8(a);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, to_operand_layout(wr.bf16(), perm_src)), acc,
-            0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, ap), __builtin_bit_cast(bf16x8, to_operand_layout(wr[b].bf16(), perm_src)),
+                acc[b], 0, 0, 0);
     }
 
-    red[wave * 64 + lane] = acc;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) red[(b * NW + wave) * 64 + lane] = acc[b];
     __syncthreads();
-    if (wave == 0) {
-        f32x4 sum = red[lane];
+    // wave b < NB sums column block b over the waves
+    if (wave < NB) {
+        const f32x4* rb = red + wave * NW * 64;
+        f32x4 sum = rb[lane];
         for (int v = 1; v < NW; ++v) {
-            const f32x4 p = red[v * 64 + lane];
+            const f32x4 p = rb[v * 64 + lane];
             sum[0] += p[0];
             sum[1] += p[1];
             sum[2] += p[2];
             sum[3] += p[3];
         }
-        const int col = g * BN + nb * 16 + (lane & 15);
+        const int col = g * BN + (nb * NB + wave) * 16 + (lane & 15);
         const float ws = W8 ? wscale[col] : 1.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -853,6 +868,9 @@ inline ss1_status launch_status() {
     return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
 }
 
+// Small-M column blocks per block where the grid stays large enough (1 or 2).
+constexpr int kSmallmPair = 2;
+
 inline size_t plan_lds_bytes(const Dims& d) {
     return static_cast<size_t>(d.J) * 4 + static_cast<size_t>(d.Jc) * 4;
 }
@@ -930,18 +948,30 @@ ss1_status launch_fused_t(const ForwardArgs& a) {
     return launch_fused_bn<32, W8, FROM_HASH>(a);
 }
 
-template <int NW, int C_T, bool W8, bool FROM_HASH>
-ss1_status launch_smallm_cfg(const ForwardArgs& a) {
+// Column blocks per small-M block: two 16-neuron blocks share each wave's
+// sketch where that still leaves 1.5 blocks per compute unit.
+inline int smallm_nb(const ForwardArgs& a) {
+    return (a.d.BN % 32 == 0 && a.d.N / 32 >= 384) ? kSmallmPair : 1;
+}
+
+template <int NW, int C_T, bool W8, bool FROM_HASH, int NB>
+ss1_status launch_smallm_cfg_nb(const ForwardArgs& a) {
     const Dims& d = a.d;
-    const long long blocks = d.G * (d.BN / 16);
+    const long long blocks = d.G * (d.BN / (16 * NB));
     if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
-    const size_t lds = static_cast<size_t>(NW) * 64 * 16 + plan_lds_bytes(d);
-    hipLaunchKernelGGL((smallm_kernel<NW, C_T, W8, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
+    const size_t lds = static_cast<size_t>(NB) * NW * 64 * 16 + plan_lds_bytes(d);
+    hipLaunchKernelGGL((smallm_kernel<NW, C_T, W8, FROM_HASH, NB>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NW * 64), lds, static_cast<hipStream_t>(a.stream),
                        static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.w),
                        a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M, (int)d.K,
                        (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, d.BN, a.act, a.wscale);
     return launch_status();
+}
+
+template <int NW, int C_T, bool W8, bool FROM_HASH>
+ss1_status launch_smallm_cfg(const ForwardArgs& a) {
+    if (smallm_nb(a) == 2) return launch_smallm_cfg_nb<NW, C_T, W8, FROM_HASH, 2>(a);
+    return launch_smallm_cfg_nb<NW, C_T, W8, FROM_HASH, 1>(a);
 }
 
 // Waves per block: about 16 of the Kc/32 k-steps per wave (measured on the

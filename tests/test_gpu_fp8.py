@@ -114,7 +114,8 @@ def test_forward_fp8w_fold_shape():
     run_case(wl, wl.M, np.r_[0:8, 1999:2007, 3990:4000])
 
 
-@pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_down_m16", "gpt2s_up", "llama_gateup_m4096"])
+@pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_gateup_m16", "llama_down_m16", "gpt2s_up",
+                                  "llama_gateup_m4096"])
 def test_forward_fp8w_full_size(name):
     wl = WORKLOADS[name]
     rows = None if wl.M <= 16 else np.r_[0:4, wl.M // 2:wl.M // 2 + 4, wl.M - 4:wl.M]

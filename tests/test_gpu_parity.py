@@ -214,6 +214,23 @@ def test_smallm_parity(name, M):
         assert torch.equal(y, ya)
 
 
+@pytest.mark.parametrize("M,K,N,BN", [(7, 1024, 12288, 32), (16, 2048, 12288, 128), (3, 4096, 14336, 64)])
+def test_smallm_column_block_pairs(M, K, N, BN):
+    # layers with at least 384 pairs of 16-neuron blocks run two per small-M
+    # block, sharing each wave's sketch (BN = 32: one pair per group; 128: two)
+    wl = Workload("pairs", 9, 5, M, K, N, 2, 32, BN, "bf16")
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="smallm")
+    check_bf16(wl, inp, y)
+    assert torch.equal(y, run(wl, inp, p, algo="smallm", use_index=True))
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, p, algo="smallm")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
+
+
 @pytest.mark.parametrize("name,M", [("llama_gateup_m1", 1), ("llama_gateup_m1", 2), ("llama_gateup_m1", 3),
                                     ("llama_gateup_m1", 4), ("llama_down_m1", 1), ("llama_down_m1", 2)])
 def test_gemv_parity(name, M):
