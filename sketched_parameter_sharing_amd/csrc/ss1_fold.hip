@@ -879,7 +879,8 @@ int max_lds_per_block() { return device_attribute(hipDeviceAttributeMaxSharedMem
 //              divides N and M is small.
 // 32-wide stages (twice the buffers) when BK % 64 != 0, bf16 weights only.
 // Buffer offsets are 32-bit: a tile's rows must span less than 2 GiB.
-inline FoldCfg fold_config(const ForwardArgs& a) {
+// (fold_config below may then trade the 256 x 256 tiles for 192 x 256 ones.)
+inline FoldCfg fold_config_base(const ForwardArgs& a) {
     const Dims& d = a.d;
     const int WB = a.w_fp8 ? 1 : 2;
     if (d.BK % 32 != 0 || (a.w_fp8 && d.BK % 64 != 0)) return FoldCfg{0, 0, 0, 0, 0};
@@ -954,6 +955,32 @@ int64_t fold_main_cols(const ForwardArgs& a, const FoldCfg& cfg) {
     return split < 0.97 * single ? n_main * 256 : d.N;
 }
 
+// The tile the fold launch uses: fold_config_base's, except that 256 x 256
+// tiles become 192 x 256 where that costs less counted in rounds of tiles
+// times tile rows (the 256-row launch with its split, where one applies).  The
+// 192-row tile runs the same 8 waves on 96 x 64 wave tiles.  GPT-2 L down
+// (M = 8192, N = 1280) is the case: 160 tiles of 256 rows leave 96 of 256
+// compute units idle for the whole launch; 215 tiles of 192 rows fill one
+// round at three quarters of the work per tile.
+FoldCfg fold_config(const ForwardArgs& a) {
+    const FoldCfg base = fold_config_base(a);
+    if (!(base.BM == 256 && base.BNB == 256 && base.KS == 64)) return base;
+    const Dims& d = a.d;
+    const double cus = device_attribute(hipDeviceAttributeMultiprocessorCount, 256);
+    const double M = static_cast<double>(a.M);
+    auto rounds = [&](double tiles) { return std::ceil(tiles / cus); };
+    const int64_t main = fold_main_cols(a, base);
+    const double cost256 =
+        256.0 * (main != d.N ? rounds(std::ceil(M / 256) * static_cast<double>(main / 256)) +
+                                   0.55 * rounds(std::ceil(M / 128) * static_cast<double>((d.N - main) / 256))
+                             : rounds(std::ceil(M / 256) * static_cast<double>(d.N / 256)));
+    const double cost192 = 192.0 * rounds(std::ceil(M / 192) * static_cast<double>(d.N / 256));
+    if (!(cost192 < cost256)) return base;
+    const size_t lds = fold_lds(192, 256, 64, base.NSTG, a.w_fp8 ? 1 : 2, d);
+    if (lds > static_cast<size_t>(max_lds_per_block())) return base;
+    return FoldCfg{192, 256, 64, base.NSTG, lds};
+}
+
 template <bool FROM_HASH, bool W8>
 ss1_status launch_fold_t(const ForwardArgs& a) {
     const FoldCfg cfg = fold_config(a);
@@ -961,6 +988,8 @@ ss1_status launch_fold_t(const ForwardArgs& a) {
     constexpr int WB = W8 ? 1 : 2;
     constexpr int NB = W8 ? 3 : 2;       // stages of the 256 x 256 tile
     constexpr int NR = W8 ? 4 : 3;       // stages of the 128 x 256 tile
+    if (cfg.BM == 192 && cfg.BNB == 256 && cfg.KS == 64 && cfg.NSTG == NB)
+        return launch_fold_cfg<192, 256, 2, 4, 64, NB, W8, FROM_HASH>(a, cfg.lds, 0, N);
     if (cfg.BM == 256 && cfg.BNB == 256) {
         if (cfg.KS == 64 && cfg.NSTG == NB) {
             const int64_t main = fold_main_cols(a, cfg);
@@ -1195,7 +1224,9 @@ double fold_estimate_us(const ForwardArgs& a) {
     const double tiles = n_mt * static_cast<double>(a.d.N / cfg.BNB);
     const double rounds = std::ceil(tiles / cus);
     const double area = static_cast<double>(cfg.BM) * cfg.BNB / 65536.0;
-    return rounds * per_round * area * (area < 1.0 ? 1.3 : 1.0);
+    // tiles 128 neurons wide run 4 waves (or 64 x 64 wave tiles), about 1.3x
+    // the time per unit of area of the 8-wave tiles 256 neurons wide
+    return rounds * per_round * area * (cfg.BNB < 256 ? 1.3 : 1.0);
 }
 
 ss1_status launch_fold(const ForwardArgs& a) {

@@ -338,14 +338,31 @@ def test_m0_is_noop_and_y_fully_written():
 
 
 @pytest.mark.parametrize("name,M", [("gpt2s_up", 1), ("gpt2s_up", 77), ("gpt2s_up", 128), ("gpt2s_up", 129),
-                                    ("gpt2l_down", 300), ("square_c2_bn128", 513), ("llama_down_m4096", 40)])
+                                    ("gpt2l_down", 300), ("square_c2_bn128", 513), ("square_c2_bn128", 4000),
+                                    ("llama_down_m4096", 40)])
 def test_fold_tile_shapes(name, M):
-    # 128 x 128 tiles (M <= 128), 256 x 256 tiles with a ragged last row tile,
-    # 128-neuron groups (two per tile), and a 14336-long K
+    # 128 x 128 tiles (M <= 128); 192 x 256 tiles where one round of them holds
+    # the layer, with a ragged last row tile; 256 x 256 tiles with a ragged
+    # last row tile (M = 4000: 256 such tiles, one round, against 336 of 192
+    # rows); 128-neuron groups (two per tile); and a 14336-long K
     wl = WORKLOADS[name].with_m(M)
     inp = make_inputs(wl)
     y = run(wl, inp, device_plan(wl), algo="fold")
     print(f"{name} M={M} fold err={check_bf16(wl, inp, y, kernel='fold'):.3e}", flush=True)
+
+
+def test_fold_192_row_tiles_full_size():
+    # GPT-2 L down (M = 8192, N = 1280): 160 tiles of 256 rows would leave 96
+    # compute units idle, so the fold runs 43 x 5 tiles of 192 rows; the last
+    # row tile holds 128 rows
+    wl = WORKLOADS["gpt2l_down"]
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="fold")
+    rng = np.random.Generator(np.random.PCG64(7))
+    rows = np.unique(np.concatenate([[0, 191, 192, 8063, 8064, wl.M - 1], rng.choice(wl.M, 40, replace=False)]))
+    assert np.isfinite(host(y)).all()
+    err = check_bf16(wl, inp, y, rows, kernel="fold")
+    print(f"gpt2l_down full M fold err={err:.3e}", flush=True)
 
 
 def test_fold_split_launch():
