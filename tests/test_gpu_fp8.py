@@ -115,8 +115,13 @@ def test_forward_fp8w_fold_shape():
 
 
 @pytest.mark.parametrize("name", ["llama_gateup_m1", "llama_gateup_m16", "llama_down_m16", "gpt2s_up",
-                                  "llama_gateup_m4096"])
+                                  "llama_gateup_m4096", "gpt2l_down"])
 def test_forward_fp8w_full_size(name):
+    # gpt2l_down runs the fold on 192-token tiles with E4M3 weights (three
+    # stages); its last row tile holds 128 rows
     wl = WORKLOADS[name]
-    rows = None if wl.M <= 16 else np.r_[0:4, wl.M // 2:wl.M // 2 + 4, wl.M - 4:wl.M]
+    rows = None
+    if wl.M > 16:
+        rows = np.r_[0:4, 191:193, wl.M // 2:wl.M // 2 + 4, 8063:8065, wl.M - 4:wl.M]
+        rows = np.unique(rows[rows < wl.M])
     run_case(wl, wl.M, rows)
