@@ -136,3 +136,23 @@ def test_backward_full_size_sampled():
     z = oracle.sketch(x, hs, ss, K, Ns, c, BK, BN)
     ref = np.concatenate([dy[:, cols[i * BN:(i + 1) * BN]].T @ z[i] for i in range(len(groups))])
     check_close(dw[cols], ref, [mir, ref])
+
+
+def test_backward_full_size_sampled_gpt2l_down():
+    # the combined dW_c + dx fold launch on a c = 4 layer with long rows: 200
+    # dW_c tiles (64 neurons x 128 compressed columns) and 128-token dx tiles
+    wl = WORKLOADS["gpt2l_down"]
+    M, K, N, c, BK, BN = wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN
+    x, w, dy, h, s, dx, dw = run(0x4f00, M, K, N, c, BK, BN)
+    rows = np.r_[0:4, M // 2:M // 2 + 4, M - 4:M]
+    W = oracle.dense_expand(w, h, s, K, N, c, BK, BN)
+    rdx = dy[rows] @ W
+    check_close(dx[rows], rdx, rdx)
+    groups = [0, 9, wl.G - 1]
+    cols = np.concatenate([np.arange(g * BN, (g + 1) * BN) for g in groups])
+    hs, ss = h[groups], s[groups]
+    Ns = len(groups) * BN
+    mir = oracle.backward_dw_mirror(x, dy[:, cols], hs, ss, K, Ns, c, BK, BN)
+    z = oracle.sketch(x, hs, ss, K, Ns, c, BK, BN)
+    ref = np.concatenate([dy[:, cols[i * BN:(i + 1) * BN]].T @ z[i] for i in range(len(groups))])
+    check_close(dw[cols], ref, [mir, ref])
