@@ -1034,8 +1034,11 @@ int dxfold_bm(int64_t M, const Dims& d) {
         const double tiles = std::ceil(static_cast<double>(M) / bm) * static_cast<double>(d.K / 256);
         return tiles / (std::ceil(tiles / cus) * cus);
     };
-    // 64 x 64 wave tiles do about 10% less per cycle than 128 x 64 ones
-    return 0.9 * eff(128) > eff(256) ? 128 : 256;
+    // 128-token tiles (64 x 64 wave tiles, a third LDS stage) only where they
+    // fill the compute units more than 25% better: on GPT-2 L down (2.5 rounds
+    // of 256-token tiles against 5 of 128) the 256-token tiles measured 10%
+    // faster over the whole backward (361 -> 325 us)
+    return 0.8 * eff(128) > eff(256) ? 128 : 256;
 }
 
 size_t dxfold_lds(int BM, const Dims& d) {
