@@ -315,7 +315,10 @@ ss1_status ss1_quantize_fp8(const ss1_tensor* W_c, ss1_tensor* Q, float* scale, 
  * converted to bf16 exactly, the products are accumulated in float32 by the
  * bf16 MFMA, and the row's scale multiplies the float32 sum before the bf16
  * rounding of y.  Halves the weight bytes each call reads, which is what
- * bounds small-M (decode) calls.
+ * bounds small-M (decode) calls.  Kernels: matrix-vector and small-M for
+ * decode shapes; the fold, the band kernel (layers whose input rows fit in
+ * LDS; c in {1, 2, 4, 8}) or the fused kernel otherwise, chosen as for
+ * ss1_forward.
  *   x : [M][K] BF16;  Q : [N][K/c] SS1_FP8_E4M3;  scale : DEVICE float[N];
  *   hash, sign : as ss1_forward;  y : [M][N] BF16, written
  * Requirements: as ss1_forward, plus BK % 32 == 0 and either M <= 16 with

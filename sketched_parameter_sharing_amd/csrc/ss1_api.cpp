@@ -84,17 +84,17 @@ int32_t auto_algo(const ForwardArgs& a) {
     return SS1_ALGO_GENERIC;
 }
 
-// The kernel ss1_forward_fp8w runs (a.w_fp8 set), or -1 when none can:
-// matrix-vector or small-M for decode shapes; otherwise the fold kernel where the time models
-// put it clearly ahead of the fused kernel, which runs fp8 weights (on layers
-// short enough for the band kernel, which has no fp8 form, the fused kernel
-// measured about 1.6x the band kernel's time); else the fused kernel.
+// The kernel ss1_forward_fp8w runs (a.w_fp8 set), or -1 when none can: the
+// same order as ss1_forward's -- matrix-vector or small-M for decode shapes,
+// the fold where the time models put it clearly ahead, else the band kernel
+// where a band of input rows fits in LDS (E4M3 weights with a fixed c), else
+// the fused kernel.
 int32_t fp8_algo(const ForwardArgs& a) {
     if (ss1::gemv_supported(a)) return SS1_ALGO_GEMV;
     if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
     if (!ss1::fused_supported(a)) return -1;
-    const double sketch = sketch_estimate_us(a) * (ss1::band_supported(a, 48) ? 1.6 : 1.0);
-    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch) return SS1_ALGO_FOLD;
+    if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return SS1_ALGO_FOLD;
+    if (ss1::band_supported(a, 48)) return SS1_ALGO_BAND;
     return SS1_ALGO_FUSED;
 }
 
@@ -347,6 +347,7 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     if (algo == SS1_ALGO_GEMV) return ss1::launch_gemv(a);
     if (algo == SS1_ALGO_SMALLM) return ss1::launch_smallm(a);
     if (algo == SS1_ALGO_FOLD) return ss1::launch_fold(a);
+    if (algo == SS1_ALGO_BAND) return ss1::launch_band(a);
     return ss1::launch_fused(a);
 }
 

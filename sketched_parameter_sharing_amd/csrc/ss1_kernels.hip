@@ -604,17 +604,22 @@ __global__ __launch_bounds__(NW * 64) void smallm_kernel(const uint16_t* __restr
 // The MFMA computes the transposed tile y^T = W_c * z^T so that each lane ends
 // up with 4*BN/16 consecutive outputs of one row (W_c rows are loaded in the
 // matching permuted order) and stores them as 16-byte vectors.
-template <int MT, int BN, int C_T, int NW, int RS, int KH, bool RAW_PF, int PD, bool FROM_HASH>
+template <int MT, int BN, int C_T, int NW, int RS, int KH, bool RAW_PF, int PD, bool FROM_HASH, bool W8>
 __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restrict__ x,
                                                        const uint16_t* __restrict__ w,
                                                        const int32_t* __restrict__ pi,
                                                        const int8_t* __restrict__ ps,
                                                        uint16_t* __restrict__ y, int M, int K, int N,
-                                                       int J, int Jc, int c_rt, int BK, int gsplit, int act) {
+                                                       int J, int Jc, int c_rt, int BK, int gsplit, int act,
+                                                       const float* __restrict__ wscale) {
     constexpr int RB = MT / 16;  // 16-row blocks of the band
     constexpr int NB = BN / 16;  // 16-neuron blocks of a group
     static_assert(RB * 16 == MT && NB * 16 == BN && NB % 2 == 0, "tile sizes");
     static_assert(KH == 1 || (KH == 2 && C_T > 0), "a step is 32*KH wide; 64 needs a fixed c");
+    static_assert(!W8 || C_T > 0, "E4M3 weights with a fixed c");
+    // weights: bf16, or E4M3 codes (one byte each) with one float32 scale per row
+    constexpr int WB = W8 ? 1 : 2;
+    using WV = typename std::conditional<W8, uint2, uint4>::type;
     // RS waves share a group, each taking RBW of the band's row blocks; NG
     // groups are in progress at a time
     constexpr int RBW = RB / RS;
@@ -679,9 +684,10 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int r = lane >> 2;
-        woff[nb] = static_cast<uint32_t>(((r >> 2) * 4 * NB + nb * 4 + (r & 3)) * Kc + (lane & 3) * 8) * 2u;
+        woff[nb] = static_cast<uint32_t>(((r >> 2) * 4 * NB + nb * 4 + (r & 3)) * Kc + (lane & 3) * 8) * WB;
     }
-    const uint32_t wslice_bytes = static_cast<uint32_t>(BN * Kc * 2);
+    const uint32_t wslice_bytes = static_cast<uint32_t>(BN * Kc * WB);
+    const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(w);
     const int perm_src = coalesced_src_lane_bytes(lane);
     const uint16_t* lrow = band + (rb0 * 16 + li) * LDK + q * 8;  // this lane's band row (first block), k offset
 
@@ -692,6 +698,13 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
             const int m = m0 + (rb0 + rb) * 16 + li;
             if (m >= M) continue;
             uint16_t* yr = y + static_cast<size_t>(m) * N + static_cast<size_t>(g) * BN + q * 4 * NB;
+            if constexpr (W8) {  // the rows' E4M3 scales (neuron g*BN + q*4*NB + nb*4 + i)
+                const float* sc = wscale + static_cast<size_t>(g) * BN + q * 4 * NB;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[rb][nb][i] *= sc[nb * 4 + i];
+            }
 #pragma unroll
             for (int h = 0; h < NB / 2; ++h) {
                 uint4 o;
@@ -729,7 +742,7 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
         // reads are prefetched too; otherwise they are issued at the start of
         // the step, ahead of the operand permutes.
         struct Stage {
-            uint4 wf[KH][NB];
+            WV wf[KH][NB];
             float sg[CR];
             uint32_t sx[CR];
             uint32_t off[CR];
@@ -759,11 +772,18 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
             const int t = k0 / BK;
             const int ub = k0 - t * BK;
             // both 32-wide halves of a row's 128-byte line are requested back to back
-            const auto wr = make_rsrc(w + static_cast<size_t>(g0 + gl) * BN * Kc, wslice_bytes);
+            const auto wr = make_rsrc(wbytes + static_cast<size_t>(g0 + gl) * BN * Kc * WB, wslice_bytes);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int h = 0; h < KH; ++h) st.wf[h][nb] = buf_load16(wr, woff[nb], (k0 + 32 * h) * 2);
+                for (int h = 0; h < KH; ++h) {
+                    if constexpr (W8) {
+                        st.wf[h][nb] = __builtin_bit_cast(
+                            uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, woff[nb], (k0 + 32 * h) * WB, 0));
+                    } else {
+                        st.wf[h][nb] = buf_load16(wr, woff[nb], (k0 + 32 * h) * 2);
+                    }
+                }
 #pragma unroll
             for (int r = 0; r < C_T; ++r) {
                 const uint32_t e = __builtin_amdgcn_readfirstlane(plan[t * C_T + r]);
@@ -783,7 +803,13 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
             for (int h = 0; h < KH; ++h) {
                 uint4 wop[NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) wop[nb] = to_operand_layout(st.wf[h][nb], perm_src);
+                for (int nb = 0; nb < NB; ++nb) {
+                    if constexpr (W8) {
+                        wop[nb] = to_operand_layout(fp8x8_to_bf16x8(st.wf[h][nb]), perm_src);
+                    } else {
+                        wop[nb] = to_operand_layout(st.wf[h][nb], perm_src);
+                    }
+                }
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb) {
                     float a[8];
@@ -1060,7 +1086,7 @@ inline BandCfg band_config(const Dims& d, int64_t M, const DeviceInfo& di) {
 // four waves per SIMD measured slower: the kernel is not latency-starved.)
 enum class BandShape { BASE, WIDE };
 
-template <int MT, int BN, int C_T, BandShape SH, bool FROM_HASH>
+template <int MT, int BN, int C_T, BandShape SH, bool FROM_HASH, bool W8>
 ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
     const Dims& d = a.d;
     constexpr int NW = (BN == 128 || C_T >= 8 || (C_T == 4 && MT == 64)) ? 4 : 8;
@@ -1069,49 +1095,51 @@ ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
     constexpr bool RAW_PF = KH == 1 && C_T <= 4 && BN < 128;
     constexpr int PD = 2;
     const long long nbands = (a.M + MT - 1) / MT;
-    auto kern = &band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH>;
+    auto kern = &band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH, W8>;
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(cfg.lds)) != hipSuccess)
         return SS1_ERR_HIP;
-    hipLaunchKernelGGL((band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH>),
+    hipLaunchKernelGGL((band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH, W8>),
                        dim3(static_cast<unsigned>(nbands * cfg.gsplit)), dim3(NW * 64), cfg.lds,
                        static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
-                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, cfg.gsplit, a.act);
+                       (int)a.M, (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.c, d.BK, cfg.gsplit, a.act, a.wscale);
     return launch_status();
 }
 
-template <int MT, int BN, bool FROM_HASH>
+template <int MT, int BN, bool FROM_HASH, bool W8>
 ss1_status launch_band_c(const ForwardArgs& a, const BandCfg& cfg) {
     const bool wide = a.d.BK % 64 == 0;
     switch (a.d.c) {
-        case 1: return wide ? launch_band_cfg<MT, BN, 1, BandShape::WIDE, FROM_HASH>(a, cfg)
-                            : launch_band_cfg<MT, BN, 1, BandShape::BASE, FROM_HASH>(a, cfg);
-        case 2: return wide ? launch_band_cfg<MT, BN, 2, BandShape::WIDE, FROM_HASH>(a, cfg)
-                            : launch_band_cfg<MT, BN, 2, BandShape::BASE, FROM_HASH>(a, cfg);
-        case 4: return launch_band_cfg<MT, BN, 4, BandShape::BASE, FROM_HASH>(a, cfg);
-        case 8: return launch_band_cfg<MT, BN, 8, BandShape::BASE, FROM_HASH>(a, cfg);
-        default: return launch_band_cfg<MT, BN, 0, BandShape::BASE, FROM_HASH>(a, cfg);
+        case 1: return wide ? launch_band_cfg<MT, BN, 1, BandShape::WIDE, FROM_HASH, W8>(a, cfg)
+                            : launch_band_cfg<MT, BN, 1, BandShape::BASE, FROM_HASH, W8>(a, cfg);
+        case 2: return wide ? launch_band_cfg<MT, BN, 2, BandShape::WIDE, FROM_HASH, W8>(a, cfg)
+                            : launch_band_cfg<MT, BN, 2, BandShape::BASE, FROM_HASH, W8>(a, cfg);
+        case 4: return launch_band_cfg<MT, BN, 4, BandShape::BASE, FROM_HASH, W8>(a, cfg);
+        case 8: return launch_band_cfg<MT, BN, 8, BandShape::BASE, FROM_HASH, W8>(a, cfg);
+        default:
+            if constexpr (W8) return SS1_ERR_ALGO;  // E4M3 weights need a fixed c
+            else return launch_band_cfg<MT, BN, 0, BandShape::BASE, FROM_HASH, false>(a, cfg);
     }
 }
 
-template <int MT, bool FROM_HASH>
+template <int MT, bool FROM_HASH, bool W8>
 ss1_status launch_band_bn(const ForwardArgs& a, const BandCfg& cfg) {
     switch (a.d.BN) {
-        case 32: return launch_band_c<MT, 32, FROM_HASH>(a, cfg);
-        case 64: return launch_band_c<MT, 64, FROM_HASH>(a, cfg);
-        case 128: return launch_band_c<MT, 128, FROM_HASH>(a, cfg);
+        case 32: return launch_band_c<MT, 32, FROM_HASH, W8>(a, cfg);
+        case 64: return launch_band_c<MT, 64, FROM_HASH, W8>(a, cfg);
+        case 128: return launch_band_c<MT, 128, FROM_HASH, W8>(a, cfg);
         default: return SS1_ERR_ALGO;
     }
 }
 
-template <bool FROM_HASH>
+template <bool FROM_HASH, bool W8>
 ss1_status launch_band_t(const ForwardArgs& a) {
     const BandCfg cfg = band_config(a.d, a.M, device_info());
     switch (cfg.MT) {
-        case 64: return launch_band_bn<64, FROM_HASH>(a, cfg);
-        case 48: return launch_band_bn<48, FROM_HASH>(a, cfg);
-        case 32: return launch_band_bn<32, FROM_HASH>(a, cfg);
+        case 64: return launch_band_bn<64, FROM_HASH, W8>(a, cfg);
+        case 48: return launch_band_bn<48, FROM_HASH, W8>(a, cfg);
+        case 32: return launch_band_bn<32, FROM_HASH, W8>(a, cfg);
         default: return SS1_ERR_ALGO;
     }
 }
@@ -1121,12 +1149,16 @@ ss1_status launch_band_t(const ForwardArgs& a) {
 bool band_supported(const ForwardArgs& a, int min_rows) {
     if (!(a.dtype == SS1_BF16 && a.d.BK % 32 == 0 && (a.d.BN == 32 || a.d.BN == 64 || a.d.BN == 128)))
         return false;
+    // E4M3 weights: the forward hash and a fixed c only
+    if (a.w_fp8 && !(a.form == PlanForm::Hash && (a.d.c == 1 || a.d.c == 2 || a.d.c == 4 || a.d.c == 8)))
+        return false;
     const BandCfg cfg = band_config(a.d, a.M > 0 ? a.M : 1, device_info());
     return cfg.MT >= min_rows;
 }
 
 ss1_status launch_band(const ForwardArgs& a) {
-    return a.form == PlanForm::Hash ? launch_band_t<true>(a) : launch_band_t<false>(a);
+    if (a.w_fp8) return a.form == PlanForm::Hash ? launch_band_t<true, true>(a) : SS1_ERR_ALGO;
+    return a.form == PlanForm::Hash ? launch_band_t<true, false>(a) : launch_band_t<false, false>(a);
 }
 
 bool fused_supported(const ForwardArgs& a) {
