@@ -612,3 +612,103 @@ def test_backward_dw_mirror_rounds_only_the_sketch():
     Wc = np.zeros((N, K // c))
     _, dWc = oracle.backward(x, Wc, dy, h, s, K, N, c, BK, BN)
     assert np.array_equal(oracle.backward_dw_mirror(x, dy, h, s, K, N, c, BK, BN), dWc)
+
+
+# --------------------------------------------------- pins of forward_mirror
+# forward_mirror is the elementwise bar of the device parity tests for the
+# kernels that round the sketch to bf16, so it is pinned here against code
+# that shares nothing with it: torch CPU matmuls of the Kronecker (CountSketch
+# matrix) form, and torch's own float32 -> bf16 conversion (nearest, ties to
+# even) in place of the oracle's frexp/ldexp rounding.
+
+def _torch_mirror(x32, Wc, h, s, K, N, c, BK, BN, group_shift=0):
+    """y from the bf16-rounded float32 sketch, built with torch: z_g is x times
+    the transposed Kronecker matrix (S_g kron I_BK) in float32 -- for c = 2
+    every output sums exactly two signed inputs, so any summation order gives
+    the one rounding of that pair -- then rounded by torch's bf16 conversion
+    and contracted in float64.  ``group_shift`` pairs group g's sketch with
+    group g + shift's weight rows (a planted slip)."""
+    torch = pytest.importorskip("torch")
+    d = oracle.dims(K, N, c, BK, BN)
+    J, Jc, G = d["J"], d["Jc"], d["G"]
+    xt = torch.from_numpy(np.asarray(x32, dtype=np.float32))
+    W = torch.from_numpy(np.asarray(Wc, dtype=np.float64))
+    y = torch.empty((xt.shape[0], N), dtype=torch.float64)
+    eye = torch.eye(BK, dtype=torch.float32)
+    for g in range(G):
+        S = torch.zeros((Jc, J), dtype=torch.float32)
+        S[torch.from_numpy(h[g].astype(np.int64)), torch.arange(J)] = torch.from_numpy(s[g].astype(np.float32))
+        z = (xt @ torch.kron(S, eye).T).to(torch.bfloat16).to(torch.float64)
+        gw = (g + group_shift) % G
+        y[:, g * BN:(g + 1) * BN] = z @ W[gw * BN:(gw + 1) * BN].T
+    return y.numpy()
+
+
+def test_forward_mirror_integer_inputs_equal_forward_bit_exact():
+    # integer inputs in {-4..4}: each sketch value is an integer of magnitude
+    # at most 4c, exact in bf16, so the rounded mirror is the definition itself
+    for K, N, c, BK, BN in [(256, 64, 2, 32, 32), (384, 48, 3, 16, 16), (512, 32, 4, 64, 8)]:
+        h, s = oracle.plan(41 + c, K, N, c, BK, BN)
+        g = np.random.default_rng(42 + c)
+        x = g.integers(-4, 5, (9, K)).astype(np.float64)
+        Wc = g.integers(-4, 5, (N, K // c)).astype(np.float64)
+        ref = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+        for rounded in (True, False):
+            assert np.array_equal(oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, rounded), ref)
+
+
+def test_forward_mirror_c2_matches_torch_kronecker_form():
+    M, K, N, c, BK, BN = 33, 512, 96, 2, 32, 32
+    h, s = oracle.plan(43, K, N, c, BK, BN)
+    x = bf16_bits_to_f32(f32_to_bf16_bits(draw("normal", 44, (M, K))))
+    Wc = bf16_bits_to_f32(f32_to_bf16_bits(draw("normal002", 45, (N, K // c)))).astype(np.float64)
+    mir = oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, True)
+    ref = _torch_mirror(x, Wc, h, s, K, N, c, BK, BN)
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(mir - ref)) <= 1e-12 * scale
+    # the rounding of the sketch is visible at this size: the unrounded mirror
+    # and the exact forward differ from the rounded one by far more than 1e-12
+    unr = oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, False)
+    assert np.max(np.abs(unr - ref)) > 1e-6 * scale
+    assert np.array_equal(unr, oracle.forward(x, Wc, h, s, K, N, c, BK, BN))  # exact pair sums
+
+
+def test_forward_mirror_pin_catches_a_wrong_group():
+    # a planted slip on the reference side (group g's sketch against group
+    # g+1's weight rows) must fail the same 1e-12 comparison by a wide margin
+    M, K, N, c, BK, BN = 17, 256, 64, 2, 32, 32
+    h, s = oracle.plan(46, K, N, c, BK, BN)
+    x = bf16_bits_to_f32(f32_to_bf16_bits(draw("normal", 47, (M, K))))
+    Wc = draw("normal002", 48, (N, K // c)).astype(np.float64)
+    mir = oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, True)
+    bad = _torch_mirror(x, Wc, h, s, K, N, c, BK, BN, group_shift=1)
+    assert np.max(np.abs(mir - bad)) > 1e-2 * np.max(np.abs(mir))
+
+
+def test_forward_mirror_c4_ascending_float32_sum():
+    # c = 4: the float32 sum depends on the order; the mirror adds the
+    # sources of each compressed chunk in ascending chunk order.  Rebuilt here
+    # from the inverse index with torch float32 adds and torch's bf16 rounding.
+    torch = pytest.importorskip("torch")
+    M, K, N, c, BK, BN = 11, 1024, 32, 4, 32, 16
+    h, s = oracle.plan(49, K, N, c, BK, BN)
+    idx, isg = oracle.plan_index(h, s, K, N, c, BK, BN)
+    d = oracle.dims(K, N, c, BK, BN)
+    x = bf16_bits_to_f32(f32_to_bf16_bits(draw("normal", 50, (M, K))))
+    Wc = draw("normal002", 51, (N, K // c)).astype(np.float64)
+    xt = torch.from_numpy(x)
+    ref = np.empty((M, N))
+    for g in range(d["G"]):
+        parts = []
+        for t in range(d["Jc"]):
+            acc = None
+            for r in range(c):
+                j = int(idx[g, t, r])
+                assert r == 0 or j > int(idx[g, t, r - 1])
+                term = float(isg[g, t, r]) * xt[:, j * BK:(j + 1) * BK]
+                acc = term if acc is None else acc + term
+            parts.append(acc.to(torch.bfloat16).to(torch.float64))
+        z = torch.cat(parts, dim=1).numpy()
+        ref[:, g * BN:(g + 1) * BN] = z @ Wc[g * BN:(g + 1) * BN].T
+    mir = oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, True)
+    assert np.max(np.abs(mir - ref)) <= 1e-12 * np.max(np.abs(ref))
