@@ -130,7 +130,8 @@ ss1_status ss1_plan(uint64_t seed, int64_t K, int64_t N, int32_t c, int32_t BK, 
 /*
  * ss1_plan_index -- HOST.  Validates a plan (0 <= hash < Jc, sign = +-1, and
  * exactly c input chunks per compressed chunk in every group) and writes its
- * inverse: idx[g][t][0..c-1] are the input chunks of compressed chunk t of
+ * inverse -- for each compressed chunk, the input chunks the sketch of the
+ * SS1 summary page ("Approach") adds into it, with their signs: idx[g][t][0..c-1] are the input chunks of compressed chunk t of
  * group g in ascending order, isign[g][t][r] = sign[g][idx[g][t][r]].
  * Inputs hash[G*J], sign[G*J]; outputs idx[G*Jc*c], isign[G*Jc*c]; all host,
  * caller-owned.  Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_PLAN (outputs are
@@ -195,6 +196,12 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  * ss1_forward picks GEMV for M <= 4 where it applies, else SMALLM for
  * M <= 16, and FOLD for large M where its modelled time is below the sketch
  * kernels' (ss1_select_algo reports the choice).
+ * Reproducibility: a row of y depends only on that row of x, but its bits
+ * depend on the kernel that runs, and the choice depends on M (and on the
+ * device's compute-unit count and LDS size).  Calls with the same M on the
+ * same device give identical bits; the same row in calls of different M may
+ * differ within the documented rounding (the fold rounds no sketch, the
+ * sketch kernels do, and the small-M kernels sum k in another order).
  */
 ss1_status ss1_forward_algo(const ss1_tensor* x, const ss1_tensor* W_c,
                             const int32_t* hash, const int8_t* sign,
@@ -280,6 +287,9 @@ ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* s
  * Requirements: each layer as for ss1_forward (chunking, alignment of x, h, y
  * and both W_c to 16 bytes, hash 4-byte aligned, balanced plans); x, h and y
  * must not overlap.  M == 0 enqueues nothing.
+ * Reproducibility: each chunk's projections run the kernels ss1_forward would
+ * pick for that chunk's row count, so y is bit-reproducible for a fixed M and
+ * R; another R can change the kernels (ss1_forward's note).
  * Errors: SS1_ERR_NULL, SS1_ERR_SHAPE, SS1_ERR_DTYPE, SS1_ERR_ALIGN (every
  * check runs for both layers before any HIP call), SS1_ERR_HIP.
  */
@@ -355,6 +365,22 @@ ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c,
                         int32_t c, int32_t BK, int32_t BN,
                         const ss1_tensor* dy, ss1_tensor* dx, ss1_tensor* dW_c,
                         void* stream);
+
+/*
+ * ss1_backward_select_algo -- HOST.  The kernels ss1_backward runs for these
+ * descriptors (only dtypes and sizes are read; data may be NULL):
+ *   *dw_algo = SS1_ALGO_FOLD  : dW_c contracted over (token, source) with no
+ *                               sketch formed -- the exact sum, rounded once
+ *              SS1_ALGO_FUSED : dW_c from the group's sketch rounded to bf16
+ *                               (as the forward's sketch kernels form it)
+ *   *dx_algo = SS1_ALGO_FOLD or SS1_ALGO_GENERIC (tiled dx kernels); neither
+ *              forms a sketch, both round only dx itself.
+ * For M == 0 it reports what a non-empty call of the same layer would use.
+ * May query the current HIP device's properties (LDS size).
+ * Errors: as the shape and dtype checks of ss1_backward.
+ */
+ss1_status ss1_backward_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
+                                    int32_t BN, int32_t* dx_algo, int32_t* dw_algo);
 
 #ifdef __cplusplus
 }

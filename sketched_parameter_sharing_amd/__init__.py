@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     SS1Error,
     backward,
+    backward_select_algo,
     forward,
     forward_fp8w,
     forward_idx,

@@ -29,7 +29,7 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
            "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w",
-           "ss1_backward")
+           "ss1_backward", "ss1_backward_select_algo")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -95,6 +95,8 @@ def load():
     lib.ss1_backward.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, tp, tp, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
+    lib.ss1_backward_select_algo.restype = i32
+    lib.ss1_backward_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     _LIB = lib
     return lib
 
@@ -176,11 +178,44 @@ def _check_device(*ts):
             raise ValueError("device entry points take GPU tensors")
 
 
+def _check_vec(t, dtype, numel: int, what: str):
+    """A device array the C ABI reads by pointer alone (a plan array, a row
+    scale): it must have the element type the kernels read, be contiguous and
+    hold exactly ``numel`` elements, since the library cannot see its size."""
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what} must hold {numel} elements, got {t.numel()}")
+
+
+def _plan_sizes(K: int, N: int, c: int, BK: int, BN: int):
+    """(G*J, G*Jc*c) for a layer, or None when the chunking does not divide
+    (the library then reports the shape error itself)."""
+    if min(K, N, c, BK, BN) <= 0 or K % BK or N % BN or (K // BK) % c:
+        return None
+    G, J = N // BN, K // BK
+    return G * J, G * (J // c) * c
+
+
+def _check_plan(hash_, sign, K: int, N: int, c: int, BK: int, BN: int, index: bool = False):
+    import torch
+    n = _plan_sizes(K, N, c, BK, BN)
+    if n is None:
+        return
+    numel = n[1] if index else n[0]
+    names = ("idx", "isign") if index else ("hash", "sign")
+    _check_vec(hash_, torch.int32, numel, names[0])
+    _check_vec(sign, torch.int8, numel, names[1])
+
+
 def forward(x, W_c, hash_, sign, c: int, BK: int, BN: int, y=None, algo: str = "auto", stream=None):
     """y = SS1(x) on the GPU (ss1_forward / ss1_forward_algo).  ``hash_`` and
     ``sign`` are device tensors (int32 / int8) of shape [G][J]."""
     import torch
     _check_device(x, W_c, hash_, sign)
+    _check_plan(hash_, sign, x.shape[-1], W_c.shape[0], c, BK, BN)
     if y is None:
         y = torch.empty((x.shape[0], W_c.shape[0]), dtype=x.dtype, device=x.device)
     dx, dw, dy = _desc(x), _desc(W_c), _desc(y)
@@ -200,6 +235,7 @@ def forward_idx(x, W_c, idx, isign, c: int, BK: int, BN: int, y=None, algo: str 
     tensors [G][Jc][c]) instead of the forward hash."""
     import torch
     _check_device(x, W_c, idx, isign)
+    _check_plan(idx, isign, x.shape[-1], W_c.shape[0], c, BK, BN, index=True)
     if y is None:
         y = torch.empty((x.shape[0], W_c.shape[0]), dtype=x.dtype, device=x.device)
     dx, dw, dy = _desc(x), _desc(W_c), _desc(y)
@@ -223,6 +259,8 @@ def mlp_forward(x, up, down, h=None, y=None, row_chunk: int | None = None, strea
     Wu, hu, su, cu, BKu, BNu = up
     Wd, hd, sd, cd, BKd, BNd = down
     _check_device(x, Wu, hu, su, Wd, hd, sd)
+    _check_plan(hu, su, x.shape[-1], Wu.shape[0], cu, BKu, BNu)
+    _check_plan(hd, sd, Wu.shape[0], Wd.shape[0], cd, BKd, BNd)
     M = x.shape[0]
     if h is None:
         R = max(1, min(M, row_chunk or M))
@@ -247,6 +285,8 @@ def quantize_fp8(W_c, Q=None, scale=None, stream=None):
         Q = torch.empty(W_c.shape, dtype=torch.uint8, device=W_c.device)
     if scale is None:
         scale = torch.empty((W_c.shape[0],), dtype=torch.float32, device=W_c.device)
+    _check_device(Q, scale)
+    _check_vec(scale, torch.float32, W_c.shape[0], "scale")
     dw, dq = _desc(W_c), _desc(Q)
     st = load().ss1_quantize_fp8(ctypes.byref(dw), ctypes.byref(dq), scale.data_ptr(), _stream(stream))
     _check(st, "ss1_quantize_fp8")
@@ -257,6 +297,8 @@ def forward_fp8w(x, Q, scale, hash_, sign, c: int, BK: int, BN: int, y=None, str
     """y = SS1(x) with fp8 compressed weights on the GPU (ss1_forward_fp8w)."""
     import torch
     _check_device(x, Q, scale, hash_, sign)
+    _check_plan(hash_, sign, x.shape[-1], Q.shape[0], c, BK, BN)
+    _check_vec(scale, torch.float32, Q.shape[0], "scale")
     if y is None:
         y = torch.empty((x.shape[0], Q.shape[0]), dtype=x.dtype, device=x.device)
     dx, dq, dy = _desc(x), _desc(Q), _desc(y)
@@ -271,6 +313,7 @@ def backward(x, W_c, hash_, sign, c: int, BK: int, BN: int, dy, dx=True, dW_c=Tr
     (dx, dW_c); pass dx=None or dW_c=None to skip one, True to allocate it."""
     import torch
     _check_device(x, W_c, hash_, sign, dy)
+    _check_plan(hash_, sign, x.shape[-1], W_c.shape[0], c, BK, BN)
     if dx is True:
         dx = torch.empty_like(x)
     if dW_c is True:
@@ -299,11 +342,25 @@ def select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: str = "
     return ALGO_NAMES[out.value]
 
 
+def backward_select_algo(M: int, K: int, N: int, c: int, BK: int, BN: int):
+    """Kernels ss1_backward runs for this layer (bf16): a pair of names
+    (dx kernel, dW_c kernel).  "fold" forms no sketch; a dW_c kernel named
+    "fused" contracts the sketch rounded to bf16; a dx kernel named "generic"
+    is a tiled kernel that forms no sketch either."""
+    x = Tensor(None, BF16, 0, M, K)
+    w = Tensor(None, BF16, 0, N, K // c if c > 0 else 0)
+    a, b = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    _check(load().ss1_backward_select_algo(ctypes.byref(x), ctypes.byref(w), c, BK, BN, ctypes.byref(a),
+                                           ctypes.byref(b)), "ss1_backward_select_algo")
+    return ALGO_NAMES[a.value], ALGO_NAMES[b.value]
+
+
 def sketch(x, hash_, sign, c: int, BK: int, BN: int, N: int, z=None, out_dtype=None, stream=None):
     """Standalone sketch on the GPU (ss1_sketch): returns z as a [G*M][K/c]
     tensor (float32 by default, or ``out_dtype``)."""
     import torch
     _check_device(x, hash_, sign)
+    _check_plan(hash_, sign, x.shape[-1], N, c, BK, BN)
     G = N // BN
     if z is None:
         z = torch.empty((G * x.shape[0], x.shape[1] // c), dtype=out_dtype or torch.float32, device=x.device)
@@ -319,6 +376,7 @@ def project(W, hash_, sign, c: int, BK: int, BN: int, W_c=None, stream=None):
     pattern on the GPU (ss1_project): returns W_c, [N][K/c], W's dtype."""
     import torch
     _check_device(W, hash_, sign)
+    _check_plan(hash_, sign, W.shape[-1], W.shape[0], c, BK, BN)
     if W_c is None:
         W_c = torch.empty((W.shape[0], W.shape[1] // c), dtype=W.dtype, device=W.device)
     dw, dc = _desc(W), _desc(W_c)

@@ -45,14 +45,27 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".cpp", ".hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libss1.so; returns its path."""
+def _stale(src: str, obj: str) -> bool:
+    """An object is stale when it is missing or older than its source or any
+    header beside the sources (every source includes some of them)."""
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (only stale objects with ``incremental``) and
+    link libss1.so; returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        if incremental and not _stale(src, obj):
+            return obj
         cmd = [hipcc, *COMMON, *EXTRA.get(os.path.basename(src), []), f"--offload-arch={ARCH}", "-c", src,
                "-o", obj]
         if src.endswith(".cpp"):
@@ -81,4 +94,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

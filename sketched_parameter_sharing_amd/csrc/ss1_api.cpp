@@ -354,6 +354,31 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     return ss1::launch_fused(a);
 }
 
+extern "C" ss1_status ss1_backward_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c,
+                                               int32_t BK, int32_t BN, int32_t* dx_algo, int32_t* dw_algo) {
+    if (!x || !W_c || !dx_algo || !dw_algo) return SS1_ERR_NULL;
+    // the shape and dtype checks of ss1_backward on stand-in buffers
+    static char dummy[16] __attribute__((aligned(16)));
+    static const int32_t plan_i = 0;
+    static const int8_t plan_s = 0;
+    ss1_tensor xs = *x, ws = *W_c;
+    if (!xs.data) xs.data = dummy;
+    if (!ws.data) ws.data = dummy;
+    ss1_tensor dy{xs.data, xs.dtype, 0, xs.rows, ws.rows};
+    ForwardArgs a;
+    ss1_status st = check_forward(&xs, &ws, &plan_i, &plan_s, c, BK, BN, &dy, PlanForm::Hash, nullptr, &a);
+    if (st != SS1_OK) return st;
+    if (xs.dtype != SS1_BF16) return SS1_ERR_DTYPE;
+    if (BK % 32 != 0 || BN % 32 != 0) return SS1_ERR_SHAPE;
+    if (a.d.G > 8192) return SS1_ERR_SHAPE;
+    // the choice ss1_backward makes: dW_c on the fold kernel (no sketch) when
+    // its shape rules hold, else on the sketch kernel; dx on the fold kernel
+    // when its rules hold, else on the tiled dx kernels (no sketch either way)
+    *dw_algo = ss1::dw_fold_supported(a.M, a.d) ? SS1_ALGO_FOLD : SS1_ALGO_FUSED;
+    *dx_algo = ss1::dx_fold_supported(a.M, a.d) ? SS1_ALGO_FOLD : SS1_ALGO_GENERIC;
+    return SS1_OK;
+}
+
 extern "C" ss1_status ss1_backward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash,
                                    const int8_t* sign, int32_t c, int32_t BK, int32_t BN, const ss1_tensor* dy,
                                    ss1_tensor* dx, ss1_tensor* dW_c, void* stream) {

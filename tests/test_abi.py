@@ -353,3 +353,46 @@ def test_select_algo_host():
     out = ctypes.c_int32(0)
     assert lib.ss1_select_algo(None, ctypes.byref(T(1, 1)), 2, 64, 64, ctypes.byref(out)) == _lib.ERR_NULL
     assert lib.ss1_select_algo(ctypes.byref(T(8, 256)), ctypes.byref(T(64, 128)), 2, 64, 64, None) == _lib.ERR_NULL
+
+
+def test_backward_select_algo_host():
+    # the kernels ss1_backward reports; its checks are ss1_backward's own
+    dx_k, dw_k = ss1.backward_select_algo(300, 768, 192, 2, 64, 64)
+    assert dx_k in ("fold", "generic") and dw_k in ("fold", "fused")
+    with pytest.raises(ss1.SS1Error) as e:
+        ss1.backward_select_algo(96, 480, 128, 2, 48, 64)       # BK % 32
+    assert e.value.status == _lib.ERR_SHAPE
+    lib = _lib.load()
+    a, b = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.ss1_backward_select_algo(None, ctypes.byref(T(1, 1)), 2, 64, 64, ctypes.byref(a),
+                                        ctypes.byref(b)) == _lib.ERR_NULL
+    assert lib.ss1_backward_select_algo(ctypes.byref(T(8, 256, _lib.F32)), ctypes.byref(T(64, 128, _lib.F32)), 2,
+                                        64, 64, ctypes.byref(a), ctypes.byref(b)) == _lib.ERR_DTYPE
+
+
+def test_binding_checks_plan_and_scale_arrays():
+    # the ABI reads plan arrays and row scales by pointer alone, so the binding
+    # checks their element type, layout and size before any call
+    torch = pytest.importorskip("torch")
+    K, N, c, BK, BN = 512, 128, 2, 64, 64          # G = 2, J = 8, Jc = 4
+    h = torch.zeros(2, 8, dtype=torch.int32)
+    s = torch.ones(2, 8, dtype=torch.int8)
+    _lib._check_plan(h, s, K, N, c, BK, BN)         # well formed
+    with pytest.raises(ValueError, match="hash must be torch.int32"):
+        _lib._check_plan(h.to(torch.int64), s, K, N, c, BK, BN)
+    with pytest.raises(ValueError, match="sign must be torch.int8"):
+        _lib._check_plan(h, s.to(torch.int32), K, N, c, BK, BN)
+    with pytest.raises(ValueError, match="hold 16 elements"):
+        _lib._check_plan(h[:, :7].contiguous(), s, K, N, c, BK, BN)
+    with pytest.raises(ValueError, match="contiguous"):
+        _lib._check_plan(torch.zeros(8, 4, dtype=torch.int32).T, s, K, N, c, BK, BN)
+    idx = torch.zeros(2, 4, 2, dtype=torch.int32)
+    _lib._check_plan(idx, s.view(2, 4, 2), K, N, c, BK, BN, index=True)
+    with pytest.raises(ValueError, match="idx must hold 16"):
+        _lib._check_plan(idx[:1], s.view(2, 4, 2), K, N, c, BK, BN, index=True)
+    sc = torch.ones(N, dtype=torch.float32)
+    _lib._check_vec(sc, torch.float32, N, "scale")
+    with pytest.raises(ValueError, match="scale must be torch.float32"):
+        _lib._check_vec(sc.double(), torch.float32, N, "scale")
+    with pytest.raises(ValueError, match="scale must hold 128"):
+        _lib._check_vec(sc[:-1], torch.float32, N, "scale")

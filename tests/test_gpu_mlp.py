@@ -2,14 +2,17 @@
 down-projection) against the CPU oracle, through the C ABI.
 
 Bars (written in each test):
-* h against the oracle's float32 mirror of the up-projection followed by the
-  float64 GELU: |h - ref| <= 2^-7 |ref| + 1e-5 max|ref| elementwise (one bf16
-  ulp for h's rounding plus float32 slack; the device's erff is within a few
-  float32 ulp), and max|h - h64| / max|h64| <= 2e-2 against the float64 chain.
-* y against the oracle's mirror of the down-projection applied to the
+* h against the mirror of the up-projection kernel that ran (ss1_select_algo:
+  bf16-rounded sketch for the sketch kernels, the exact projection for the
+  fold kernel) followed by the float64 GELU: |h - ref| <= 2^-7 |ref| +
+  1e-5 max|ref| elementwise (one bf16 ulp for h's rounding plus float32
+  slack; the device's GELU is within 1.5e-7 absolute), and
+  max|h - h64| / max|h64| <= 2e-2 against the float64 chain.
+* y against the mirror of the down-projection kernel that ran, applied to the
   device's own h (elementwise as above), and normwise <= 2e-2 against the
   float64 chain with h rounded to bf16.
-* row chunks that run the same kernels give bit-identical y.
+* row chunks that run the same kernels give bit-identical y; chunkings that
+  change the kernel family meet their own kernels' mirrors.
 * float32 layers: normwise <= 1e-5 against the float64 chain.
 """
 import numpy as np
@@ -74,7 +77,21 @@ class Pair:
         torch.cuda.synchronize()
         return h, y
 
-    def check(self, h, y, rows=None):
+    def kernels(self, rows_per_chunk):
+        """(up kernel, down kernel) the library runs on a chunk of this many
+        rows (ss1_select_algo)."""
+        U, D = self.up, self.down
+        dt = self.dtype
+        return (ss1.select_algo(rows_per_chunk, U["K"], U["N"], U["c"], U["BK"], U["BN"], dt),
+                ss1.select_algo(rows_per_chunk, D["K"], D["N"], D["c"], D["BK"], D["BN"], dt))
+
+    def check(self, h, y, rows=None, chunk_rows=None):
+        """Normwise bars against the float64 chain, then (bf16) elementwise
+        bars against the mirror of each kernel that ran: the sketch kernels
+        round the sketch to bf16 (forward_mirror), the fold kernel forms no
+        sketch (its mirror is the exact float64 projection).  ``chunk_rows``
+        is the row count of the chunk that held these rows (default: all rows
+        of the call in one chunk)."""
         x = self.x if rows is None else self.x[rows[0]:rows[1]]
         U, D = self.up, self.down
         bf = self.dtype == "bf16"
@@ -84,14 +101,20 @@ class Pair:
         assert np.max(np.abs(y - y64)) / np.max(np.abs(y64)) <= (TOL_BF16 if bf else TOL_F32)
         if not bf:
             return
+        ku, kd = self.kernels(chunk_rows or self.M)
+
+        def proj(inp, L, kernel):
+            args = (inp, L["Wc"], L["hash"], L["sign"], L["K"], L["N"], L["c"], L["BK"], L["BN"])
+            return oracle.forward(*args) if kernel == "fold" else oracle.forward_mirror(*args, True)
+
+        def ulp_ok(got, ref):
+            return np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-5 * np.max(np.abs(ref))
+
         if h is not None:
-            a = oracle.forward_mirror(x, U["Wc"], U["hash"], U["sign"], U["K"], U["N"], U["c"], U["BK"],
-                                      U["BN"], True)
-            ref = oracle.gelu(a)
-            assert np.all(np.abs(h - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-5 * np.max(np.abs(ref)))
-            ym = oracle.forward_mirror(h, D["Wc"], D["hash"], D["sign"], D["K"], D["N"], D["c"], D["BK"],
-                                       D["BN"], True)
-            assert np.all(np.abs(y - ym) <= 2.0 ** -7 * np.abs(ym) + 1e-5 * np.max(np.abs(ym)))
+            ref = oracle.gelu(proj(x, U, ku))
+            assert np.all(ulp_ok(h, ref)), f"h off the {ku} mirror"
+            ym = proj(h, D, kd)
+            assert np.all(ulp_ok(y, ym)), f"y off the {kd} mirror"
 
 
 def test_mlp_gpt2l_shapes_reduced_rows():
@@ -107,18 +130,42 @@ def test_mlp_c2_gpt2s_shapes():
 
 
 def test_mlp_row_chunks_bit_identical():
-    # chunks of more than 16 rows run the same kernels as the whole call, whose
-    # per-output arithmetic does not depend on the row count
+    # y's bits depend on M only through the kernels each chunk runs: chunks
+    # whose kernels (ss1_select_algo) match the whole call's give bit-identical
+    # y; other chunkings are held to their own kernels' mirrors
     P = Pair(0x5e20, 300, 1280, 5120, 1280, 4, 4, 64, 64, "bf16")
     _, y_full = P.run()
-    for R in (128, 100):
+    whole = P.kernels(300)
+    for R in (128, 100, 97, 1):
         h, y = P.run(row_chunk=R)
         assert h.shape[0] == R
-        assert torch.equal(y.view(torch.int16), y_full.view(torch.int16)), f"row_chunk {R}"
-    # a last chunk of 9 rows, and one row per chunk, take the small-M kernels
-    for R in (97, 1):
-        _, y = P.run(row_chunk=R)
-        P.check(None, to_host(y))
+        sizes = {R, 300 % R} - {0}
+        if all(P.kernels(n) == whole for n in sizes):
+            assert torch.equal(y.view(torch.int16), y_full.view(torch.int16)), f"row_chunk {R}"
+        yh = to_host(y)
+        for r0 in range(0, 300, R):
+            n = min(R, 300 - r0)
+            P.check(None, yh[r0:r0 + n], rows=(r0, r0 + n), chunk_rows=n)
+
+
+def test_mlp_row_chunks_change_kernel_family():
+    # GPT-2 L pair at 4096 rows: whole, the layers run a large-M kernel; in
+    # 9-row chunks they run the small-M kernels.  Sampled rows of each are
+    # held elementwise to their own kernels' mirrors (a chunk's h comes from a
+    # call on that chunk's rows alone, whose y must be the chunked call's y
+    # bit for bit: rows are independent and the kernels are the same).
+    P = Pair(0x5e21, 4096, 1280, 5120, 1280, 4, 4, 64, 64, "bf16")
+    assert P.kernels(4096) != P.kernels(9)
+    assert P.kernels(9) == ("smallm", "smallm")
+    hw, yw = P.run()
+    _, yc = P.run(row_chunk=9)
+    hw, yw = to_host(hw), to_host(yw)
+    for r0 in (0, 9 * 227, 4095 - 4095 % 9):
+        n = min(9, 4096 - r0)
+        P.check(hw[r0:r0 + n], yw[r0:r0 + n], rows=(r0, r0 + n), chunk_rows=4096)
+        h9, y9 = P.run(rows=(r0, r0 + n))
+        assert torch.equal(y9.view(torch.int16), yc[r0:r0 + n].view(torch.int16))
+        P.check(to_host(h9), to_host(y9), rows=(r0, r0 + n), chunk_rows=n)
 
 
 def test_mlp_small_m_and_odd_shapes():
@@ -148,11 +195,21 @@ def test_mlp_float32_tiny():
 
 
 def test_mlp_full_size_sampled_rows():
+    # the GPT-2 L pair at 8192 rows in one chunk (the bench's setting): both
+    # projections run the fold kernel, the up-projection with the GELU
+    # epilogue; sampled rows of h and y are held elementwise to the exact
+    # float64 mirrors
     P = Pair(0x5e60, 8192, 1280, 5120, 1280, 4, 4, 64, 64, "bf16")
+    assert P.kernels(8192) == ("fold", "fold")
+    h, y = P.run(row_chunk=8192)
+    h, y = to_host(h), to_host(y)
+    for r0 in (0, 4093, 8184):
+        P.check(h[r0:r0 + 8], y[r0:r0 + 8], rows=(r0, r0 + 8), chunk_rows=8192)
+    # in 2048-row chunks (h then stays in the last-level cache)
     _, y = P.run(row_chunk=2048)
     y = to_host(y)
     for r0 in (0, 4093, 8184):
-        P.check(None, y[r0:r0 + 8], rows=(r0, r0 + 8))
+        P.check(None, y[r0:r0 + 8], rows=(r0, r0 + 8), chunk_rows=2048)
 
 
 def test_mlp_empty_and_no_write_past_end():
