@@ -110,7 +110,7 @@ KERNEL_SOURCES = {
     "smallm": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "gemv": ("ss1_gemv.hip", "ss1_device.h", "ss1_internal.h"),
     "generic": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
-    "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_internal.h"),
+    "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "project": ("ss1_project.hip", "ss1_device.h", "ss1_internal.h"),
 }
 
@@ -167,6 +167,72 @@ def copy_calibration(n=20):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "copies": n}))
+
+
+def measured_peaks():
+    """Measured machine rates from the probes of libss1_peaks.so, each timed
+    with events over one launch on the current stream:
+      mfma_bf16_tflops  16x16x32 bf16 MFMA issue rate, 8 chains per wave
+      l2_read_tbs       reads into registers of a 2 MiB window every block
+                        shares (L2-resident after the first sweep)
+      l2_dma_tbs        the same window by direct buffer-to-LDS loads, 1 KB
+                        of consecutive bytes per wave-load
+      l2_dma_half_tbs   buffer-to-LDS loads of 64-byte half rows, one per
+                        128-byte line (a 32-column bf16 tile of a matrix)
+      hbm_read_tbs      reads of a 4 GiB buffer, each block its own 2 MiB
+      hbm_copy_tbs      torch's device copy of 1 GiB (read + write bytes)
+      lds_read_tbs      ds_read_b128 at conflict-free addresses"""
+    import ctypes
+    import torch
+    here = os.path.join(ROOT, "sketched_parameter_sharing_amd", "libss1_peaks.so")
+    lib = ctypes.CDLL(here)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream or None
+    vp = ctypes.c_void_p
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3
+            best = t if best is None else min(best, t)
+        return best
+
+    out = {}
+    blocks, iters = 256 * 8, 4096
+    t = timed(lambda: lib.ss1_peak_mfma(blocks, iters, vp(sink.data_ptr()), vp(st)))
+    out["mfma_bf16_tflops"] = blocks * 4 * iters * 8 * 2 * 16 * 16 * 32 / t / 1e12
+    win, reps, nb = 2 << 20, 16, 2048
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    t = timed(lambda: lib.ss1_peak_read(nb, vp(buf.data_ptr()), ctypes.c_uint32(win), reps, 0,
+                                        vp(sink.data_ptr()), vp(st)))
+    out["l2_read_tbs"] = nb * reps * win / t / 1e12
+    t = timed(lambda: lib.ss1_peak_dma(nb, 256, vp(buf.data_ptr()), ctypes.c_uint32(win), reps, 0,
+                                       vp(sink.data_ptr()), vp(st)))
+    out["l2_dma_tbs"] = nb * reps * win / t / 1e12
+    t = timed(lambda: lib.ss1_peak_dma(nb, 256, vp(buf.data_ptr()), ctypes.c_uint32(win), reps, 1,
+                                       vp(sink.data_ptr()), vp(st)))
+    out["l2_dma_half_tbs"] = nb * reps * win / 2 / t / 1e12
+    hwin = 2 << 20
+    nh = (4 << 30) // hwin
+    t = timed(lambda: lib.ss1_peak_read(nh, vp(buf.data_ptr()), ctypes.c_uint32(hwin), 1, 1,
+                                        vp(sink.data_ptr()), vp(st)))
+    out["hbm_read_tbs"] = nh * hwin / t / 1e12
+    src = buf[: 1 << 30]
+    dst = buf[2 << 30: (2 << 30) + (1 << 30)]
+    t = timed(lambda: dst.copy_(src))
+    out["hbm_copy_tbs"] = 2 * (1 << 30) / t / 1e12
+    li = 2048
+    t = timed(lambda: lib.ss1_peak_lds(256 * 8, li, vp(sink.data_ptr()), vp(st)))
+    out["lds_read_tbs"] = 256 * 8 * 256 * li * 8 * 16 / t / 1e12
+    del buf
+    return out
 
 
 def to_dev(a, dtype):
@@ -558,6 +624,8 @@ def main():
     ap.add_argument("--sweep", default=None, help="also time every workload, JSON lines into this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="run only the machine-rate probes (MFMA, L2, LDS-DMA, HBM, LDS) and print them")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -571,6 +639,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.peaks:
+        print(json.dumps({"measured_peaks": measured_peaks()}), flush=True)
         return
     import sketched_parameter_sharing_amd as ss1
     from ss1_inputs import WORKLOADS

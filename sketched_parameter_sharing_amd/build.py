@@ -90,7 +90,25 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, OUT)
+    build_peaks()
     return OUT
+
+
+PEAKS_SRC = os.path.join(HERE, "peaks", "ss1_peaks.hip")
+PEAKS_OUT = os.path.join(HERE, "libss1_peaks.so")
+
+
+def build_peaks() -> str:
+    """The benchmark's machine-rate probes (MFMA, L2, LDS-DMA, HBM, LDS) as
+    their own library; the SS1 library does not link them."""
+    tmp = PEAKS_OUT + ".tmp"
+    cmd = [_hipcc(), *COMMON, "-Wno-inline-asm", "-mllvm", "-amdgpu-mfma-vgpr-form=1", f"--offload-arch={ARCH}",
+           "-shared", PEAKS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, PEAKS_OUT)
+    return PEAKS_OUT
 
 
 if __name__ == "__main__":

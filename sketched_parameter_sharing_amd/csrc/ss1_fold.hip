@@ -38,6 +38,7 @@
 #include <cmath>
 
 #include "ss1_device.h"
+#include "ss1_dma.h"
 #include "ss1_internal.h"
 
 namespace ss1 {
@@ -55,20 +56,13 @@ __device__ __forceinline__ int fold_neuron(int p) {
     return (r >> 2) * 4 * FN + nb * 4 + (r & 3);
 }
 
-// XOR key of LDS row p for rows of RB bytes: the 16 rows that one quarter-wave
-// reads at a given 16-byte column land on 16 distinct bank groups.
-template <int RB>
-__device__ __forceinline__ int fold_key(int p) {
-    return (p / (256 / RB)) % (RB / 16);
-}
-
 // Plan of the block's groups in LDS, per (group gl of the tile, input chunk j):
 // s_off = byte offset inside a W_c row of the chunk j maps to (t*BK*WB, WB
 // bytes per stored weight), or
 // kFoldAbsent for an absent source; s_sgn = 0x80008000 for a negative sign,
 // else 0.  Hash form: pi/ps are hash/sign [G][J]; index form: idx/isign
 // [G][Jc][c].  Entries out of range leave the source absent.
-constexpr uint32_t kFoldAbsent = 0x7FFFFFFFu;  // plus any in-tile offset: past the extent
+constexpr uint32_t kFoldAbsent = kDmaAbsent;  // plus any in-tile offset: past the extent
 
 template <bool FROM_HASH, int WB>
 __device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __restrict__ ps, int g0, int ngr,
@@ -107,45 +101,6 @@ __device__ void stage_fold_plan(const int32_t* __restrict__ pi, const int8_t* __
         }
     }
     __syncthreads();
-}
-
-// Direct buffer-to-LDS load of 16 bytes per lane: lane l writes its 16 bytes
-// at LDS byte address lds + 16*l (an offset past the descriptor's extent
-// writes zeros).  Issued from inline asm: the instruction has no register
-// result, and the compiler, which cannot tell these LDS writes apart from the
-// operand reads of other stages, would otherwise wait for every one in flight
-// before each LDS read.  The stage barriers order them instead; the memory
-// clobber keeps LDS accesses on their side of the issue point.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 fold_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu), static_cast<int>(bytes),
-                 kBufferWord3};
-}
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
-}
-// M0 is listed as clobbered for the record; nothing else in these kernels
-// uses it (no LDS DMA builtins, no relative register indexing), and clang's
-// note that a reserved register is not preserved across the statement is
-// silenced here.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
-                 "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Waits until at most N of this wave's buffer loads are in flight and its LDS
-// reads are done, then joins the workgroup barrier.  A compiler fence here
-// would wait for every direct-to-LDS load in flight (they count as LDS
-// writes), which would drain the stage pipeline; the memory clobber keeps the
-// compiler from moving LDS accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void fold_stage_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 template <int BM, int BNB, int WM, int WN, int KS, int NSTG, bool W8, bool FROM_HASH>
@@ -210,17 +165,17 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     // l%CPR, and so reads piece (l%CPR) ^ key(row) of that row.  This wave
     // does loads wave, wave+NWV, ...; the key repeats every 16 rows, so one
     // lane offset serves all of them.
-    const i32x4 xr = fold_rsrc(x + static_cast<size_t>(m0) * K,
+    const i32x4 xr = dma_rsrc(x + static_cast<size_t>(m0) * K,
                                static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K * 2));
-    const i32x4 wr = fold_rsrc(reinterpret_cast<const uint8_t*>(w) + static_cast<size_t>(n0) * Kc * WB,
+    const i32x4 wr = dma_rsrc(reinterpret_cast<const uint8_t*>(w) + static_cast<size_t>(n0) * Kc * WB,
                                static_cast<uint32_t>(static_cast<size_t>(BNB) * Kc * WB));
     const int lrow = lane / CPR;
-    const int piece = (lane % CPR) ^ fold_key<RB>(wave * RPI + lrow);
+    const int piece = (lane % CPR) ^ swz_key<RB>(wave * RPI + lrow);
     const uint32_t x_voff = static_cast<uint32_t>(lrow * K + piece * 8) * 2u;
     uint32_t w_voff[WI];
     int w_gl[WI];  // group (inside the tile) of this lane's weight row, per load
     const int lroww = lane / CPRW;
-    const int piecew = (lane % CPRW) ^ fold_key<RBW>(wave * RPIW + lroww);
+    const int piecew = (lane % CPRW) ^ swz_key<RBW>(wave * RPIW + lroww);
 #pragma unroll
     for (int ii = 0; ii < WI; ++ii) {
         const int p = (wave + NWV * ii) * RPIW + lroww;               // LDS row in the weight tile
@@ -240,7 +195,8 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
 #pragma unroll
         for (int ii = 0; ii < XI; ++ii) {
             const int row0 = (wave + NWV * ii) * RPI;
-            lds_dma16(xr, base + row0 * RB, x_voff, static_cast<uint32_t>((row0 * K + k0) * 2));
+            lds_dma16(xr, base + row0 * RB, x_voff + static_cast<uint32_t>(row0 * K * 2),
+                      static_cast<uint32_t>(k0 * 2));
         }
 #pragma unroll
         for (int ii = 0; ii < WI; ++ii) {
@@ -253,7 +209,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     // kk/8 + l/16; the key of that row depends on l%16 only.
     const int fr = lane & 15;
     const int q = lane >> 4;
-    const int key = fold_key<RB>(fr);
+    const int key = swz_key<RB>(fr);
     // group (inside the tile) of the weight rows this lane feeds to the MFMA
     const int sg_gl = (wn * TNW + (fr >> 2) * 4 * FN) / BN;
 
@@ -273,7 +229,7 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     auto w_off = [&](int half) {
         if constexpr (W8) {
             const int byte = half * 32 + 8 * q;
-            return (((byte >> 4) ^ fold_key<RBW>(fr)) << 4) | (byte & 8);
+            return (((byte >> 4) ^ swz_key<RBW>(fr)) << 4) | (byte & 8);
         } else {
             return ((half * 4 + q) ^ key) * 16;
         }
@@ -310,9 +266,9 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     // wait until stage s's loads (all waves) have landed; `ahead` stages were
     // issued after it
     auto wait_stage = [&](int ahead) {
-        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
-        else if (ahead == 1) fold_stage_barrier<DPW>();
-        else fold_stage_barrier<0>();
+        if (ahead >= 2) dma_stage_barrier<2 * DPW>();
+        else if (ahead == 1) dma_stage_barrier<DPW>();
+        else dma_stage_barrier<0>();
     };
 
     // ---- pipeline.  Stage s lives in buffer s % NSTG.
@@ -452,13 +408,13 @@ __device__ __forceinline__ void dxfold_body(int bid, const uint16_t* __restrict_
     const int nstage = N / KS;
 
     // dy loads: as the x loads of the forward
-    const i32x4 dr = fold_rsrc(dy + static_cast<size_t>(m0) * N,
+    const i32x4 dr = dma_rsrc(dy + static_cast<size_t>(m0) * N,
                                static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * N * 2));
     const int lrow = lane / 8;
-    const int dpiece = (lane % 8) ^ fold_key<RB>(wave * RPI + lrow);
+    const int dpiece = (lane % 8) ^ swz_key<RB>(wave * RPI + lrow);
     const uint32_t dy_voff = static_cast<uint32_t>(lrow * N + dpiece * 8) * 2u;
     // W_c loads: load i = wave + NWV*ii fills rows (i % 8)*8 .. +7 of sub-tile i / 8
-    const i32x4 wr = fold_rsrc(w, static_cast<uint32_t>(static_cast<size_t>(N) * Kc * 2));
+    const i32x4 wr = dma_rsrc(w, static_cast<uint32_t>(static_cast<size_t>(N) * Kc * 2));
     int w_row[WI], w_sub[WI];
     uint32_t w_base[WI];
 #pragma unroll
@@ -481,7 +437,8 @@ __device__ __forceinline__ void dxfold_body(int bid, const uint16_t* __restrict_
 #pragma unroll
         for (int ii = 0; ii < XI; ++ii) {
             const int row0 = (wave + NWV * ii) * RPI;
-            lds_dma16(dr, base + row0 * RB, dy_voff, static_cast<uint32_t>((row0 * N + n0) * 2));
+            lds_dma16(dr, base + row0 * RB, dy_voff + static_cast<uint32_t>(row0 * N * 2),
+                      static_cast<uint32_t>(n0 * 2));
         }
 #pragma unroll
         for (int ii = 0; ii < WI; ++ii) {
@@ -492,7 +449,7 @@ __device__ __forceinline__ void dxfold_body(int bid, const uint16_t* __restrict_
 
     const int fr = lane & 15;
     const int q = lane >> 4;
-    const int key = fold_key<RB>(fr);
+    const int key = swz_key<RB>(fr);
 
     f32x4 acc[FN][FM];
 #pragma unroll
@@ -540,9 +497,9 @@ __device__ __forceinline__ void dxfold_body(int bid, const uint16_t* __restrict_
                 acc[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.w[i], o.d[jj], acc[i][jj], 0, 0, 0);
     };
     auto wait_stage = [&](int ahead) {
-        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
-        else if (ahead == 1) fold_stage_barrier<DPW>();
-        else fold_stage_barrier<0>();
+        if (ahead >= 2) dma_stage_barrier<2 * DPW>();
+        else if (ahead == 1) dma_stage_barrier<DPW>();
+        else dma_stage_barrier<0>();
     };
 
 #pragma unroll
@@ -691,8 +648,8 @@ __device__ __forceinline__ void dwfold_body(int bid, const uint16_t* __restrict_
     // Loads: load i = wave + NWV*ii fills rows (i % 8)*8 .. +7 of tile i / 8
     // (tiles 0 .. NSUB*CS-1: x sub-tile st = tile / CS, source r = tile % CS;
     // tile NSUB*CS: dy).  Tokens past M lie past both buffers and load zeros.
-    const i32x4 xr = fold_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(M) * K * 2));
-    const i32x4 dr = fold_rsrc(dy, static_cast<uint32_t>(static_cast<size_t>(M) * N * 2));
+    const i32x4 xr = dma_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(M) * K * 2));
+    const i32x4 dr = dma_rsrc(dy, static_cast<uint32_t>(static_cast<size_t>(M) * N * 2));
     const int lrow = lane / 8;
     int l_tile[DPW];
     uint32_t l_voff[DPW];
@@ -713,10 +670,14 @@ __device__ __forceinline__ void dwfold_body(int bid, const uint16_t* __restrict_
         for (int ii = 0; ii < DPW; ++ii) {
             const int i = wave + NWV * ii;
             const uint32_t dst = base + static_cast<uint32_t>(l_tile[ii] * TB + (i % (KS / RPI)) * RPI * RB);
-            if (l_tile[ii] < NSUB * CS)
-                lds_dma16(xr, dst, l_voff[ii] + s_xoff[l_tile[ii]], static_cast<uint32_t>(m0) * K * 2u);
-            else
-                lds_dma16(dr, dst, l_voff[ii], static_cast<uint32_t>(m0) * N * 2u);
+            if (l_tile[ii] < NSUB * CS) {
+                // an absent source keeps its offset past the extent (no wrap)
+                const uint32_t xo = s_xoff[l_tile[ii]];
+                lds_dma16(xr, dst,
+                          xo == kFoldAbsent ? kFoldAbsent : l_voff[ii] + xo + static_cast<uint32_t>(m0) * K * 2u, 0u);
+            } else {
+                lds_dma16(dr, dst, l_voff[ii] + static_cast<uint32_t>(m0) * N * 2u, 0u);
+            }
         }
     };
 
@@ -769,9 +730,9 @@ __device__ __forceinline__ void dwfold_body(int bid, const uint16_t* __restrict_
         }
     };
     auto wait_stage = [&](int ahead) {
-        if (ahead >= 2) fold_stage_barrier<2 * DPW>();
-        else if (ahead == 1) fold_stage_barrier<DPW>();
-        else fold_stage_barrier<0>();
+        if (ahead >= 2) dma_stage_barrier<2 * DPW>();
+        else if (ahead == 1) dma_stage_barrier<DPW>();
+        else dma_stage_barrier<0>();
     };
 
 #pragma unroll
@@ -790,7 +751,7 @@ __device__ __forceinline__ void dwfold_body(int bid, const uint16_t* __restrict_
 
     // the two halves' partial tiles meet in LDS (the stage buffers are free
     // once every wave has passed this barrier)
-    fold_stage_barrier<0>();
+    dma_stage_barrier<0>();
     float* red = reinterpret_cast<float*>(fold_smem);
     if (half == 1) {
 #pragma unroll

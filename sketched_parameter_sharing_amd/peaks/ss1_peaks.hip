@@ -1,0 +1,154 @@
+// Microbenchmarks of the MI355X (gfx950) rates the SS1 kernels are measured
+// against: bf16 MFMA issue rate, L2-resident read bandwidth into registers and
+// into LDS by direct buffer-to-LDS loads (whole 128-byte rows and 64-byte half
+// rows), HBM read bandwidth, and LDS read bandwidth.  Built as its own
+// library (libss1_peaks.so) for the benchmark; the SS1 library does not use
+// it.  Every kernel writes one value per block to `sink` so that no load or
+// multiply is dead code; the caller times the launch with events.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 MFMA 16x16x32: each wave runs `iters` rounds of 8 independent
+// accumulator chains (enough in flight to keep the matrix core busy).
+__global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* sink) {
+    const int lane = threadIdx.x & 63;
+    bf16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = static_cast<__bf16>(0.001f * (lane + i));
+        b[i] = static_cast<__bf16>(0.002f * (lane - i));
+    }
+    f32x4 acc[8];
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.0f;
+    for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    if (s == 1234.5f) sink[blockIdx.x] = s;  // never true for these inputs; keeps the chain live
+}
+
+// Reads into registers: block b sweeps `reps` times over a window of `win`
+// bytes (16 bytes per lane per load, whole 1 KB per wave-load): the shared
+// window [0, win) (L2-resident after the first sweep when it fits), or with
+// `own` its own window [b*win, (b+1)*win) (HBM reads for a large buffer).
+__global__ __launch_bounds__(256) void peak_read_kernel(const uint4* __restrict__ buf0, uint32_t win, int reps,
+                                                        int own, uint32_t* sink) {
+    const uint32_t n = win / 16;
+    const uint4* buf = buf0 + (own ? static_cast<size_t>(blockIdx.x) * n : 0);
+    uint32_t x = 0;
+    for (int r = 0; r < reps; ++r) {
+        for (uint32_t i = threadIdx.x; i < n; i += blockDim.x * 4) {
+            const uint4 v0 = buf[i];
+            const uint4 v1 = (i + blockDim.x < n) ? buf[i + blockDim.x] : make_uint4(0, 0, 0, 0);
+            const uint4 v2 = (i + 2 * blockDim.x < n) ? buf[i + 2 * blockDim.x] : make_uint4(0, 0, 0, 0);
+            const uint4 v3 = (i + 3 * blockDim.x < n) ? buf[i + 3 * blockDim.x] : make_uint4(0, 0, 0, 0);
+            x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.w ^ v2.y ^ v2.z ^ v3.x ^ v3.w;
+        }
+    }
+    if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+__device__ __forceinline__ i32x4 rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{static_cast<int>(a & 0xFFFFFFFFu), static_cast<int>((a >> 32) & 0xFFFFu), static_cast<int>(bytes),
+                 0x00020000};
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(i32x4 r, uint32_t lds, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(lds), "v"(voff),
+                 "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Direct buffer-to-LDS loads over a window of `win` bytes, `reps` sweeps.
+// half == 0: each wave-load brings 1 KB of consecutive bytes (8 rows of 128
+// bytes); half == 1: 16 half rows of 64 bytes, one per 128-byte line, the
+// pattern of a 32-column tile of a row-major bf16 matrix.  Each wave cycles
+// through 4 LDS slots of 1 KB and waits for its loads every 4.
+__global__ __launch_bounds__(256) void peak_dma_kernel(const uint8_t* __restrict__ buf, uint32_t win, int reps,
+                                                       int half, uint32_t* sink) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw = blockDim.x >> 6;
+    const i32x4 r = rsrc(buf, win);
+    const uint32_t base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) uint8_t*)(lds + wave * 4096)));
+    // per-lane offset inside one wave-load's footprint
+    const uint32_t voff = half ? static_cast<uint32_t>((lane >> 2) * 128 + (lane & 3) * 16) : static_cast<uint32_t>(lane * 16);
+    const uint32_t step = half ? 2048u : 1024u;  // footprint of one wave-load
+    const uint32_t loads = win / step;
+    uint32_t k = 0;
+    for (int rp = 0; rp < reps; ++rp) {
+        for (uint32_t i = wave; i < loads; i += nw) {
+            dma16(r, base + (k & 3) * 1024, voff, i * step);
+            ++k;
+            if ((k & 3) == 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const uint32_t v = reinterpret_cast<const uint32_t*>(lds)[threadIdx.x];
+    if (v == 0x9E3779B9u) sink[blockIdx.x] = v;
+}
+
+// LDS reads: each lane reads 16 bytes per ds_read_b128 at conflict-free
+// addresses, `iters` rounds of 8 reads.
+__global__ __launch_bounds__(256) void peak_lds_kernel(int iters, uint32_t* sink) {
+    __shared__ __attribute__((aligned(16))) uint4 s[4096];
+    for (int i = threadIdx.x; i < 4096; i += blockDim.x) s[i] = make_uint4(i, i + 1, i + 2, i + 3);
+    __syncthreads();
+    uint32_t x = 0;
+    const int t = threadIdx.x;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint4 v = s[(t + j * 256 + it) & 4095];
+            x ^= v.x ^ v.w;
+        }
+    }
+    if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss1_peak_mfma(int blocks, int iters, float* sink, void* stream) {
+    hipLaunchKernelGGL(peak_mfma_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int ss1_peak_read(int blocks, const void* buf, uint32_t win, int reps, int own, uint32_t* sink, void* stream) {
+    if (win % 16 != 0) return 2;
+    hipLaunchKernelGGL(peak_read_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4*>(buf), win, reps, own, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int ss1_peak_dma(int blocks, int threads, const void* buf, uint32_t win, int reps, int half, uint32_t* sink,
+                 void* stream) {
+    if (threads % 64 != 0 || threads > 256 || win % 2048 != 0) return 2;
+    const size_t lds = static_cast<size_t>(threads / 64) * 4096;
+    hipLaunchKernelGGL(peak_dma_kernel, dim3(blocks), dim3(threads), lds, static_cast<hipStream_t>(stream),
+                       static_cast<const uint8_t*>(buf), win, reps, half, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int ss1_peak_lds(int blocks, int iters, uint32_t* sink, void* stream) {
+    hipLaunchKernelGGL(peak_lds_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+}  // extern "C"
