@@ -296,6 +296,34 @@ ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, const int8_t* s
 ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
                            ss1_tensor* h, ss1_tensor* y, void* stream);
 
+/* Bytes of the library's static device workspace used by
+   ss1_mlp_forward_static (one array per GPU, held until the process ends). */
+#define SS1_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * ss1_mlp_forward_static -- DEVICE, asynchronous on `stream`.  ss1_mlp_forward
+ * with no workspace argument and no allocation of any kind, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  h lives in a static device array of
+ * SS1_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on;
+ * its device address is looked up once per device (hipGetSymbolAddress) on
+ * the first call made there.  The rows are processed in chunks of
+ *   R = floor(SS1_STATIC_SCRATCH_BYTES / (N1 * e))   (e = 2 for BF16, 4 for F32),
+ * rounded down to a multiple of 256 when R >= 256 -- the same result as
+ * ss1_mlp_forward with an h of R rows.  h is written by each chunk's
+ * up-projection before its down-projection reads it, so nothing needs
+ * clearing; its contents after a call are unspecified.
+ *   x, up, down, y : as ss1_mlp_forward
+ * Calls that overlap on one GPU (on different streams, or from several host
+ * threads) race on the shared array; serialise them.
+ * Errors: as ss1_mlp_forward, plus SS1_ERR_SHAPE when one row of h (N1 * e
+ * bytes) exceeds SS1_STATIC_SCRATCH_BYTES (checked before any HIP call), and
+ * SS1_ERR_HIP when the device or the array's address cannot be obtained.
+ * M == 0 checks the descriptors and makes no HIP call.
+ */
+ss1_status ss1_mlp_forward_static(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down, ss1_tensor* y,
+                                  void* stream);
+
 /*
  * ss1_quantize_fp8 -- DEVICE, asynchronous on `stream`.  Per-row fp8
  * quantization of a compressed weight, for ss1_forward_fp8w.  The SS1

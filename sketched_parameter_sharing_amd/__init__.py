@@ -18,11 +18,13 @@ from ._lib import (  # noqa: F401
     forward_idx,
     load,
     mlp_forward,
+    mlp_forward_static,
     plan,
     plan_index,
     project,
     quantize_fp8,
     select_algo,
+    static_rows,
     sketch,
     version,
 )

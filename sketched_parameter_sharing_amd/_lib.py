@@ -29,7 +29,7 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
            "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w",
-           "ss1_backward", "ss1_backward_select_algo")
+           "ss1_backward", "ss1_backward_select_algo", "ss1_mlp_forward_static")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -87,6 +87,8 @@ def load():
     lib.ss1_project.argtypes = [tp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_mlp_forward.restype = i32
     lib.ss1_mlp_forward.argtypes = [tp, ctypes.POINTER(Layer), ctypes.POINTER(Layer), tp, tp, vp]
+    lib.ss1_mlp_forward_static.restype = i32
+    lib.ss1_mlp_forward_static.argtypes = [tp, ctypes.POINTER(Layer), ctypes.POINTER(Layer), tp, vp]
     lib.ss1_quantize_fp8.restype = i32
     lib.ss1_quantize_fp8.argtypes = [tp, tp, vp, vp]
     lib.ss1_forward_fp8w.restype = i32
@@ -274,6 +276,38 @@ def mlp_forward(x, up, down, h=None, y=None, row_chunk: int | None = None, strea
                                 ctypes.byref(dy), _stream(stream))
     _check(st, "ss1_mlp_forward")
     return h, y
+
+
+# Bytes of the library's static h workspace (SS1_STATIC_SCRATCH_BYTES).
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def static_rows(N1: int, dtype_bytes: int) -> int:
+    """Rows per chunk ss1_mlp_forward_static uses for an up-projection of N1
+    neurons (the header's formula)."""
+    R = STATIC_SCRATCH_BYTES // (N1 * dtype_bytes)
+    return R - R % 256 if R >= 256 else R
+
+
+def mlp_forward_static(x, up, down, y=None, stream=None):
+    """SS1 MLP pair on the GPU with no workspace argument and no allocation in
+    the library (ss1_mlp_forward_static): h lives in the library's static
+    device array.  Allocates y only when it is None; returns y."""
+    import torch
+    Wu, hu, su, cu, BKu, BNu = up
+    Wd, hd, sd, cd, BKd, BNd = down
+    _check_device(x, Wu, hu, su, Wd, hd, sd)
+    _check_plan(hu, su, x.shape[-1], Wu.shape[0], cu, BKu, BNu)
+    _check_plan(hd, sd, Wu.shape[0], Wd.shape[0], cd, BKd, BNd)
+    if y is None:
+        y = torch.empty((x.shape[0], Wd.shape[0]), dtype=x.dtype, device=x.device)
+    lu = Layer(_desc(Wu), hu.data_ptr(), su.data_ptr(), cu, BKu, BNu, 0)
+    ld = Layer(_desc(Wd), hd.data_ptr(), sd.data_ptr(), cd, BKd, BNd, 0)
+    dx, dy = _desc(x), _desc(y)
+    st = load().ss1_mlp_forward_static(ctypes.byref(dx), ctypes.byref(lu), ctypes.byref(ld), ctypes.byref(dy),
+                                       _stream(stream))
+    _check(st, "ss1_mlp_forward_static")
+    return y
 
 
 def quantize_fp8(W_c, Q=None, scale=None, stream=None):

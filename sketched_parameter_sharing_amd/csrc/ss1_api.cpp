@@ -268,8 +268,10 @@ extern "C" ss1_status ss1_project(const ss1_tensor* W, const int32_t* hash, cons
     return ss1::launch_project(W->data, W->dtype, hash, sign, d, W_c->data, stream);
 }
 
-extern "C" ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
-                                      ss1_tensor* h, ss1_tensor* y, void* stream) {
+namespace ss1 {
+
+ss1_status mlp_forward_ws(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down, ss1_tensor* h,
+                          ss1_tensor* y, void* stream) {
     if (!x || !up || !down || !h || !y) return SS1_ERR_NULL;
     if (up->reserved != 0 || down->reserved != 0 || h->reserved != 0) return SS1_ERR_SHAPE;
     const int64_t M = x->rows;
@@ -311,6 +313,13 @@ extern "C" ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, 
         if (st != SS1_OK) return st;
     }
     return SS1_OK;
+}
+
+}  // namespace ss1
+
+extern "C" ss1_status ss1_mlp_forward(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down,
+                                      ss1_tensor* h, ss1_tensor* y, void* stream) {
+    return ss1::mlp_forward_ws(x, up, down, h, y, stream);
 }
 
 extern "C" ss1_status ss1_quantize_fp8(const ss1_tensor* W_c, ss1_tensor* Q, float* scale, void* stream) {

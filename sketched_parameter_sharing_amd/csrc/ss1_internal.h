@@ -71,6 +71,11 @@ ss1_status launch_bwd_fold(const void* x, const void* W_c, const int32_t* hash, 
 ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, const int8_t* sign, void* dW,
                           int64_t M, const Dims& d, void* stream);
 
+// The MLP pair (ss1_mlp_forward's checks and chunked launches) with h as the
+// per-chunk workspace; every check runs before any HIP call.
+ss1_status mlp_forward_ws(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down, ss1_tensor* h,
+                          ss1_tensor* y, void* stream);
+
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);
 ss1_status launch_smallm(const ForwardArgs& a);

@@ -396,3 +396,26 @@ def test_binding_checks_plan_and_scale_arrays():
         _lib._check_vec(sc.double(), torch.float32, N, "scale")
     with pytest.raises(ValueError, match="scale must hold 128"):
         _lib._check_vec(sc[:-1], torch.float32, N, "scale")
+
+
+def test_mlp_forward_static_argument_checks():
+    # checks that run before any HIP call: a row of h wider than the static
+    # array, a null descriptor, a dtype the library has no kernel for
+    lib = _lib.load()
+    N1 = (_lib.STATIC_SCRATCH_BYTES // 2) + 64          # one bf16 row of h > the array
+    up = _lib.Layer(T(N1, 128), A, A, 2, 64, 64, 0)
+    down = _lib.Layer(T(64, N1 // 2), A, A, 2, 64, 64, 0)
+    x, y = T(8, 256), T(8, 64)
+    f = lib.ss1_mlp_forward_static
+    assert f(ctypes.byref(x), ctypes.byref(up), ctypes.byref(down), ctypes.byref(y), None) == _lib.ERR_SHAPE
+    assert f(None, ctypes.byref(up), ctypes.byref(down), ctypes.byref(y), None) == _lib.ERR_NULL
+    assert f(ctypes.byref(T(8, 256, 7)), ctypes.byref(up), ctypes.byref(down), ctypes.byref(y),
+             None) == _lib.ERR_DTYPE
+    # M == 0 only checks the descriptors (no device needed)
+    up = _lib.Layer(T(3072, 384), A, A, 2, 64, 64, 0)
+    down = _lib.Layer(T(768, 1536), A, A, 2, 64, 64, 0)
+    assert f(ctypes.byref(T(0, 768, data=None)), ctypes.byref(up), ctypes.byref(down),
+             ctypes.byref(T(0, 768, data=None)), None) == _lib.OK
+    assert f(ctypes.byref(T(0, 768, data=None)), ctypes.byref(up), ctypes.byref(down),
+             ctypes.byref(T(0, 700, data=None)), None) == _lib.ERR_SHAPE
+    assert _lib.static_rows(5120, 2) == 3072 and _lib.static_rows(N1 - 64, 2) == 1
