@@ -2,18 +2,25 @@
 
 One step = one ss1_forward call (input sketch, contraction, epilogue: the whole
 hot path) over one batch of synthetic inputs already resident in HBM.  By
-default the workload is the GPT-2 Small MLP up-projection at 2x compression
-(M=8192 tokens, K=768, N=3072, c=2, BK=64, BN=64, bf16).  Steps rotate through
-enough distinct input/output buffer sets (> 512 MB in total, twice the MALL)
-that every step reads its operands from HBM, not from a warm cache.
+default the workload is the largest single-GPU configuration, the
+Llama-3-8B-shaped gate/up projection at 2x compression (M=4096 tokens,
+K=4096, N=14336, c=2, BK=64, BN=64, bf16).  Steps rotate through enough
+distinct input/output buffer sets (> 512 MB in total, twice the MALL) that
+every step reads its operands from HBM, not from a warm cache.  The K timed
+steps run as at least 20 trials of equal length, each bracketed by events on
+the stream the library launches on; ms_per_step is the median trial's time
+per step (p10 / p90 beside it), the whole region is also timed.
 
 Prints ONE JSON line: dense-equivalent TFLOP/s (2*M*N*K per step / time), the
 fraction of the binding roofline of the dominant kernel (MFMA bf16 on the
 compressed FLOPs 2*M*N*K/c, or HBM on the algorithmic bytes
-e*(M*K + N*K/c + M*N), whichever bound is the larger lower time), and the CPU
-oracle timed on a bounded sample of the same workload.
+e*(M*K + N*K/c + M*N), whichever bound is the larger lower time) against the
+spec peak and against the peak measured by the probes of --peaks, the L2
+operand traffic of the fold kernel against the measured L2-to-LDS rate, and
+the CPU oracle (float64, and float32) timed on a bounded sample of the same
+workload.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload gpt2s_up]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama_gateup_m4096]
                     [--algo auto] [--index] [--warm] [--graph] [--no-cpu-baseline]
                     [--sweep FILE]   # one extra JSON line per workload into FILE
         # --graph: the timed calls captured in one HIP graph and replayed
@@ -34,11 +41,11 @@ oracle timed on a bounded sample of the same workload.
         # ss1_project instead: least-squares projection of the layer's dense
         # [N][K] weight onto its sharing pattern, GB/s against the HBM roofline
 
-roofline.traffic is the HBM traffic of one launch measured with rocprofv3
-FETCH_SIZE and WRITE_SIZE counters, each scaled by what the counter reads for
-the plain copy of --copy-calibration; it is read from
-profiles/traffic_counters.json and reported only while the kernel source the
-counters were taken on is unchanged (else null).
+roofline.traffic is the HBM traffic of one step measured with rocprofv3
+counters (reads from TCC_EA0_RDREQ / _128B / _32B, writes from WRITE_SIZE),
+checked against the plain copy of --copy-calibration; it is read from
+profiles/traffic_counters.json and reported only while the kernel sources the
+counters were taken on are unchanged (else null).
 """
 from __future__ import annotations
 
@@ -58,7 +65,7 @@ METRIC = "SS1 layer dense-equiv TFLOP/s + % of MFMA/HBM roofline at M×K×N, c"
 PEAK_MFMA_BF16 = 2.5e15     # MI355X dense bf16 MFMA, FLOP/s
 PEAK_MFMA_F32 = 157.3e12
 PEAK_HBM = 8.0e12           # MI355X HBM3E, B/s
-HEADLINE = "gpt2s_up"
+HEADLINE = "llama_gateup_m4096"
 SWEEP = ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m1", "llama_down_m1",
          "llama_gateup_m16", "llama_down_m16", "llama_gateup_m4096", "llama_down_m4096"] + [
     f"square_c{c}_bn{bn}" for c in (1, 2, 4, 8) for bn in (32, 64, 128)]
@@ -77,8 +84,44 @@ def work(wl):
     }
 
 
-def roofline(wl, t, kernel=None):
-    """Roofline record of one launch lasting t seconds of `kernel`."""
+def fold_operand_bytes(wl, cus):
+    """Bytes the fold kernel moves from L2 into LDS per call (the x tile and
+    the expanded weight tile of every stage of every tile), for its usual
+    256 x 256 tiles: when they end in a partial round of compute units, the
+    neurons past the last whole round run as 128 x 256 tiles (the library's
+    split launch); 192 x 256 tiles where those fill one round of tiles with
+    fewer tile rows (GPT-2 L down).  A model of the launch, not a counter."""
+    M, N, K = wl.M, wl.N, wl.K
+    e = 2
+    if N % 256:
+        return None
+    n_mt, n_nt = -(-M // 256), N // 256
+    tiles = n_mt * n_nt
+    full = tiles // cus
+    main = N
+    if full and tiles % cus:
+        n_main = full * cus // n_mt
+        if 0 < n_main < n_nt:
+            single = -(-tiles // cus)
+            split = -(-(n_mt * n_main) // cus) + 0.55 * -(-((-(-M // 128)) * (n_nt - n_main)) // cus)
+            if split < 0.97 * single:
+                main = n_main * 256
+    cost256 = 256 * (-(-(n_mt * (main // 256)) // cus) + (0.55 * -(-((-(-M // 128)) * ((N - main) // 256)) // cus)
+                                                         if main != N else 0))
+    cost192 = 192 * -(-((-(-M // 192)) * n_nt) // cus)
+    if cost192 < cost256:
+        return (-(-M // 192)) * n_nt * K * (192 + 256) * e
+    b = n_mt * (main // 256) * K * (256 + 256) * e
+    if main != N:
+        b += (-(-M // 128)) * ((N - main) // 256) * K * (128 + 256) * e
+    return b
+
+
+def roofline(wl, t, kernel=None, peaks=None):
+    """Roofline record of one launch lasting t seconds of `kernel`; with
+    `peaks` (measured_peaks()), the fraction of the measured peak too and, for
+    the fold kernel, its L2-to-LDS operand traffic against the measured
+    buffer-to-LDS rate."""
     wk = work(wl)
     peak_f = PEAK_MFMA_BF16 if wl.dtype == "bf16" else PEAK_MFMA_F32
     t_f = wk["compressed_flops"] / peak_f
@@ -92,9 +135,23 @@ def roofline(wl, t, kernel=None):
     else:
         r = {"bound": "hbm", **hb, "other": {"bound": "mfma", **mf}}
     r["t_lower_us"] = max(t_f, t_b) * 1e6
+    if peaks:
+        meas = (peaks["mfma_bf16_tflops"] * 1e12 if r["bound"] == "mfma" else peaks["hbm_read_tbs"] * 1e12)
+        unit_div = 1e12 if r["bound"] == "mfma" else 1e9
+        r["measured_peak"] = {"peak": meas / unit_div, "unit": r["unit"], "frac": r["achieved"] / (meas / unit_div),
+                              "source": "bench.py --peaks probes, same process"}
+        if kernel == "fold":
+            import torch
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+            ob = fold_operand_bytes(wl, cus)
+            if ob:
+                r["l2_operand"] = {"bytes": ob, "achieved_tbs": ob / t / 1e12,
+                                   "peak_tbs": peaks["l2_dma_tbs"], "frac": ob / t / 1e12 / peaks["l2_dma_tbs"],
+                                   "note": "x and expanded-weight tiles moved L2 -> LDS per call (tile model) "
+                                           "against the measured buffer-to-LDS read rate"}
     traffic = recorded_traffic(wl.name, kernel)
     r["traffic"] = traffic
-    r["traffic_unit"] = "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)"
+    r["traffic_unit"] = "HBM bytes per step (TCC_EA0_RDREQ* read bytes + WRITE_SIZE; all launches of one call)"
     r["traffic_vs_algorithmic"] = (traffic / wk["bytes"]) if traffic else None
     return r
 
@@ -137,23 +194,24 @@ def kernel_source_sha256(names=None):
 
 
 def recorded_traffic(name, kernel=None):
-    """Calibrated HBM bytes per launch for record `name` (a workload, or
-    "project:<workload>" / "fp8:<workload>") from the committed counter
-    record, or None when there is none, when it measured another kernel family
-    than `kernel`, or when the sources of its kernel changed since."""
+    """HBM bytes per step (every launch of one call) for record `name` (a
+    workload, or "project:<workload>" / "fp8:<workload>") from the committed
+    counter record, or None when there is none, when it measured another
+    kernel family than `kernel`, or when the sources of its kernels changed
+    since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    w = rec.get("workloads", {}).get(name)
+    w = rec.get("records", {}).get(name)
     if not w or "sources" not in w:
         return None
-    if kernel is not None and kernel_family(w.get("kernel", "")) != kernel:
+    if kernel is not None and w.get("family") != kernel:
         return None
     if w.get("sources_sha256") != kernel_source_sha256(w["sources"]):
         return None
-    return w.get("hbm_bytes_per_launch")
+    return w.get("hbm_bytes_per_step")
 
 
 def copy_calibration(n=20):
@@ -291,20 +349,39 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm, graph=False):
         plan.forward(xs[k], ws[k], y=ys[k], algo=algo, use_index=use_index)
 
     if graph:
-        return time_graph(step, steps, warmup), nsets
+        t = time_graph(step, steps, warmup)
+        return t, nsets, {"median": t, "p10": t, "p90": t, "mean": t, "trials": 1, "steps_per_trial": steps}
     for i in range(warmup):
         step(i)
+    stats = time_trials(step, steps)
+    return stats["median"], nsets, stats
+
+
+def time_trials(step, steps, min_trials=20):
+    """Times exactly `steps` calls of step(i) as at least `min_trials` trials
+    of equal length (the last one takes the remainder), each bracketed by
+    events recorded on the current stream, the one the library launches on;
+    the whole region is bracketed by synchronizations.  Returns seconds per
+    step: median, p10, p90 over trials, and the mean over the whole region."""
+    import torch
+    per = max(1, steps // min_trials)
+    bounds = list(range(0, steps, per)) + [steps]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in bounds]
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev[0].record()
+    for b in range(len(bounds) - 1):
+        for i in range(bounds[b], bounds[b + 1]):
+            step(i)
+        ev[b + 1].record()
     torch.cuda.synchronize()
-    start.record()
-    for i in range(steps):
-        step(i)
-    end.record()
-    torch.cuda.synchronize()
-    t = start.elapsed_time(end) / 1e3 / steps
-    return t, nsets
+    wall = time.perf_counter() - t0
+    per_step = np.array([ev[b].elapsed_time(ev[b + 1]) / 1e3 / (bounds[b + 1] - bounds[b])
+                         for b in range(len(bounds) - 1)])
+    total = ev[0].elapsed_time(ev[-1]) / 1e3
+    return {"median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+            "p90": float(np.percentile(per_step, 90)), "mean": total / steps, "trials": len(per_step),
+            "steps_per_trial": per, "wall_s": wall}
 
 
 def project_work(wl):
@@ -569,7 +646,16 @@ def kernel_name(wl, algo):
 
 
 def cpu_baseline(wl, budget_s=10.0):
-    """The oracle as it stands, float64, on a bounded sample of rows."""
+    """The oracle as it stands, float64 (its definition) and float32 (the
+    same steps, for CPU speed), each on a bounded sample of rows."""
+    r64 = cpu_baseline_dtype(wl, np.float64, budget_s)
+    r32 = cpu_baseline_dtype(wl, np.float32, budget_s)
+    r64["float32"] = {"value": r32["value"], "unit": r32["unit"], "sample": r32["sample"]}
+    return r64
+
+
+def cpu_baseline_dtype(wl, dtype, budget_s=10.0):
+    """The oracle's forward in `dtype` on a bounded sample of rows."""
     import oracle
     from ss1_inputs import make_inputs
 
@@ -584,8 +670,9 @@ def cpu_baseline(wl, budget_s=10.0):
     h, s = oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
     rows = min(wl.M, 256)
     inp = make_inputs(wl.with_m(rows))
+    name = np.dtype(dtype).name
     t0 = time.perf_counter()
-    oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, dtype=dtype)
     t1 = time.perf_counter() - t0
     # scale the sample to about budget_s of CPU time
     rows = int(min(wl.M, max(rows, rows * budget_s / max(t1, 1e-3))))
@@ -593,14 +680,14 @@ def cpu_baseline(wl, budget_s=10.0):
     reps = 0
     t0 = time.perf_counter()
     while True:   # whole-workload samples repeat until about budget_s of CPU time
-        oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+        oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN, dtype=dtype)
         reps += 1
         if time.perf_counter() - t0 > budget_s or reps >= 50:
             break
     t = (time.perf_counter() - t0) / reps
     return {"value": 2 * rows * wl.N * wl.K / t / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{rows} of {wl.M} rows of {wl.name}, float64 NumPy oracle, {reps} rep(s), "
+            "sample": f"{rows} of {wl.M} rows of {wl.name}, {name} NumPy oracle, {reps} rep(s), "
                       f"{t:.3f} s each (dense-equivalent FLOPs of the sample / time)"}
 
 
@@ -621,6 +708,8 @@ def main():
                     help="capture the timed calls in one HIP graph (forward and fp8 ops): no host launch "
                          "cost in the timed region, for microsecond decode layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the machine-rate probes (roofline against spec peaks only); for profiler runs")
     ap.add_argument("--sweep", default=None, help="also time every workload, JSON lines into this file")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 256 MiB device copy (counter calibration)")
@@ -647,9 +736,11 @@ def main():
     from ss1_inputs import WORKLOADS
     ss1.load()
 
+    peaks = None if (args.no_peaks or args.op != "forward") else measured_peaks()
+
     def measure(name, steps, warmup):
         wl = WORKLOADS[name]
-        t, nsets = time_gpu(wl, steps, warmup, args.algo, args.index, args.warm, args.graph)
+        t, nsets, stats = time_gpu(wl, steps, warmup, args.algo, args.index, args.warm, args.graph)
         wk = work(wl)
         rec = {
             "metric": METRIC,
@@ -670,9 +761,15 @@ def main():
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)",
                        "launch": "one HIP graph of the timed calls" if args.graph else "eager",
                        "compressed_tflops": wk["compressed_flops"] / t / 1e12,
-                       "x_l2_gb": wk["x_l2_bytes"] / 1e9},
+                       "x_l2_gb": wk["x_l2_bytes"] / 1e9,
+                       "timing": {"trials": stats["trials"], "steps_per_trial": stats["steps_per_trial"],
+                                  "ms_per_step_median": stats["median"] * 1e3,
+                                  "ms_per_step_p10": stats["p10"] * 1e3, "ms_per_step_p90": stats["p90"] * 1e3,
+                                  "ms_per_step_mean": stats["mean"] * 1e3}},
         }
-        rec["roofline"] = roofline(wl, t, rec["config"]["kernel"])
+        rec["roofline"] = roofline(wl, t, rec["config"]["kernel"], peaks)
+        if peaks:
+            rec["config"]["measured_peaks"] = peaks
         if rec["config"]["kernel"] == "fold":
             # the fold kernel multiplies by the expanded weight: its matrix
             # cores execute the dense FLOP count, c times the algorithmic one
@@ -703,7 +800,7 @@ def main():
                        "cache": "warm" if args.warm else f"cold ({nsets} rotating buffer sets)"},
             "roofline": {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9,
                          "unit": "GB/s", "frac": wk["bytes"] / t / PEAK_HBM, "traffic": traffic,
-                         "traffic_unit": "HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE)",
+                         "traffic_unit": "HBM bytes per call (TCC_EA0_RDREQ* read bytes + WRITE_SIZE)",
                          "traffic_vs_algorithmic": (traffic / wk["bytes"]) if traffic else None,
                          "t_lower_us": wk["bytes"] / PEAK_HBM * 1e6},
         }
@@ -816,7 +913,7 @@ def main():
         name = args.workload or "llama_gateup_m1"
         wl = WORKLOADS[name]
         t, nsets = time_fp8(wl, args.steps, args.warmup, args.warm, args.graph)
-        t16, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, args.warm,
+        t16, _, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, args.warm,
                           args.graph)
         wk = fp8_work(wl)
         t_f = wk["compressed_flops"] / PEAK_MFMA_BF16
@@ -862,7 +959,7 @@ def main():
 
     rec, wl = measure(args.workload or HEADLINE, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl)
+        rec["cpu_baseline"] = cpu_baseline(wl, budget_s=8.0)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -180,44 +180,48 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def sketch(x, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+def sketch(x, hash_, sign, K: int, N: int, c: int, BK: int, BN: int, dtype=np.float64) -> np.ndarray:
     """Per-group chunk sketch of the input rows, in float64.
 
     For every group g a fresh [M][Kc] accumulator starts at zero; walking the
     input chunks j in ascending order, chunk j of every row, times sign[g][j],
     is added into compressed chunk hash[g][j] at the same offsets.  Returns
-    z with shape [G][M][Kc].  Accepts any in-range hash (balance not needed)."""
+    z with shape [G][M][Kc].  Accepts any in-range hash (balance not needed).
+    ``dtype`` float32 runs the same steps in float32 (only the CPU-speed
+    baseline of the benchmark uses it; the definition is float64)."""
     d = dims(K, N, c, BK, BN)
     J, Kc, G = d["J"], d["Kc"], d["G"]
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x, dtype=dtype)
     if x.ndim != 2 or x.shape[1] != K:
         raise ValueError(f"x must have shape [M][{K}]")
     check_plan(hash_, sign, K, N, c, BK, BN, balanced=False)
     M = x.shape[0]
-    z = np.zeros((G, M, Kc), dtype=np.float64)
+    z = np.zeros((G, M, Kc), dtype=dtype)
     for g in range(G):
         for j in range(J):
             t = int(hash_[g, j])
-            s = float(sign[g, j])
+            s = dtype(sign[g, j])
             z[g, :, t * BK:(t + 1) * BK] += s * x[:, j * BK:(j + 1) * BK]
     return z
 
 
-def forward(x, Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int) -> np.ndarray:
+def forward(x, Wc, hash_, sign, K: int, N: int, c: int, BK: int, BN: int, dtype=np.float64) -> np.ndarray:
     """SS1 forward in float64: sketch the input (as in :func:`sketch`), then
     multiply group g's sketch by its BN rows of the compressed weight,
     ``y[:, g*BN:(g+1)*BN] = z_g @ Wc[g*BN:(g+1)*BN, :].T``.
 
     ``x`` is [M][K], ``Wc`` is [N][Kc] (row-major, one row per neuron, like a
-    dense linear layer's [out][in] weight).  Returns y, [M][N] float64."""
+    dense linear layer's [out][in] weight).  Returns y, [M][N] float64
+    (``dtype`` float32: the same steps in float32, for the benchmark's
+    CPU-speed baseline only)."""
     d = dims(K, N, c, BK, BN)
     Kc, G = d["Kc"], d["G"]
-    Wc = np.asarray(Wc, dtype=np.float64)
+    Wc = np.asarray(Wc, dtype=dtype)
     if Wc.shape != (N, Kc):
         raise ValueError(f"Wc must have shape {(N, Kc)}")
-    z = sketch(x, hash_, sign, K, N, c, BK, BN)
+    z = sketch(x, hash_, sign, K, N, c, BK, BN, dtype=dtype)
     M = z.shape[1]
-    y = np.empty((M, N), dtype=np.float64)
+    y = np.empty((M, N), dtype=dtype)
     for g in range(G):
         y[:, g * BN:(g + 1) * BN] = z[g] @ Wc[g * BN:(g + 1) * BN, :].T
     return y

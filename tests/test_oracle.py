@@ -712,3 +712,17 @@ def test_forward_mirror_c4_ascending_float32_sum():
         ref[:, g * BN:(g + 1) * BN] = z @ Wc[g * BN:(g + 1) * BN].T
     mir = oracle.forward_mirror(x, Wc, h, s, K, N, c, BK, BN, True)
     assert np.max(np.abs(mir - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_forward_float32_steps_match_float64():
+    # the float32 run of the same steps (the benchmark's CPU-speed baseline)
+    # agrees with the float64 definition to float32 accuracy, and the default
+    # stays float64
+    M, K, N, c, BK, BN = 40, 512, 96, 2, 32, 32
+    h, s = oracle.plan(52, K, N, c, BK, BN)
+    x = draw("normal", 53, (M, K)).astype(np.float64)
+    Wc = draw("normal002", 54, (N, K // c)).astype(np.float64)
+    y64 = oracle.forward(x, Wc, h, s, K, N, c, BK, BN)
+    y32 = oracle.forward(x, Wc, h, s, K, N, c, BK, BN, dtype=np.float32)
+    assert y64.dtype == np.float64 and y32.dtype == np.float32
+    assert np.max(np.abs(y32 - y64)) <= 1e-5 * np.max(np.abs(y64))
