@@ -421,6 +421,46 @@ def time_fp8(wl, steps, warmup, warm, graph=False):
     return time_events_i(step, steps, warmup), nsets
 
 
+def fp8a_work(wl):
+    """Per step: quantize x (read bf16, write E4M3 codes and row scales), then
+    the fp8 layer (read the codes, W_c codes and scales, write bf16 y)."""
+    return {"dense_flops": 2 * wl.M * wl.N * wl.K, "compressed_flops": 2 * wl.M * wl.N * wl.K // wl.c,
+            "bytes": 2 * wl.M * wl.K + (wl.M * wl.K + 4 * wl.M) * 2 + wl.N * wl.Kc + 4 * wl.N + 2 * wl.M * wl.N
+                     + wl.G * wl.J * 5}
+
+
+def time_fp8a(wl, steps, warmup):
+    """One step = ss1_quantize_fp8 of x then ss1_forward_fp8 (W_c quantized
+    once, as weights are), over rotating buffer sets: returns
+    (seconds per step, sets, seconds of the forward alone)."""
+    import torch
+    import sketched_parameter_sharing_amd as ss1
+    from ss1_inputs import make_inputs
+
+    inp = make_inputs(wl)
+    plan = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    Q, ws = ss1.quantize_fp8(to_dev(inp.w_bits, "bf16"))
+    nsets = min(64, max(2, int(np.ceil(512e6 / fp8a_work(wl)["bytes"])) + 1))
+    x0 = to_dev(inp.x_bits, "bf16")
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    xq = [torch.empty(x0.shape, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    sc = [torch.empty((wl.M,), dtype=torch.float32, device="cuda") for _ in range(nsets)]
+    ys = [torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+
+    def step(i):
+        k = i % nsets
+        ss1.quantize_fp8(xs[k], Q=xq[k], scale=sc[k])
+        ss1.forward_fp8(xq[k], sc[k], Q, ws, plan.hash, plan.sign, wl.c, wl.BK, wl.BN, y=ys[k])
+
+    def fwd(i):
+        k = i % nsets
+        ss1.forward_fp8(xq[k], sc[k], Q, ws, plan.hash, plan.sign, wl.c, wl.BK, wl.BN, y=ys[k])
+
+    t = time_events_i(step, steps, warmup)
+    t_fwd = time_events_i(fwd, steps, warmup)
+    return t, nsets, t_fwd
+
+
 def time_events_i(fn, steps, warmup):
     import torch
     for i in range(warmup):
@@ -698,7 +738,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None,
                     help=f"default: {HEADLINE} (forward), {PROJECT_HEADLINE} (project)")
-    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "backward"])
+    ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "fp8a", "backward"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "generic", "band", "fold"])
@@ -947,6 +987,47 @@ def main():
         else:
             rec["cpu_baseline"] = cpu_baseline(wl)
             rec["cpu_baseline"]["sample"] += " (bf16-weight oracle: the fp8 layer's arithmetic is the same)"
+        print(json.dumps(rec), flush=True)
+        return
+
+    if args.op == "fp8a":
+        name = args.workload or HEADLINE
+        wl = WORKLOADS[name]
+        t, nsets, t_fwd = time_fp8a(wl, args.steps, args.warmup)
+        t16, _, _ = time_gpu(wl, max(20, args.steps // 2), max(5, args.warmup // 2), "auto", False, False)
+        wk = fp8a_work(wl)
+        peak8 = 5.0e15   # MI355X dense fp8 MFMA
+        mf = {"bound": "mfma", "achieved": wk["compressed_flops"] / t / 1e12, "peak": peak8 / 1e12,
+              "unit": "TFLOP/s"}
+        mf["frac"] = mf["achieved"] / mf["peak"]
+        hb = {"bound": "hbm", "achieved": wk["bytes"] / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+        hb["frac"] = hb["achieved"] / hb["peak"]
+        t_f, t_b = wk["compressed_flops"] / peak8, wk["bytes"] / PEAK_HBM
+        roof = dict(mf if t_f >= t_b else hb)
+        roof.update({"other": hb if t_f >= t_b else mf, "traffic": recorded_traffic("fp8a:" + name),
+                     "t_lower_us": max(t_f, t_b) * 1e6,
+                     "note": "per step: x quantized to E4M3 per row, then the fp8 fold (dense fp8 MFMA work "
+                             "2*M*N*K; the compressed count is the algorithmic one)"})
+        rec = {
+            "metric": "SS1 layer with fp8 (E4M3) input and weights on fp8 MFMA: dense-equiv TFLOP/s + % of "
+                      "fp8 MFMA/HBM roofline",
+            "value": wk["dense_flops"] / t / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": t * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8 e4m3 (x and W_c, per-row scales), fp32 accumulate, bf16 y",
+            "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) compressed weights, both quantized per row, "
+                    "seeded balanced plan)",
+            "config": {"workload": name + "_fp8a", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c, "BK": wl.BK,
+                       "BN": wl.BN, "kernel": "quantize_fp8 + fold8",
+                       "cache": f"cold ({nsets} rotating buffer sets)", "forward_only_ms": t_fwd * 1e3,
+                       "executed_fp8_tflops": wk["dense_flops"] / t_fwd / 1e12,
+                       "bf16_layer_ms": t16 * 1e3, "speedup_vs_bf16_layer": t16 / t},
+            "roofline": roof,
+        }
+        if args.no_cpu_baseline:
+            rec["cpu_baseline"] = None
+        else:
+            rec["cpu_baseline"] = cpu_baseline_dtype(wl, np.float64, 8.0)
+            rec["cpu_baseline"]["sample"] += " (the dequantized layer's arithmetic is the same)"
         print(json.dumps(rec), flush=True)
         return
 

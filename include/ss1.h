@@ -369,6 +369,35 @@ ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q, const floa
                             ss1_tensor* y, void* stream);
 
 /*
+ * ss1_forward_fp8 -- DEVICE, asynchronous on `stream`.  The SS1 layer with
+ * both operands quantized to fp8 and contracted on the fp8 matrix cores (the
+ * SS1 summary page, "Limitations": quantized SS1 kernels were not built;
+ * "Measured effects": SS1 models quantized after training keep their
+ * quality; the SS1 author abstract: SS1 combines with quantization).  The
+ * layer computed (a reading; the pages fix no scheme):
+ *   y[m][n] = xscale[m] * wscale[n] * sum_k e4m3(xq[m][k]) * sign_g(j) *
+ *             e4m3(Wq[n][h_g(j)*BK + u])      (k = j*BK + u, g = n / BN)
+ * i.e. SS1 of the dequantized input and weight.  Each product of two E4M3
+ * values is exact in float32, the sums accumulate in float32 on the MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, unit block scales), the two row
+ * scales multiply the sum, and y is rounded to bf16 (nearest, ties to even).
+ * Quantize x per row with ss1_quantize_fp8 (one scale per token row) and W_c
+ * per row likewise.  The kernel multiplies x by the expanded weight (no
+ * sketch is formed), dense MFMA work at twice the bf16 rate.
+ *   xq : [M][K] SS1_FP8_E4M3;  xscale : DEVICE float[M]
+ *   Wq : [N][K/c] SS1_FP8_E4M3;  wscale : DEVICE float[N]
+ *   hash, sign : as ss1_forward;  y : [M][N] BF16, written
+ * Requirements: ss1_forward's chunking, plus N % 256 == 0, 256 % BN == 0,
+ * BK % 64 == 0, K % 128 == 0, 256*K and N*K/c under 2^31; xq, Wq and y
+ * 16-byte aligned, scales 4-byte aligned.  M == 0 enqueues nothing.
+ * Errors: SS1_ERR_NULL, SS1_ERR_DTYPE, SS1_ERR_SHAPE, SS1_ERR_ALIGN (before
+ * any HIP call), SS1_ERR_HIP.
+ */
+ss1_status ss1_forward_fp8(const ss1_tensor* xq, const float* xscale, const ss1_tensor* Wq, const float* wscale,
+                           const int32_t* hash, const int8_t* sign, int32_t c, int32_t BK, int32_t BN,
+                           ss1_tensor* y, void* stream);
+
+/*
  * ss1_backward -- DEVICE, asynchronous on `stream`.  Gradients of
  * y = ss1_forward(x, W_c) for an upstream gradient dy (the SS1 summary page,
  * "Limitations": the backward pass is not reduced, it costs what a dense

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     backward,
     backward_select_algo,
     forward,
+    forward_fp8,
     forward_fp8w,
     forward_idx,
     load,

@@ -29,7 +29,7 @@ ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
            "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w",
-           "ss1_backward", "ss1_backward_select_algo", "ss1_mlp_forward_static")
+           "ss1_backward", "ss1_backward_select_algo", "ss1_mlp_forward_static", "ss1_forward_fp8")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -91,6 +91,8 @@ def load():
     lib.ss1_mlp_forward_static.argtypes = [tp, ctypes.POINTER(Layer), ctypes.POINTER(Layer), tp, vp]
     lib.ss1_quantize_fp8.restype = i32
     lib.ss1_quantize_fp8.argtypes = [tp, tp, vp, vp]
+    lib.ss1_forward_fp8.restype = i32
+    lib.ss1_forward_fp8.argtypes = [tp, vp, tp, vp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_forward_fp8w.restype = i32
     lib.ss1_forward_fp8w.argtypes = [tp, tp, vp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_backward.restype = i32
@@ -339,6 +341,24 @@ def forward_fp8w(x, Q, scale, hash_, sign, c: int, BK: int, BN: int, y=None, str
     st = load().ss1_forward_fp8w(ctypes.byref(dx), ctypes.byref(dq), scale.data_ptr(), hash_.data_ptr(),
                                  sign.data_ptr(), c, BK, BN, ctypes.byref(dy), _stream(stream))
     _check(st, "ss1_forward_fp8w")
+    return y
+
+
+def forward_fp8(xq, xscale, Q, wscale, hash_, sign, c: int, BK: int, BN: int, y=None, stream=None):
+    """y = SS1 with fp8 (E4M3) input and weights on the fp8 matrix cores
+    (ss1_forward_fp8): ``xq``/``xscale`` from quantize_fp8(x), ``Q``/``wscale``
+    from quantize_fp8(W_c); y is bf16."""
+    import torch
+    _check_device(xq, xscale, Q, wscale, hash_, sign)
+    _check_plan(hash_, sign, xq.shape[-1], Q.shape[0], c, BK, BN)
+    _check_vec(xscale, torch.float32, xq.shape[0], "xscale")
+    _check_vec(wscale, torch.float32, Q.shape[0], "wscale")
+    if y is None:
+        y = torch.empty((xq.shape[0], Q.shape[0]), dtype=torch.bfloat16, device=xq.device)
+    dx, dq, dy = _desc(xq), _desc(Q), _desc(y)
+    st = load().ss1_forward_fp8(ctypes.byref(dx), xscale.data_ptr(), ctypes.byref(dq), wscale.data_ptr(),
+                                hash_.data_ptr(), sign.data_ptr(), c, BK, BN, ctypes.byref(dy), _stream(stream))
+    _check(st, "ss1_forward_fp8")
     return y
 
 

@@ -363,6 +363,26 @@ extern "C" ss1_status ss1_forward_fp8w(const ss1_tensor* x, const ss1_tensor* Q,
     return ss1::launch_fused(a);
 }
 
+extern "C" ss1_status ss1_forward_fp8(const ss1_tensor* xq, const float* xscale, const ss1_tensor* Wq,
+                                      const float* wscale, const int32_t* hash, const int8_t* sign, int32_t c,
+                                      int32_t BK, int32_t BN, ss1_tensor* y, void* stream) {
+    if (!xq || !Wq || !y) return SS1_ERR_NULL;
+    if (xq->dtype != SS1_FP8_E4M3 || Wq->dtype != SS1_FP8_E4M3 || y->dtype != SS1_BF16) return SS1_ERR_DTYPE;
+    // the forward's own checks, on descriptors of the same shapes in bf16
+    ss1_tensor xb = *xq, wb = *Wq;
+    xb.dtype = SS1_BF16;
+    wb.dtype = SS1_BF16;
+    ForwardArgs a;
+    ss1_status st = check_forward(&xb, &wb, hash, sign, c, BK, BN, y, PlanForm::Hash, stream, &a);
+    if (st != SS1_OK) return st;
+    if (!wscale || (a.M > 0 && !xscale)) return SS1_ERR_NULL;
+    if (!aligned(wscale, 4) || !aligned(xscale, 4)) return SS1_ERR_ALIGN;
+    if (!ss1::fold8_supported(a.M, a.d)) return SS1_ERR_SHAPE;
+    if (a.M == 0) return SS1_OK;
+    return ss1::launch_fold8(xq->data, xscale, Wq->data, wscale, hash, sign, y->data, a.M, a.d, ss1::kActNone,
+                             stream);
+}
+
 extern "C" ss1_status ss1_backward_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c,
                                                int32_t BK, int32_t BN, int32_t* dx_algo, int32_t* dw_algo) {
     if (!x || !W_c || !dx_algo || !dw_algo) return SS1_ERR_NULL;

@@ -328,6 +328,207 @@ __global__ __launch_bounds__(WM * WN * 64) void fold_kernel(const uint16_t* __re
     }
 }
 
+// ============================================================ fp8 fold kernel
+// The fold with both operands in OCP E4M3 (x quantized per token row, W_c per
+// neuron row, each with a float32 scale) on the gfx950 fp8 matrix cores:
+// y[m][n] = xs[m] * ws[n] * sum_k e4m3(xq[m][k]) * B8[n][k], with B8 the
+// expanded E4M3 weight (codes of W_c at each input chunk's compressed chunk,
+// the chunk's sign on the code's sign bit).  Products of two E4M3 values are
+// exact in float32, which accumulates them.
+//
+// Block: 8 waves (2 x 4), tile 256 tokens x 256 neurons (whole groups), wave
+// tile 128 x 64.  K runs in stages of 128 inputs (128 bytes of a token row);
+// per stage the MFMA is v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales): each
+// lane feeds 32 bytes of one row, at byte 32*(lane/16) of the stage, on both
+// operands.  The x tile [256][128 B] comes in 8-row loads (whole 128-byte
+// rows); the weight tile comes as two [256][64 B] halves, one per 64 inputs
+// (BK % 64 == 0, so a half sits inside one input chunk), each row's half at
+// the compressed chunk its group maps that input chunk to; an absent source
+// points past the buffer and loads zeros.  The half's sign goes onto the
+// weight operand as it leaves LDS (lanes 0-31 read the first half, 32-63 the
+// second).  Two LDS stages, the next one loading during the current one.
+template <int NSTG>
+__global__ __launch_bounds__(512) void fold8_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ xs,
+                                                   const uint8_t* __restrict__ wq, const float* __restrict__ ws,
+                                                   const int32_t* __restrict__ hash, const int8_t* __restrict__ sign,
+                                                   uint16_t* __restrict__ y, int M, int K, int N, int J, int Jc,
+                                                   int BK, int BN, int n_mt, int act) {
+    constexpr int BM = 256, BNB = 256, WM = 2, WN = 4, NWV = 8;
+    constexpr int TMW = BM / WM, TNW = BNB / WN;  // 128 x 64
+    constexpr int FM = TMW / 16, FN = TNW / 16;   // 8 x 4
+    constexpr int KS = 128;                       // inputs (bytes) per stage
+    constexpr int RBX = 128, RPIX = 8;            // x tile: 128-byte rows, 8 rows per wave-wide load
+    constexpr int RBW = 64, RPIW = 16;            // weight halves: 64-byte rows, 16 per load
+    constexpr int XI = BM / RPIX / NWV;           // 4 x loads per wave per stage
+    constexpr int WI = 2 * BNB / RPIW / NWV;      // 4 weight loads per wave per stage
+    constexpr int DPW = XI + WI;
+    constexpr int SX = BM * RBX;                  // 32 KB
+    constexpr int SWH = BNB * RBW;                // 16 KB per weight half
+    constexpr int SB = SX + 2 * SWH;              // 64 KB per stage
+
+    extern __shared__ __attribute__((aligned(16))) uint8_t fold_smem[];
+    uint32_t* s_off = reinterpret_cast<uint32_t*>(fold_smem + NSTG * SB);
+
+    constexpr int GM = 4;
+    const int n_nt = N / BNB;
+    const int tile = xcd_tile(blockIdx.x, n_mt * n_nt);
+    const int strip = tile / (GM * n_nt);
+    const int gm = min(GM, n_mt - strip * GM);
+    const int rem = tile - strip * GM * n_nt;
+    const int mt = strip * GM + rem % gm;
+    const int nt = rem / gm;
+    const int m0 = mt * BM;
+    const int n0 = nt * BNB;
+    const int ngr = BNB / BN;
+    uint32_t* s_sgn = s_off + ngr * J;
+    const int Kc = Jc * BK;
+    stage_fold_plan<true, 1>(hash, sign, n0 / BN, ngr, J, Jc, 1, BK, s_off, s_sgn);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int nstage = K / KS;
+
+    const i32x4 xr = dma_rsrc(xq + static_cast<size_t>(m0) * K,
+                              static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K));
+    const i32x4 wr = dma_rsrc(wq + static_cast<size_t>(n0) * Kc, static_cast<uint32_t>(static_cast<size_t>(BNB) * Kc));
+    // x loads: load i = wave + NWV*ii fills rows i*8 .. i*8+7; the key of a
+    // row repeats every 16 rows and NWV*8 is a multiple of 16
+    const int lrx = lane >> 3;
+    const int pcx = (lane & 7) ^ swz_key<RBX>(wave * RPIX + lrx);
+    const uint32_t x_voff = static_cast<uint32_t>(lrx * K + pcx * 16);
+    // weight loads: load i = wave + NWV*ii < 32; half i / 16, rows (i % 16)*16
+    // .. +15 of that half; row p holds neuron (p/64)*64 + fold_neuron(p % 64)
+    const int lrw = lane >> 2;
+    const int pcw = (lane & 3) ^ swz_key<RBW>(lrw);
+    uint32_t w_voff[WI];
+    int w_gl[WI];
+#pragma unroll
+    for (int ii = 0; ii < WI; ++ii) {
+        const int i = wave + NWV * ii;
+        const int p = (i % 16) * RPIW + lrw;
+        const int n = (p / TNW) * TNW + fold_neuron<FN>(p % TNW);
+        w_voff[ii] = static_cast<uint32_t>(n * Kc + pcw * 16);
+        w_gl[ii] = n / BN;
+    }
+    const uint32_t lds0 = lds_address(fold_smem);
+    auto dma = [&](int s, int buf) {
+        const int k0 = s * KS;
+        const uint32_t base = lds0 + static_cast<uint32_t>(buf * SB);
+#pragma unroll
+        for (int ii = 0; ii < XI; ++ii) {
+            const int row0 = (wave + NWV * ii) * RPIX;
+            lds_dma16(xr, base + row0 * RBX, x_voff + static_cast<uint32_t>(row0 * K), static_cast<uint32_t>(k0));
+        }
+#pragma unroll
+        for (int ii = 0; ii < WI; ++ii) {
+            const int i = wave + NWV * ii;
+            const int h = i / 16;                      // weight half (compile-time per ii and wave parity)
+            const int kh = k0 + 64 * h;                // first input of the half
+            const int j = kh / BK;
+            const uint32_t off = s_off[w_gl[ii] * J + j];
+            lds_dma16(wr, base + SX + h * SWH + (i % 16) * RPIW * RBW,
+                      off == kFoldAbsent ? kFoldAbsent : w_voff[ii] + off + static_cast<uint32_t>(kh - j * BK), 0u);
+        }
+    };
+
+    // operands: lane l reads row (block base + l%16), bytes 32q .. 32q+31 of
+    // the stage (q = l/16): x pieces 2q, 2q+1 of its 128-byte row; weight
+    // half q/2, pieces 2(q%2), 2(q%2)+1 of its 64-byte row
+    const int fr = lane & 15;
+    const int q = lane >> 4;
+    const int keyx = swz_key<RBX>(fr);
+    const int keyw = swz_key<RBW>(fr);
+    const int hq = q >> 1;
+    const int sg_gl = (wn * TNW + (fr >> 2) * 4 * FN) / BN;
+
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj) acc[i][jj] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    auto step = [&](int s, int buf) {
+        if (nstage - 1 - s >= 1 && NSTG >= 3) dma_stage_barrier<DPW>();
+        else dma_stage_barrier<0>();
+        if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        const uint8_t* S = fold_smem + buf * SB;
+        const int jq = (s * KS + 64 * hq) / BK;        // input chunk of this lane's weight half
+        const uint32_t sx = s_sgn[sg_gl * J + jq] ? 0x80808080u : 0u;
+        i32x8 wv[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const uint8_t* W = S + SX + hq * SWH + (wn * TNW + i * 16 + fr) * RBW;
+            const uint4 a = *reinterpret_cast<const uint4*>(W + (((2 * (q & 1)) ^ keyw) << 4));
+            const uint4 b = *reinterpret_cast<const uint4*>(W + (((2 * (q & 1) + 1) ^ keyw) << 4));
+            wv[i] = i32x8{static_cast<int>(a.x ^ sx), static_cast<int>(a.y ^ sx), static_cast<int>(a.z ^ sx),
+                          static_cast<int>(a.w ^ sx), static_cast<int>(b.x ^ sx), static_cast<int>(b.y ^ sx),
+                          static_cast<int>(b.z ^ sx), static_cast<int>(b.w ^ sx)};
+        }
+        // token operands one 16-row block at a time (the next one read while
+        // the current block's MFMAs run): 128 accumulators, 32 weight and 16
+        // token registers fit the 256 a wave has at two waves per SIMD
+        auto xread = [&](int jj) {
+            const uint8_t* X = S + (wm * TMW + jj * 16 + fr) * RBX;
+            const uint4 a = *reinterpret_cast<const uint4*>(X + (((2 * q) ^ keyx) << 4));
+            const uint4 b = *reinterpret_cast<const uint4*>(X + (((2 * q + 1) ^ keyx) << 4));
+            return i32x8{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w),
+                         static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
+        };
+        i32x8 xv = xread(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int jj = 0; jj < FM; ++jj) {
+            const i32x8 xn = jj + 1 < FM ? xread(jj + 1) : xv;
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wv[i], xv, acc[i][jj], 0, 0, 0, 127,
+                                                                              0, 127);
+            xv = xn;
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+#pragma unroll
+    for (int p = 0; p < NSTG - 1; ++p)
+        if (p < nstage) dma(p, p);
+    for (int s0 = 0; s0 < nstage; s0 += NSTG) {
+#pragma unroll
+        for (int b = 0; b < NSTG; ++b)
+            if (s0 + b < nstage) step(s0 + b, b);
+    }
+
+    // epilogue: lane holds neurons wn*64 + (lane/16)*16 + nb*4 + i of token
+    // wm*128 + mb*16 + lane%16; y = acc * xs[m] * ws[n]
+    const int nbase = n0 + wn * TNW + q * 4 * FN;
+    float wsc[4 * FN];
+#pragma unroll
+    for (int i = 0; i < 4 * FN; ++i) wsc[i] = ws[nbase + i];
+#pragma unroll
+    for (int mb = 0; mb < FM; ++mb) {
+        const int m = m0 + wm * TMW + mb * 16 + fr;
+        if (m >= M) continue;
+        const float xsm = xs[m];
+        uint16_t* yr = y + static_cast<size_t>(m) * N + nbase;
+#pragma unroll
+        for (int h = 0; h < FN / 2; ++h) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = acc[2 * h][mb][i] * xsm * wsc[8 * h + i];
+                v[4 + i] = acc[2 * h + 1][mb][i] * xsm * wsc[8 * h + 4 + i];
+            }
+            uint4 o;
+            o.x = pack_bf16(apply_act(v[0], act), apply_act(v[1], act));
+            o.y = pack_bf16(apply_act(v[2], act), apply_act(v[3], act));
+            o.z = pack_bf16(apply_act(v[4], act), apply_act(v[5], act));
+            o.w = pack_bf16(apply_act(v[6], act), apply_act(v[7], act));
+            *reinterpret_cast<uint4*>(yr + 8 * h) = o;
+        }
+    }
+}
+
 // ================================================================ dx kernel
 // dx = dy B, with B the expanded weight of the forward (dx[m][j*BK + u] =
 // sum_n dy[m][n] sign_g(n)(j) W_c[n][h_g(n)(j)*BK + u]): the same contraction
@@ -1206,6 +1407,37 @@ ss1_status launch_fold(const ForwardArgs& a) {
     // fp8 weights come with the forward hash only
     if (a.w_fp8) return a.form == PlanForm::Hash ? launch_fold_t<true, true>(a) : SS1_ERR_ALGO;
     return a.form == PlanForm::Hash ? launch_fold_t<true, false>(a) : launch_fold_t<false, false>(a);
+}
+
+// fp8 fold (both operands E4M3): 256 x 256 tiles, two 64 KB stages.  Needs
+// N a multiple of 256 split into whole groups, BK % 64 == 0 (each 64-input
+// weight half inside one chunk), K % 128 == 0, and 32-bit byte offsets over a
+// tile's x rows and over W_c.
+size_t fold8_lds(const Dims& d) { return static_cast<size_t>(2) * 64 * 1024 + static_cast<size_t>(256 / d.BN) * d.J * 8; }
+
+bool fold8_supported(int64_t M, const Dims& d) {
+    if (M < 0 || d.N % 256 != 0 || 256 % d.BN != 0 || d.BK % 64 != 0 || d.K % 128 != 0) return false;
+    if (256.0 * static_cast<double>(d.K) >= 2147483648.0 || static_cast<double>(d.N) * d.Kc >= 2147483648.0) return false;
+    return fold8_lds(d) <= static_cast<size_t>(max_lds_per_block());
+}
+
+ss1_status launch_fold8(const void* xq, const float* xs, const void* wq, const float* ws, const int32_t* hash,
+                        const int8_t* sign, void* y, int64_t M, const Dims& d, int32_t act, void* stream) {
+    if (!fold8_supported(M, d)) return SS1_ERR_ALGO;
+    if (M == 0) return SS1_OK;
+    const int n_mt = static_cast<int>((M + 255) / 256);
+    const long long blocks = static_cast<long long>(n_mt) * (d.N / 256);
+    if (blocks > 0x7FFFFFFFLL) return SS1_ERR_SHAPE;
+    const size_t lds = fold8_lds(d);
+    auto kern = &fold8_kernel<2>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((fold8_kernel<2>), dim3(static_cast<unsigned>(blocks)), dim3(512), lds,
+                       static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(xq), xs,
+                       static_cast<const uint8_t*>(wq), ws, hash, sign, static_cast<uint16_t*>(y), (int)M, (int)d.K,
+                       (int)d.N, (int)d.J, (int)d.Jc, d.BK, d.BN, n_mt, act);
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
 }
 
 }  // namespace ss1

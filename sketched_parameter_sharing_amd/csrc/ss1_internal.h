@@ -76,6 +76,13 @@ ss1_status launch_dw_fold(const void* x, const void* dy, const int32_t* hash, co
 ss1_status mlp_forward_ws(const ss1_tensor* x, const ss1_layer* up, const ss1_layer* down, ss1_tensor* h,
                           ss1_tensor* y, void* stream);
 
+// fp8 fold (ss1_fold.hip): x and W_c both as E4M3 codes with float32 row
+// scales, bf16 y; hash plan; N % 256 == 0, 256 % BN == 0, BK % 64 == 0,
+// K % 128 == 0.
+bool fold8_supported(int64_t M, const Dims& d);
+ss1_status launch_fold8(const void* xq, const float* xs, const void* wq, const float* ws, const int32_t* hash,
+                        const int8_t* sign, void* y, int64_t M, const Dims& d, int32_t act, void* stream);
+
 // Kernel launchers (ss1_kernels.hip).  Return SS1_OK or SS1_ERR_HIP.
 ss1_status launch_fused(const ForwardArgs& a);
 ss1_status launch_smallm(const ForwardArgs& a);

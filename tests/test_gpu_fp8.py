@@ -130,3 +130,98 @@ def test_forward_fp8w_full_size(name):
         rows = np.r_[0:4, 191:193, wl.M // 2:wl.M // 2 + 4, 8063:8065, wl.M - 4:wl.M]
         rows = np.unique(rows[rows < wl.M])
     run_case(wl, wl.M, rows)
+
+
+# ------------------------------------------- fp8 input and weights (fp8 MFMA)
+# ss1_forward_fp8: x and W_c both E4M3 with per-row scales, contracted on the
+# fp8 matrix cores.  The layer it computes is SS1 of the dequantized operands;
+# the kernel forms no sketch (fold) and every product of two E4M3 values is
+# exact in float32, so the mirror is the float64 oracle of the dequantized
+# layer, under one bf16 ulp plus the float32 summation bound (below).  Integer
+# codes with power-of-two scales make every sum exact: y must then equal the
+# rounded oracle bit for bit.
+
+def e4m3_int_codes(g, shape):
+    """E4M3 codes of integers in {-4..4} (exact in E4M3)."""
+    vals = g.integers(-4, 5, shape)
+    lut = {0: 0x00, 1: 0x38, 2: 0x40, 3: 0x44, 4: 0x48}
+    codes = np.vectorize(lambda v: lut[abs(v)] | (0x80 if v < 0 else 0))(vals).astype(np.uint8)
+    return codes, vals.astype(np.float64)
+
+
+def rne_bf16(a):
+    return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(a, dtype=np.float32))).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [(300, 2048, 512, 2, 64, 64), (257, 1024, 256, 4, 64, 32),
+                                           (40, 4096, 256, 1, 128, 128), (513, 768, 768, 2, 64, 256)])
+def test_forward_fp8_integer_bit_exact(M, K, N, c, BK, BN):
+    g = np.random.default_rng(M + K)
+    xc, xv = e4m3_int_codes(g, (M, K))
+    wc, wv = e4m3_int_codes(g, (N, K // c))
+    xs = (2.0 ** g.integers(-2, 3, M)).astype(np.float32)
+    wsc = (2.0 ** g.integers(-2, 3, N)).astype(np.float32)
+    p = ss1.DevicePlan.make(0x8100 + M, K, N, c, BK, BN)
+    y = ss1.forward_fp8(torch.from_numpy(xc).cuda(), torch.from_numpy(xs).cuda(), torch.from_numpy(wc).cuda(),
+                        torch.from_numpy(wsc).cuda(), p.hash, p.sign, c, BK, BN)
+    torch.cuda.synchronize()
+    h, s = oracle.plan(0x8100 + M, K, N, c, BK, BN)
+    ref = oracle.forward(xv * xs[:, None], wv * wsc[:, None], h, s, K, N, c, BK, BN)
+    assert np.array_equal(to_host(y), rne_bf16(ref))
+
+
+def run_fp8a(wl, M, rows=None):
+    """Quantize x and W_c on the device, run ss1_forward_fp8, check against the
+    dequantized layer's float64 oracle (the mirror) and report the error
+    against the unquantized bf16 layer."""
+    inp = make_inputs(wl.with_m(M))
+    p = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    xq, xs = ss1.quantize_fp8(bf16_dev(inp.x_bits))
+    Q, wsc = ss1.quantize_fp8(bf16_dev(inp.w_bits))
+    y = ss1.forward_fp8(xq, xs, Q, wsc, p.hash, p.sign, wl.c, wl.BK, wl.BN)
+    torch.cuda.synchronize()
+    y = to_host(y)
+    h, s = oracle.plan(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    codes_x, sc_x = xq.cpu().numpy(), xs.cpu().numpy()
+    if rows is not None:
+        codes_x, sc_x, y, x = codes_x[rows], sc_x[rows], y[rows], inp.x[rows]
+    else:
+        x = inp.x
+    # the device quantizer is the oracle's (codes and scales bit for bit)
+    qc, qs = oracle.quantize_fp8_rows(x)
+    assert np.array_equal(codes_x, qc) and np.array_equal(sc_x.view(np.uint32), qs.view(np.uint32))
+    xd = oracle.dequantize_fp8_rows(codes_x, sc_x)
+    Wd = oracle.dequantize_fp8_rows(Q.cpu().numpy(), wsc.cpu().numpy())
+    ref = oracle.forward(xd, Wd, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    # bar: one bf16 ulp of the result, plus the worst case of a float32 sum of
+    # K exact products in any order (K * 2^-24 * sum of |products|, Higham's
+    # bound), plus the two float32 scale multiplies; a float32 sum of K = 2048
+    # to 14336 products can leave an output that nearly cancels well outside
+    # 1e-5 max|y|, which no rounding-order-free bar can exclude
+    sum_abs = np.abs(xd) @ np.abs(oracle.dense_expand(Wd, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)).T
+    bound = 2.0 ** -7 * np.abs(ref) + wl.K * 2.0 ** -24 * sum_abs + 2.0 ** -22 * np.abs(ref)
+    bad = np.abs(y - ref) > bound
+    assert not bad.any(), f"{wl.name}: {int(bad.sum())} outputs off the dequantized layer beyond the bar"
+    # and the bf16 bar the other kernels meet, on all but a few near-cancelling outputs
+    tight = np.abs(y - ref) > 2.0 ** -7 * np.abs(ref) + 1e-5 * np.max(np.abs(ref))
+    assert tight.sum() <= max(1, tight.size // 10000)
+    # against the unquantized layer: E4M3 keeps 3 mantissa bits (relative
+    # rounding error <= 2^-4 per operand), so each product is off by about
+    # 2^-3 relative at most and the errors of K random-signed terms add like
+    # a random walk: normwise (by max|y|) error well under 5e-2
+    full = oracle.forward(x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    err = np.max(np.abs(y - full)) / np.max(np.abs(full))
+    assert err <= 5e-2, f"{wl.name}: error against the bf16 layer {err:.3e}"
+    return err
+
+
+def test_forward_fp8_reduced_ragged():
+    wl = Workload("fp8a_ragged", 8, 31, 300, 2048, 512, 2, 64, 64, "bf16")
+    run_fp8a(wl, 300)
+
+
+@pytest.mark.parametrize("name", ["llama_gateup_m4096", "llama_down_m4096", "gpt2l_up", "gpt2l_down", "gpt2s_up"])
+def test_forward_fp8_full_size_sampled(name):
+    wl = WORKLOADS[name]
+    rows = np.r_[0:4, 255:257, wl.M // 2:wl.M // 2 + 4, wl.M - 4:wl.M]
+    run_fp8a(wl, wl.M, rows)
