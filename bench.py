@@ -168,6 +168,7 @@ KERNEL_SOURCES = {
     "gemv": ("ss1_gemv.hip", "ss1_device.h", "ss1_internal.h"),
     "generic": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
+    "fold8": ("ss1_fold.hip", "ss1_quant.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "project": ("ss1_project.hip", "ss1_device.h", "ss1_internal.h"),
 }
 
@@ -357,6 +358,30 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm, graph=False):
     return stats["median"], nsets, stats
 
 
+def time_dense_layer(wl, steps, warmup, warm=False):
+    """The dense layer of the same shape, y = x @ W^T with W [N][K] (torch's
+    GEMM, hipBLASLt on ROCm), cold over rotating buffer sets as time_gpu
+    rotates the SS1 layer's: seconds per step (median over trials)."""
+    import torch
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    e = 2 if wl.dtype == "bf16" else 4
+    set_bytes = e * (wl.M * wl.K + wl.N * wl.K + wl.M * wl.N)
+    nsets = 1 if warm else min(64, max(2, int(np.ceil(512e6 / max(set_bytes, 1))) + 1))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    xs = [torch.randn(wl.M, wl.K, device="cuda", dtype=dt, generator=g) for _ in range(nsets)]
+    ws = [(0.02 * torch.randn(wl.N, wl.K, device="cuda", dtype=torch.float32, generator=g)).to(dt)
+          for _ in range(nsets)]
+    ys = [torch.empty(wl.M, wl.N, device="cuda", dtype=dt) for _ in range(nsets)]
+
+    def step(i):
+        k = i % nsets
+        torch.mm(xs[k], ws[k].t(), out=ys[k])
+
+    for i in range(warmup):
+        step(i)
+    return time_trials(step, steps)["median"]
+
+
 def time_trials(step, steps, min_trials=20):
     """Times exactly `steps` calls of step(i) as at least `min_trials` trials
     of equal length (the last one takes the remainder), each bracketed by
@@ -483,22 +508,39 @@ def backward_work(wl):
             "bytes": 2 * (2 * wl.M * wl.K + 2 * wl.N * wl.Kc + wl.M * wl.N)}
 
 
-def time_backward(wl, steps, warmup):
+def time_backward(wl, steps, warmup, warm=False):
+    """ss1_backward (dx and dW_c) per call, and the dense layer's two backward
+    GEMMs at the same shapes; cold (default): rotating sets of every operand
+    and output totalling over 512 MB.  Returns (seconds, dense seconds, sets)."""
     import torch
     import sketched_parameter_sharing_amd as ss1
     from ss1_inputs import make_inputs, draw, f32_to_bf16_bits
     inp = make_inputs(wl)
     p = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
-    x, w = to_dev(inp.x_bits, "bf16"), to_dev(inp.w_bits, "bf16")
-    dy = to_dev(f32_to_bf16_bits(draw("normal", wl.x_seed + 7, (wl.M, wl.N))), "bf16")
-    dx, dw = torch.empty_like(x), torch.empty_like(w)
-    t = time_events(lambda: ss1.backward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, dy, dx=dx, dW_c=dw),
-                    steps, warmup)
+    x0, w0 = to_dev(inp.x_bits, "bf16"), to_dev(inp.w_bits, "bf16")
+    dy0 = to_dev(f32_to_bf16_bits(draw("normal", wl.x_seed + 7, (wl.M, wl.N))), "bf16")
+    set_bytes = 2 * (2 * wl.M * wl.K + 2 * wl.N * wl.Kc + wl.M * wl.N)
+    nsets = 1 if warm else min(16, max(2, int(np.ceil(512e6 / set_bytes)) + 1))
+    sets = [(x0, w0, dy0)] + [(x0.clone(), w0.clone(), dy0.clone()) for _ in range(nsets - 1)]
+    outs = [(torch.empty_like(x0), torch.empty_like(w0)) for _ in range(nsets)]
+
+    def step(i):
+        x, w, dy = sets[i % nsets]
+        dx, dw = outs[i % nsets]
+        ss1.backward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, dy, dx=dx, dW_c=dw)
+
+    t = time_events_i(step, steps, warmup)
     # the dense layer's backward at the same shapes: dx = dy W, dW = dy^T x
-    W = to_dev(f32_to_bf16_bits(draw("normal002", wl.w_seed, (wl.N, wl.K))), "bf16")
-    dyt = dy.t().contiguous()
-    t_dense = time_events(lambda: (torch.matmul(dy, W), torch.matmul(dyt, x)), steps, warmup)
-    return t, t_dense
+    W0 = to_dev(f32_to_bf16_bits(draw("normal002", wl.w_seed, (wl.N, wl.K))), "bf16")
+    dsets = [(dy, dy.t().contiguous(), x, W0 if k == 0 else W0.clone()) for k, (x, _, dy) in enumerate(sets)]
+
+    def dense(i):
+        dy, dyt, x, W = dsets[i % nsets]
+        torch.matmul(dy, W)
+        torch.matmul(dyt, x)
+
+    t_dense = time_events_i(dense, steps, warmup)
+    return t, t_dense, nsets
 
 
 def time_project(wl, steps, warmup, warm):
@@ -613,18 +655,37 @@ def time_events(fn, steps, warmup):
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def time_mlp(c, steps, warmup, row_chunk):
+def time_mlp(c, steps, warmup, row_chunk, warm=False):
+    """ss1_mlp_forward per call; cold (default): rotating sets of x, both
+    weights, h and y totalling over 512 MB, so every call reads its operands
+    from HBM.  Returns (seconds per call, sets)."""
     import torch
     import sketched_parameter_sharing_amd as ss1
-    x, up, down = make_mlp(c)
-    h = torch.empty((min(row_chunk, x.shape[0]), up[0].shape[0]), dtype=x.dtype, device="cuda")
-    y = torch.empty((x.shape[0], down[0].shape[0]), dtype=x.dtype, device="cuda")
-    return time_events(lambda: ss1.mlp_forward(x, up, down, h=h, y=y), steps, warmup)
+    x0, up0, down0 = make_mlp(c)
+    R = min(row_chunk, x0.shape[0])
+    set_bytes = 2 * (x0.numel() + up0[0].numel() + down0[0].numel() + R * up0[0].shape[0]
+                     + x0.shape[0] * down0[0].shape[0])
+    nsets = 1 if warm else min(16, max(2, int(np.ceil(512e6 / set_bytes)) + 1))
+    sets = []
+    for k in range(nsets):
+        x = x0 if k == 0 else x0.clone()
+        up = up0 if k == 0 else (up0[0].clone(),) + tuple(up0[1:])
+        down = down0 if k == 0 else (down0[0].clone(),) + tuple(down0[1:])
+        h = torch.empty((R, up0[0].shape[0]), dtype=x0.dtype, device="cuda")
+        y = torch.empty((x0.shape[0], down0[0].shape[0]), dtype=x0.dtype, device="cuda")
+        sets.append((x, up, down, h, y))
+
+    def step(i):
+        x, up, down, h, y = sets[i % nsets]
+        ss1.mlp_forward(x, up, down, h=h, y=y)
+
+    return time_events_i(step, steps, warmup), nsets
 
 
-def time_dense_mlp(steps, warmup, m=MLP_SHAPE):
+def time_dense_mlp(steps, warmup, m=MLP_SHAPE, warm=False):
     """The dense pair at the same shapes: torch (hipBLASLt) bf16 matmuls and
-    torch's erf GELU, weights [out][in] as a linear layer's."""
+    torch's erf GELU, weights [out][in] as a linear layer's; cold (default)
+    over rotating sets of x, both weights and y like time_mlp."""
     import torch
     from ss1_inputs import draw, f32_to_bf16_bits
     M, K, N1, N2 = m["M"], m["K"], m["N1"], m["N2"]
@@ -632,8 +693,16 @@ def time_dense_mlp(steps, warmup, m=MLP_SHAPE):
     w1 = to_dev(f32_to_bf16_bits(draw("normal002", 0x5f01, (N1, K))), "bf16")
     w2 = to_dev(f32_to_bf16_bits(draw("normal002", 0x5f02, (N2, N1))), "bf16")
     w1t, w2t = w1.t().contiguous(), w2.t().contiguous()
+    set_bytes = 2 * (M * K + 2 * N1 * K + M * N1 + M * N2)
+    nsets = 1 if warm else min(16, max(2, int(np.ceil(512e6 / set_bytes)) + 1))
+    sets = [(x, w1t, w2t)] + [(x.clone(), w1t.clone(), w2t.clone()) for _ in range(nsets - 1)]
     gelu = torch.nn.GELU()
-    return time_events(lambda: torch.matmul(gelu(torch.matmul(x, w1t)), w2t), steps, warmup)
+
+    def step(i):
+        a, b, c = sets[i % nsets]
+        torch.matmul(gelu(torch.matmul(a, b)), c)
+
+    return time_events_i(step, steps, warmup)
 
 
 def cpu_baseline_mlp(c, budget_s=10.0, m=MLP_SHAPE):
@@ -741,6 +810,8 @@ def main():
     ap.add_argument("--op", default="forward", choices=["forward", "project", "mlp", "fp8", "fp8a", "backward"])
     ap.add_argument("--mlp-c", type=int, default=4, help="compression of the timed MLP pair (op mlp)")
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
+    ap.add_argument("--mlp-only", action="store_true",
+                    help="op mlp: time only the pair at --mlp-c and --row-chunk and the dense pair (for profiling)")
     ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "generic", "band", "fold"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
@@ -748,6 +819,8 @@ def main():
                     help="capture the timed calls in one HIP graph (forward and fp8 ops): no host launch "
                          "cost in the timed region, for microsecond decode layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the dense layer of the same shape beside the forward")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the machine-rate probes (roofline against spec peaks only); for profiler runs")
     ap.add_argument("--sweep", default=None, help="also time every workload, JSON lines into this file")
@@ -814,6 +887,10 @@ def main():
             # the fold kernel multiplies by the expanded weight: its matrix
             # cores execute the dense FLOP count, c times the algorithmic one
             rec["config"]["executed_mfma_tflops"] = wk["dense_flops"] / t / 1e12
+        if not args.no_dense:
+            td = time_dense_layer(wl, max(20, steps // 2), max(5, warmup // 2), args.warm)
+            rec["config"]["dense_layer_ms"] = td * 1e3
+            rec["config"]["speedup_vs_dense_layer"] = td / t
         return rec, wl
 
     def measure_project(name, steps, warmup):
@@ -869,14 +946,21 @@ def main():
 
     if args.op == "mlp":
         c = args.mlp_c
-        t = time_mlp(c, args.steps, args.warmup, args.row_chunk)
+        t, nsets = time_mlp(c, args.steps, args.warmup, args.row_chunk, args.warm)
         wk = mlp_work(c)
-        t_dense = time_dense_mlp(max(20, args.steps // 2), max(5, args.warmup // 2))
+        t_dense = time_dense_mlp(max(20, args.steps // 2), max(5, args.warmup // 2), warm=args.warm)
         sweep = []
-        for cc in (2, 4, 8):
-            tc = t if cc == c else time_mlp(cc, max(20, args.steps // 2), max(5, args.warmup // 2), args.row_chunk)
+        for cc in ((c,) if args.mlp_only else (2, 4, 8)):
+            tc = t if cc == c else time_mlp(cc, max(20, args.steps // 2), max(5, args.warmup // 2), args.row_chunk,
+                                            args.warm)[0]
             sweep.append({"c": cc, "BK": mlp_bk(cc), "ms": tc * 1e3, "dense_equiv_tflops": mlp_work(cc)["dense_flops"] / tc / 1e12,
                           "speedup_vs_dense": t_dense / tc})
+        chunks = []
+        for R in (() if args.mlp_only else (8192, 4096, 2048, 1024)):
+            if R == args.row_chunk:
+                continue
+            tr = time_mlp(c, max(20, args.steps // 2), max(5, args.warmup // 2), R, args.warm)[0]
+            chunks.append({"row_chunk": R, "ms": tr * 1e3})
         t_f = wk["compressed_flops"] / PEAK_MFMA_BF16
         t_b = wk["bytes"] / PEAK_HBM
         mf = {"bound": "mfma", "achieved": wk["compressed_flops"] / t / 1e12, "peak": PEAK_MFMA_BF16 / 1e12,
@@ -886,8 +970,10 @@ def main():
             r["frac"] = r["achieved"] / r["peak"]
         roof = dict(mf if t_f >= t_b else hb)
         roof["other"] = hb if t_f >= t_b else mf
-        roof.update({"traffic": None, "t_lower_us": max(t_f, t_b) * 1e6,
+        roof.update({"traffic": recorded_traffic(f"mlp:gpt2l_mlp_pair_c{c}_r{args.row_chunk}", "fold"),
+                     "t_lower_us": max(t_f, t_b) * 1e6,
                      "note": "whole pair (both projections and the GELU epilogue) per call"})
+        roof["traffic_vs_algorithmic"] = roof["traffic"] / wk["bytes"] if roof["traffic"] else None
         rec = {
             "metric": "SS1 MLP pair (up, GELU, down) dense-equiv TFLOP/s + % of MFMA/HBM roofline",
             "value": wk["dense_flops"] / t / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -896,8 +982,9 @@ def main():
             "data": "synthetic (seeded N(0,1) inputs, N(0,0.02) compressed weights, seeded balanced plans)",
             "config": {"workload": f"gpt2l_mlp_pair_c{c}", **MLP_SHAPE, "BK": mlp_bk(c), "c": c,
                        "row_chunk": args.row_chunk,
-                       "cache": "warm (one buffer set; h chunk stays in the MALL)",
-                       "dense_pair_ms": t_dense * 1e3, "c_sweep": sweep},
+                       "cache": "warm (one buffer set)" if args.warm else f"cold ({nsets} rotating buffer sets)",
+                       "dense_pair_ms": t_dense * 1e3, "speedup_vs_dense": t_dense / t, "c_sweep": sweep,
+                       "row_chunk_sweep": chunks},
             "roofline": roof,
         }
         rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_mlp(c)
@@ -907,7 +994,7 @@ def main():
     if args.op == "backward":
         name = args.workload or HEADLINE
         wl = WORKLOADS[name]
-        t, t_dense = time_backward(wl, args.steps, args.warmup)
+        t, t_dense, nsets = time_backward(wl, args.steps, args.warmup, args.warm)
         wk = backward_work(wl)
         mf = {"bound": "mfma", "achieved": wk["flops"] / t / 1e12, "peak": PEAK_MFMA_BF16 / 1e12,
               "unit": "TFLOP/s"}
@@ -916,7 +1003,9 @@ def main():
         hb["frac"] = hb["achieved"] / hb["peak"]
         t_f, t_b = wk["flops"] / PEAK_MFMA_BF16, wk["bytes"] / PEAK_HBM
         roof = dict(mf if t_f >= t_b else hb)
-        roof.update({"other": hb if t_f >= t_b else mf, "traffic": None, "t_lower_us": max(t_f, t_b) * 1e6,
+        traffic = recorded_traffic("backward:" + name, "fold")
+        roof.update({"other": hb if t_f >= t_b else mf, "traffic": traffic, "t_lower_us": max(t_f, t_b) * 1e6,
+                     "traffic_vs_algorithmic": traffic / wk["bytes"] if traffic else None,
                      "note": "dx (dense-cost GEMM on the expanded weight) plus dW_c, both kernels per call"})
         rec = {
             "metric": "SS1 layer backward (dx + dW_c) TFLOP/s + % of MFMA/HBM roofline",
@@ -925,7 +1014,8 @@ def main():
             "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded N(0,1) inputs and upstream gradient, N(0,0.02) weights, seeded plan)",
             "config": {"workload": name + "_backward", "M": wl.M, "K": wl.K, "N": wl.N, "c": wl.c,
-                       "BK": wl.BK, "BN": wl.BN, "cache": "warm (one buffer set)",
+                       "BK": wl.BK, "BN": wl.BN,
+                       "cache": "warm (one buffer set)" if args.warm else f"cold ({nsets} rotating buffer sets)",
                        "dense_backward_ms": t_dense * 1e3, "ratio_to_dense": t / t_dense},
             "roofline": roof,
         }
@@ -1004,10 +1094,13 @@ def main():
         hb["frac"] = hb["achieved"] / hb["peak"]
         t_f, t_b = wk["compressed_flops"] / peak8, wk["bytes"] / PEAK_HBM
         roof = dict(mf if t_f >= t_b else hb)
-        roof.update({"other": hb if t_f >= t_b else mf, "traffic": recorded_traffic("fp8a:" + name),
+        roof.update({"other": hb if t_f >= t_b else mf, "traffic": recorded_traffic("fp8a:" + name, "fold8"),
+                     "traffic_vs_algorithmic": None,
                      "t_lower_us": max(t_f, t_b) * 1e6,
                      "note": "per step: x quantized to E4M3 per row, then the fp8 fold (dense fp8 MFMA work "
                              "2*M*N*K; the compressed count is the algorithmic one)"})
+        if roof["traffic"]:
+            roof["traffic_vs_algorithmic"] = roof["traffic"] / wk["bytes"]
         rec = {
             "metric": "SS1 layer with fp8 (E4M3) input and weights on fp8 MFMA: dense-equiv TFLOP/s + % of "
                       "fp8 MFMA/HBM roofline",
