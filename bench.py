@@ -240,7 +240,10 @@ def measured_peaks():
                         128-byte line (a 32-column bf16 tile of a matrix)
       hbm_read_tbs      reads of a 4 GiB buffer, each block its own 2 MiB
       hbm_copy_tbs      torch's device copy of 1 GiB (read + write bytes)
-      lds_read_tbs      ds_read_b128 at conflict-free addresses"""
+      lds_read_tbs      ds_read_b128 at conflict-free addresses, immediate
+                        offsets (few vector instructions per read)
+      lds_read_valu_addr_tbs  the same reads with every address computed in
+                        the loop"""
     import ctypes
     import torch
     here = os.path.join(ROOT, "sketched_parameter_sharing_amd", "libss1_peaks.so")
@@ -288,8 +291,10 @@ def measured_peaks():
     t = timed(lambda: dst.copy_(src))
     out["hbm_copy_tbs"] = 2 * (1 << 30) / t / 1e12
     li = 2048
-    t = timed(lambda: lib.ss1_peak_lds(256 * 8, li, vp(sink.data_ptr()), vp(st)))
+    t = timed(lambda: lib.ss1_peak_lds(256 * 8, li, 1, vp(sink.data_ptr()), vp(st)))
     out["lds_read_tbs"] = 256 * 8 * 256 * li * 8 * 16 / t / 1e12
+    t = timed(lambda: lib.ss1_peak_lds(256 * 8, li, 0, vp(sink.data_ptr()), vp(st)))
+    out["lds_read_valu_addr_tbs"] = 256 * 8 * 256 * li * 8 * 16 / t / 1e12
     del buf
     return out
 

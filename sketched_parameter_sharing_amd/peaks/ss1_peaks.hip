@@ -104,18 +104,34 @@ __global__ __launch_bounds__(256) void peak_dma_kernel(const uint8_t* __restrict
 }
 
 // LDS reads: each lane reads 16 bytes per ds_read_b128 at conflict-free
-// addresses, `iters` rounds of 8 reads.
-__global__ __launch_bounds__(256) void peak_lds_kernel(int iters, uint32_t* sink) {
+// addresses (the 64 lanes of a wave read 1 KB of consecutive bytes), `iters`
+// rounds of 8 reads.  mode 0 computes every address in the loop (about five
+// vector instructions per read); mode 1 takes one base per round and the 8
+// reads at immediate offsets 4 KB apart (two vector instructions per read: the
+// XORs that keep all 16 bytes live).
+__global__ __launch_bounds__(256) void peak_lds_kernel(int iters, int mode, uint32_t* sink) {
     __shared__ __attribute__((aligned(16))) uint4 s[4096];
     for (int i = threadIdx.x; i < 4096; i += blockDim.x) s[i] = make_uint4(i, i + 1, i + 2, i + 3);
     __syncthreads();
     uint32_t x = 0;
     const int t = threadIdx.x;
-    for (int it = 0; it < iters; ++it) {
+    if (mode == 0) {
+        for (int it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint4 v = s[(t + j * 256 + it) & 4095];
-            x ^= v.x ^ v.w;
+            for (int j = 0; j < 8; ++j) {
+                const uint4 v = s[(t + j * 256 + it) & 4095];
+                x ^= v.x ^ v.w;
+            }
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            // base row of this round: 0..7 (x 256 entries), so base + 7*256 + t < 4096
+            const uint4* q = s + (((it * 5) & 7) << 8) + t;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint4 v = q[j * 256];
+                x ^= v.x ^ v.y ^ v.z ^ v.w;
+            }
         }
     }
     if (x == 0x9E3779B9u) sink[blockIdx.x] = x;
@@ -146,8 +162,9 @@ int ss1_peak_dma(int blocks, int threads, const void* buf, uint32_t win, int rep
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-int ss1_peak_lds(int blocks, int iters, uint32_t* sink, void* stream) {
-    hipLaunchKernelGGL(peak_lds_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+int ss1_peak_lds(int blocks, int iters, int mode, uint32_t* sink, void* stream) {
+    hipLaunchKernelGGL(peak_lds_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, mode,
+                       sink);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
