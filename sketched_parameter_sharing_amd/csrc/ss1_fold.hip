@@ -433,14 +433,16 @@ __global__ __launch_bounds__(512) void fold8_kernel(const uint8_t* __restrict__ 
         }
     };
 
-    // operands: lane l reads row (block base + l%16), bytes 32q .. 32q+31 of
-    // the stage (q = l/16): x pieces 2q, 2q+1 of its 128-byte row; weight
-    // half q/2, pieces 2(q%2), 2(q%2)+1 of its 64-byte row
+    // operands: lane l (q = l/16) holds row (block base + l%16) at stage
+    // inputs 16q .. 16q+15 and 64+16q .. 64+16q+15: x pieces q and q+4 of its
+    // 128-byte row, and piece q of its 64-byte row in each weight half.  The
+    // MFMA sums over k, so any assignment of the 128 inputs to lanes and
+    // registers serves as long as both operands use the same one; this one
+    // has the four quarter-waves of each read on consecutive pieces.
     const int fr = lane & 15;
     const int q = lane >> 4;
     const int keyx = swz_key<RBX>(fr);
     const int keyw = swz_key<RBW>(fr);
-    const int hq = q >> 1;
     const int sg_gl = (wn * TNW + (fr >> 2) * 4 * FN) / BN;
 
     f32x4 acc[FN][FM];
@@ -455,25 +457,26 @@ __global__ __launch_bounds__(512) void fold8_kernel(const uint8_t* __restrict__ 
         else dma_stage_barrier<0>();
         if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
         const uint8_t* S = fold_smem + buf * SB;
-        const int jq = (s * KS + 64 * hq) / BK;        // input chunk of this lane's weight half
-        const uint32_t sx = s_sgn[sg_gl * J + jq] ? 0x80808080u : 0u;
+        // signs of the input chunks of the stage's two 64-input halves
+        const uint32_t sx0 = s_sgn[sg_gl * J + (s * KS) / BK] ? 0x80808080u : 0u;
+        const uint32_t sx1 = s_sgn[sg_gl * J + (s * KS + 64) / BK] ? 0x80808080u : 0u;
         i32x8 wv[FN];
 #pragma unroll
         for (int i = 0; i < FN; ++i) {
-            const uint8_t* W = S + SX + hq * SWH + (wn * TNW + i * 16 + fr) * RBW;
-            const uint4 a = *reinterpret_cast<const uint4*>(W + (((2 * (q & 1)) ^ keyw) << 4));
-            const uint4 b = *reinterpret_cast<const uint4*>(W + (((2 * (q & 1) + 1) ^ keyw) << 4));
-            wv[i] = i32x8{static_cast<int>(a.x ^ sx), static_cast<int>(a.y ^ sx), static_cast<int>(a.z ^ sx),
-                          static_cast<int>(a.w ^ sx), static_cast<int>(b.x ^ sx), static_cast<int>(b.y ^ sx),
-                          static_cast<int>(b.z ^ sx), static_cast<int>(b.w ^ sx)};
+            const uint8_t* W = S + SX + (wn * TNW + i * 16 + fr) * RBW + ((q ^ keyw) << 4);
+            const uint4 a = *reinterpret_cast<const uint4*>(W);
+            const uint4 b = *reinterpret_cast<const uint4*>(W + SWH);
+            wv[i] = i32x8{static_cast<int>(a.x ^ sx0), static_cast<int>(a.y ^ sx0), static_cast<int>(a.z ^ sx0),
+                          static_cast<int>(a.w ^ sx0), static_cast<int>(b.x ^ sx1), static_cast<int>(b.y ^ sx1),
+                          static_cast<int>(b.z ^ sx1), static_cast<int>(b.w ^ sx1)};
         }
         // token operands one 16-row block at a time (the next one read while
         // the current block's MFMAs run): 128 accumulators, 32 weight and 16
         // token registers fit the 256 a wave has at two waves per SIMD
         auto xread = [&](int jj) {
             const uint8_t* X = S + (wm * TMW + jj * 16 + fr) * RBX;
-            const uint4 a = *reinterpret_cast<const uint4*>(X + (((2 * q) ^ keyx) << 4));
-            const uint4 b = *reinterpret_cast<const uint4*>(X + (((2 * q + 1) ^ keyx) << 4));
+            const uint4 a = *reinterpret_cast<const uint4*>(X + ((q ^ keyx) << 4));
+            const uint4 b = *reinterpret_cast<const uint4*>(X + (((q + 4) ^ keyx) << 4));
             return i32x8{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(a.z), static_cast<int>(a.w),
                          static_cast<int>(b.x), static_cast<int>(b.y), static_cast<int>(b.z), static_cast<int>(b.w)};
         };
