@@ -75,7 +75,9 @@ typedef enum {
     SS1_ALGO_GENERIC = 3,  /* any dtype and chunking: LDS-tiled FMA kernel             */
     SS1_ALGO_BAND = 4,     /* bf16, short rows: a band of input rows held in LDS        */
     SS1_ALGO_FOLD = 5,     /* bf16: W_c expanded on chip, one dense-shaped MFMA GEMM    */
-    SS1_ALGO_GEMV = 6      /* bf16: M <= 4, matrix-vector kernel, W_c streamed once     */
+    SS1_ALGO_GEMV = 6,     /* bf16: M <= 4, matrix-vector kernel, W_c streamed once     */
+    SS1_ALGO_DECODE = 7    /* bf16: M <= 16 with 16 input rows in LDS, one group per
+                              block, every weight load in flight, MFMA               */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */
@@ -185,6 +187,12 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *            T = 64 ceil(Kc / (512 Q)) threads take Q = 1 (Kc <= 8192), 2, 4
  *            or 8 slices of 8 compressed columns each.  Each block's weight
  *            loads are all issued before it waits for anything.
+ *   DECODE : BF16, M <= 16, K % 512 == 0, BN in {32, 64}, BK % 32 == 0,
+ *            K/BK <= 1024, and 16 rows of K bf16 plus the group's plan fit
+ *            in one block's LDS (K up to 4096 on gfx950).  One block per
+ *            neuron group: the input rows go to LDS once, every weight load
+ *            of a wave is issued before it waits, the sketch rounded to bf16
+ *            feeds bf16 MFMAs (the same y as SMALLM up to summation order).
  *   GENERIC: any valid call
  *   BAND   : BF16, BK % 32 == 0, BN in {32, 64, 128}, and 32 input rows of K
  *            bf16 (plus the plan) fit in one block's LDS (K up to about 2400)
@@ -193,8 +201,8 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *            Multiplies x by the expanded weight W_c S_g (built in LDS from
  *            W_c, never stored): the same y as the sketch kernels up to
  *            rounding (no bf16 rounding of a sketch), dense MFMA work.
- * ss1_forward picks GEMV for M <= 4 where it applies, else SMALLM for
- * M <= 16, and FOLD for large M where its modelled time is below the sketch
+ * ss1_forward picks GEMV for M <= 4 where it applies, else DECODE, else
+ * SMALLM for M <= 16, and FOLD for large M where its modelled time is below the sketch
  * kernels' (ss1_select_algo reports the choice).
  * Reproducibility: a row of y depends only on that row of x, but its bits
  * depend on the kernel that runs, and the choice depends on M (and on the

@@ -75,11 +75,13 @@ double sketch_estimate_us(const ForwardArgs& a) {
 }
 
 // The kernel ss1_forward picks for a validated call: decode shapes go to the
-// matrix-vector kernel (M <= 4) or the small-M kernel; otherwise the fold kernel when its estimate is clearly
-// (10%) below the sketch kernels', else the band kernel where a band of input
-// rows fits in LDS, else the fused kernel.
+// matrix-vector kernel (M <= 4), the decode kernel (up to 16 rows of x in
+// LDS) or the small-M kernel; otherwise the fold kernel when its estimate is
+// clearly (10%) below the sketch kernels', else the band kernel where a band
+// of input rows fits in LDS, else the fused kernel.
 int32_t auto_algo(const ForwardArgs& a) {
     if (ss1::gemv_supported(a)) return SS1_ALGO_GEMV;
+    if (ss1::decode_supported(a)) return SS1_ALGO_DECODE;
     if (ss1::smallm_supported(a)) return SS1_ALGO_SMALLM;
     if (ss1::fold_supported(a) && ss1::fold_estimate_us(a) < 0.9 * sketch_estimate_us(a)) return SS1_ALGO_FOLD;
     if (ss1::band_supported(a, 48)) return SS1_ALGO_BAND;
@@ -105,6 +107,7 @@ ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
     switch (algo) {
         case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
         case SS1_ALGO_GEMV: return ss1::launch_gemv(a);
+        case SS1_ALGO_DECODE: return ss1::launch_decode(a);
         case SS1_ALGO_BAND: return ss1::launch_band(a);
         case SS1_ALGO_FUSED: return ss1::launch_fused(a);
         case SS1_ALGO_FOLD: return ss1::launch_fold(a);
@@ -131,6 +134,9 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_GEMV:
             if (!ss1::gemv_supported(a)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_gemv(a);
+        case SS1_ALGO_DECODE:
+            if (!ss1::decode_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_decode(a);
         case SS1_ALGO_BAND:
             if (!ss1::band_supported(a, 32)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_band(a);

@@ -1,0 +1,234 @@
+// Decode forward for up to 16 tokens whose input rows fit in LDS (16*K bf16):
+// y = z_g W_c,g^T per group, the sketch z_g of the SS1 summary page,
+// "Approach" (signed sums of the input chunks that hash to each compressed
+// chunk), rounded to bf16 and multiplied on the bf16 matrix cores.
+//
+// At 16 tokens the layer moves its compressed weight once (58.7 MB for the
+// Llama-3-8B gate/up projection) and little else, so the kernel is built to
+// keep that stream going: a block is one neuron group (BN = 16*RB neurons)
+// and all its compressed columns, 8 waves each taking an eighth of the
+// columns.  Each wave issues all of its weight loads (RB x 8 loads of 16 bytes
+// per lane, 32-wide k-steps) before it waits for anything; the input rows
+// reach LDS once per block by direct buffer-to-LDS loads (rows past M read
+// zeros) and the sketch of every k-step is formed from LDS, so no input
+// element is gathered from L2 per k-step.  The plan entries are read into
+// registers first, since loads return in the order issued.
+//
+// Per k-step a lane forms 8 sketch elements (token lane%16, columns
+// 8*(lane/16) ..) in float32 from the c source chunks, rounds them to bf16,
+// and feeds RB MFMAs 16x16x32 with the weight operand of each 16-neuron row
+// block (read straight in the operand layout).  The partial tiles of the 8
+// waves are summed in LDS in wave order, and each lane stores 4 consecutive
+// neurons of one token (8 bytes).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ss1_device.h"
+#include "ss1_dma.h"
+#include "ss1_internal.h"
+
+namespace ss1 {
+
+namespace {
+
+using namespace dev;
+
+constexpr int kDecWaves = 8;
+constexpr int kDecSteps = 8;  // k-steps per wave whose weight loads are in flight together
+
+// LDS of a decode launch: the x tile (or the wave partials, which reuse it)
+// and the group's plan (J entries plus Jc counters).
+size_t decode_lds(int64_t K, const Dims& d) {
+    const size_t xb = static_cast<size_t>(16) * K * 2;
+    const size_t red = static_cast<size_t>(d.BN / 16) * kDecWaves * 64 * 16;
+    return std::max(xb, red) + static_cast<size_t>(d.J + d.Jc) * 4;
+}
+
+template <int RB, int C_T, bool FROM_HASH>
+__global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w,
+                                                                const int32_t* __restrict__ pi,
+                                                                const int8_t* __restrict__ ps,
+                                                                uint16_t* __restrict__ y, int M, int K, int N,
+                                                                int J, int Jc, int c_rt, int BK, int act) {
+    constexpr int NW = kDecWaves;
+    constexpr int BN = 16 * RB;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dec_smem[];
+    const int xbytes = 16 * K * 2;
+    const int redbytes = RB * NW * 64 * 16;
+    uint16_t* sx = reinterpret_cast<uint16_t*>(dec_smem);
+    f32x4* red = reinterpret_cast<f32x4*>(dec_smem);  // [RB][NW][64], over the x tile once it is read
+    uint32_t* s_src = reinterpret_cast<uint32_t*>(dec_smem + (xbytes > redbytes ? xbytes : redbytes));
+    int* s_cnt = reinterpret_cast<int*>(s_src + J);
+
+    const int c = (C_T > 0) ? C_T : c_rt;
+    const int g = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int Kc = Jc * BK;
+
+    // (1) this thread's plan entries, first: loads return in the order issued
+    int32_t iv[kPlanPerThread];
+    int8_t sv[kPlanPerThread];
+    fetch_plan_regs<kPlanPerThread>(pi, ps, g, J, iv, sv);
+
+    // (2) the input rows into LDS.  Row t holds K bf16 as K/8 pieces of 16
+    // bytes; piece p sits at slot p ^ t (t < 16), so the 16 lanes that read
+    // one column of rows 0..15 hit 16 distinct bank groups.  K % 512 == 0:
+    // a row is a whole number of wave-wide loads (64 pieces each), and the 16
+    // rows' loads split evenly over the 8 waves.
+    const int lpr = K / 512;  // wave-wide loads per row
+    const i32x4 xrs = dma_rsrc(x, static_cast<uint32_t>(M * K * 2));
+    const uint32_t xlds = lds_address(dec_smem);
+    for (int i = wave; i < 16 * lpr; i += NW) {
+        const int t = i / lpr;
+        const int pb = (i - t * lpr) * 64;
+        const uint32_t voff = static_cast<uint32_t>(t * K * 2 + ((pb + lane) ^ t) * 16);
+        lds_dma16(xrs, xlds + static_cast<uint32_t>(i * 1024), voff, 0u);
+    }
+
+    // (3) this wave's weight loads: k-steps [sb, se) of the group's Kc/32.
+    // Lane l reads row l%16 of a 16-row block at columns 8*(l/16) of the step,
+    // the MFMA operand layout itself (16 rows x 64 bytes per load; measured
+    // slightly ahead of reading 64 contiguous bytes per lane quad and
+    // permuting across lanes); a step past se reads zeros.
+    const int S = Kc / 32;
+    const int sb = (S * wave) / NW;
+    const int se = (S * (wave + 1)) / NW;
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w + static_cast<size_t>(g) * BN * Kc, static_cast<uint32_t>(BN * Kc * 2));
+    const uint32_t wl = static_cast<uint32_t>(((lane & 15) * Kc + (lane >> 4) * 8) * 2);
+    uint4 wv[kDecSteps][RB];
+    auto load_w = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < kDecSteps; ++u)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const uint32_t off = (s0 + u < se)
+                                         ? wl + static_cast<uint32_t>((rb * 16 * Kc + (s0 + u) * 32) * 2)
+                                         : kOutOfRange;
+                wv[u][rb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, kNonTemporal));
+            }
+    };
+    load_w(sb);
+
+    // (4) the plan into LDS from the registers of (1); then every wave's part
+    // of the x tile must have landed (the weight loads may stay in flight)
+    stage_plan_regs<FROM_HASH, kPlanPerThread>(iv, sv, J, Jc, c, BK, s_src, s_cnt);
+    dma_stage_barrier<RB * kDecSteps>();
+
+    // (5) sketch and MFMA per k-step
+    const int tok = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    const uint16_t* xrow = sx + tok * K;
+    f32x4 acc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = sb; s0 < se; s0 += kDecSteps) {
+        if (s0 != sb) load_w(s0);
+        // the sketches of all the batch's steps first (LDS and vector work
+        // only), then the MFMAs in the order the weights arrive
+        uint4 z[kDecSteps];
+#pragma unroll
+        for (int u = 0; u < kDecSteps; ++u) {
+            const int kc = min(s0 + u, se - 1) * 32 + kq;  // compressed column of this lane's 8 elements
+            const int t = kc / BK;
+            const int u0 = kc - t * BK;
+            float a[8];
+            for (int r = 0; r < c; ++r) {
+                const uint32_t e = s_src[t * c + r];
+                const int piece = static_cast<int>(((e & kOffMask) + static_cast<uint32_t>(u0)) >> 3);
+                const uint4 raw = *reinterpret_cast<const uint4*>(xrow + ((piece ^ tok) << 3));
+                acc_bf16x8(a, raw, entry_sign(e), r == 0);
+            }
+            z[u] = pack_bf16x8(a);
+        }
+#pragma unroll
+        for (int u = 0; u < kDecSteps; ++u) {
+            if (s0 + u < se) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[u][rb]),
+                                                                       __builtin_bit_cast(bf16x8, z[u]), acc[rb],
+                                                                       0, 0, 0);
+            }
+        }
+    }
+
+    // (6) partial tiles summed over the waves in wave order; lane l of wave
+    // rb < RB holds neurons rb*16 + 4*(l/16) .. +3 of token l%16
+    lds_barrier();  // every wave is done with the x tile
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) red[(rb * NW + wave) * 64 + lane] = acc[rb];
+    lds_barrier();
+    if (wave < RB) {
+        const f32x4* rp = red + wave * NW * 64;
+        f32x4 sum = rp[lane];
+        for (int v = 1; v < NW; ++v) {
+            const f32x4 p = rp[v * 64 + lane];
+            sum[0] += p[0];
+            sum[1] += p[1];
+            sum[2] += p[2];
+            sum[3] += p[3];
+        }
+        if (tok < M) {
+            const int n = g * BN + wave * 16 + 4 * (lane >> 4);
+            uint2 o;
+            o.x = pack_bf16(apply_act(sum[0], act), apply_act(sum[1], act));
+            o.y = pack_bf16(apply_act(sum[2], act), apply_act(sum[3], act));
+            *reinterpret_cast<uint2*>(y + static_cast<size_t>(tok) * N + n) = o;
+        }
+    }
+}
+
+template <int RB, int C_T, bool FROM_HASH>
+ss1_status launch_decode_cfg(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    const size_t lds = decode_lds(d.K, d);
+    auto kern = &decode_kernel<RB, C_T, FROM_HASH>;
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds)) != hipSuccess)
+        return SS1_ERR_HIP;
+    hipLaunchKernelGGL((decode_kernel<RB, C_T, FROM_HASH>), dim3(static_cast<unsigned>(d.G)), dim3(kDecWaves * 64),
+                       lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
+                       static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y),
+                       static_cast<int>(a.M), static_cast<int>(d.K), static_cast<int>(d.N), static_cast<int>(d.J),
+                       static_cast<int>(d.Jc), d.c, d.BK, a.act);
+    return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
+}
+
+template <int RB, bool FROM_HASH>
+ss1_status launch_decode_rb(const ForwardArgs& a) {
+    if (a.d.c == 2) return launch_decode_cfg<RB, 2, FROM_HASH>(a);
+    return launch_decode_cfg<RB, 0, FROM_HASH>(a);
+}
+
+int max_lds() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
+        return 64 * 1024;
+    return v;
+}
+
+}  // namespace
+
+bool decode_supported(const ForwardArgs& a) {
+    const Dims& d = a.d;
+    if (a.dtype != SS1_BF16 || a.w_fp8 || a.M > 16) return false;
+    if (d.K % 512 != 0 || d.BK % 32 != 0 || (d.BN != 32 && d.BN != 64)) return false;
+    if (d.J > kPlanPerThread * kDecWaves * 64) return false;
+    if (static_cast<double>(d.BN) * d.Kc * 2 >= 2147483648.0) return false;
+    return decode_lds(d.K, d) <= static_cast<size_t>(max_lds());
+}
+
+ss1_status launch_decode(const ForwardArgs& a) {
+    const bool hash = a.form == PlanForm::Hash;
+    if (a.d.BN == 64) return hash ? launch_decode_rb<4, true>(a) : launch_decode_rb<4, false>(a);
+    return hash ? launch_decode_rb<2, true>(a) : launch_decode_rb<2, false>(a);
+}
+
+}  // namespace ss1

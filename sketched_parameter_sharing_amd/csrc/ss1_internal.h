@@ -47,6 +47,9 @@ bool smallm_supported(const ForwardArgs& a);
 // Matrix-vector kernel (ss1_gemv.hip): bf16, M <= 4, BN % 16 == 0, 512 to
 // 65536 compressed columns (fewer for M > 1) and J within twice the block.
 bool gemv_supported(const ForwardArgs& a);
+// Decode kernel (ss1_decode.hip): bf16, M <= 16, K % 512 == 0 with 16 input
+// rows of K bf16 in LDS, BN of 32 or 64, BK % 32 == 0, J <= 1024.
+bool decode_supported(const ForwardArgs& a);
 // Band kernel: the layer's rows are short enough for a band of at least
 // min_rows input rows to sit in LDS.
 bool band_supported(const ForwardArgs& a, int min_rows);
@@ -87,6 +90,7 @@ ss1_status launch_fold8(const void* xq, const float* xs, const void* wq, const f
 ss1_status launch_fused(const ForwardArgs& a);
 ss1_status launch_smallm(const ForwardArgs& a);
 ss1_status launch_gemv(const ForwardArgs& a);
+ss1_status launch_decode(const ForwardArgs& a);
 ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_fold(const ForwardArgs& a);

@@ -183,6 +183,7 @@ def test_bf16_full_size_sampled_rows(name):
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("gpt2l_down", "fused"),
                                        ("llama_gateup_m16", "smallm"), ("llama_down_m16", "smallm"),
+                                       ("llama_gateup_m16", "decode"),
                                        ("llama_gateup_m1", "gemv"), ("llama_down_m1", "gemv"),
                                        ("square_c8_bn128", "fused"), ("square_c1_bn32", "fused"),
                                        ("gpt2l_up", "generic"), ("gpt2s_up", "band"),
@@ -191,7 +192,7 @@ def test_bf16_full_size_sampled_rows(name):
                                        ("square_c8_bn32", "fold")])
 def test_bf16_integer_bit_exact(name, algo):
     wl = WORKLOADS[name]
-    wl = wl.with_m(min(wl.M, {"smallm": 16, "gemv": 4}.get(algo, 300)))
+    wl = wl.with_m(min(wl.M, {"smallm": 16, "decode": 16, "gemv": 4}.get(algo, 300)))
     inp = make_inputs(wl, integer=True)
     y = run(wl, inp, device_plan(wl), algo=algo)
     h, s = oracle_plan(wl)
@@ -209,9 +210,44 @@ def test_smallm_parity(name, M):
     p = device_plan(wl)
     y = run(wl, inp, p, algo="smallm")
     check_bf16(wl, inp, y)
-    if M > 4:
-        ya = run(wl, inp, p)  # auto picks the same kernel for 4 < M <= 16
+    if M > 4 and kernel_of(wl, "auto") == "smallm":
+        ya = run(wl, inp, p)  # auto picks the same kernel
         assert torch.equal(y, ya)
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 9, 16])
+def test_decode_parity(M):
+    # Llama-3-8B gate/up at decode sizes: 16 input rows of 4096 in LDS, one
+    # group per block; rows past M read zeros and are not stored
+    wl = WORKLOADS["llama_gateup_m16"].with_m(M)
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="decode")
+    check_bf16(wl, inp, y, kernel="decode")
+    assert torch.equal(y, run(wl, inp, p, algo="decode", use_index=True))
+    if M > 4:
+        assert kernel_of(wl, "auto") == "decode"
+        assert torch.equal(y, run(wl, inp, p))
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [(16, 1024, 4096, 2, 32, 32), (11, 2048, 8192, 4, 64, 64),
+                                           (7, 512, 1024, 1, 32, 64), (16, 3072, 2048, 3, 64, 64),
+                                           (3, 1536, 768, 8, 32, 32), (5, 4096, 1024, 1, 64, 64)])
+def test_decode_shapes(M, K, N, c, BK, BN):
+    # both group widths, runtime c (3, 4, 8) and compile-time c (2), c = 1, Kc
+    # that does not split evenly over the 8 waves (some waves get no k-step),
+    # and 16 k-steps per wave (two batches of weight loads); against the
+    # oracle and bit-exact on integer inputs
+    wl = Workload("decode", 9, 6, M, K, N, c, BK, BN, "bf16")
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run(wl, inp, p, algo="decode")
+    check_bf16(wl, inp, y, kernel="decode")
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, p, algo="decode")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
 
 
 @pytest.mark.parametrize("M,K,N,BN", [(7, 1024, 12288, 32), (16, 2048, 12288, 128), (3, 4096, 14336, 64)])
@@ -293,7 +329,7 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
     inp = make_inputs(wl)
     p = device_plan(wl)
     ys = {}
-    for algo in ("auto", "fused", "smallm", "gemv", "band", "generic", "fold"):
+    for algo in ("auto", "fused", "smallm", "gemv", "decode", "band", "generic", "fold"):
         try:
             ys[algo] = run(wl, inp, p, algo=algo)
         except ss1.SS1Error as e:
@@ -304,6 +340,7 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
 
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("llama_down_m16", "smallm"),
+                                       ("llama_gateup_m16", "decode"),
                                        ("gpt2l_up", "generic"), ("tiny", "generic"),
                                        ("gpt2s_up", "band"), ("gpt2l_up", "band"),
                                        ("gpt2s_up", "fold"), ("llama_gateup_m4096", "fold")])
