@@ -188,7 +188,7 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *            or 8 slices of 8 compressed columns each.  Each block's weight
  *            loads are all issued before it waits for anything.
  *   DECODE : BF16, M <= 16, K % 512 == 0, BN in {32, 64}, BK % 32 == 0,
- *            K/BK <= 1024, and 16 rows of K bf16 plus the group's plan fit
+ *            K/BK <= 2048, and 16 rows of K bf16 plus the group's plan fit
  *            in one block's LDS (K up to 4096 on gfx950).  One block per
  *            neuron group: the input rows go to LDS once, every weight load
  *            of a wave is issued before it waits, the sketch rounded to bf16

@@ -48,7 +48,7 @@ bool smallm_supported(const ForwardArgs& a);
 // 65536 compressed columns (fewer for M > 1) and J within twice the block.
 bool gemv_supported(const ForwardArgs& a);
 // Decode kernel (ss1_decode.hip): bf16, M <= 16, K % 512 == 0 with 16 input
-// rows of K bf16 in LDS, BN of 32 or 64, BK % 32 == 0, J <= 1024.
+// rows of K bf16 in LDS, BN of 32 or 64, BK % 32 == 0, J <= 2048.
 bool decode_supported(const ForwardArgs& a);
 // Band kernel: the layer's rows are short enough for a band of at least
 // min_rows input rows to sit in LDS.
