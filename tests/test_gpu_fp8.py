@@ -39,8 +39,12 @@ def to_host(t):
 
 
 @pytest.mark.parametrize("N,Kc,dtype", [(64, 128, "bf16"), (130, 384, "bf16"), (96, 2048, "f32"),
-                                        (3, 2, "bf16"), (14336, 2048, "bf16")])
+                                        (3, 2, "bf16"), (14336, 2048, "bf16"), (7, 4096, "bf16"),
+                                        (5, 4104, "bf16"), (2, 16384, "bf16"), (3, 20000, "f32")])
 def test_quantize_bit_exact(N, Kc, dtype):
+    # rows of a multiple of 8 elements: one block per row with up to 16384
+    # elements in registers (20000: the rest read twice); other lengths the
+    # scalar kernel
     w = draw("normal002", 0x5800 + N + Kc, (N, Kc))
     w[min(1, N - 1)] = 0.0                        # an all-zero row
     if N > 2:
