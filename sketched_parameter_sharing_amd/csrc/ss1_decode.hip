@@ -8,7 +8,8 @@
 // keep that stream going: a block is one neuron group (BN = 16*RB neurons)
 // and all its compressed columns, 16 waves each taking a sixteenth of the
 // columns.  Each wave issues all of its weight loads (RB x 4 loads of 16 bytes
-// per lane, 32-wide k-steps) before it waits for anything; the input rows
+// per lane, 32-wide k-steps, whole 128-byte lines) before it waits for
+// anything; the input rows
 // reach LDS once per block by direct buffer-to-LDS loads (rows past M read
 // zeros) and the sketch of every k-step is formed from LDS, so no input
 // element is gathered from L2 per k-step.  The plan entries are read into
@@ -17,7 +18,10 @@
 // Per k-step a lane forms 8 sketch elements (token lane%16, columns
 // 8*(lane/16) ..) in float32 from the c source chunks, rounds them to bf16,
 // and feeds RB MFMAs 16x16x32 with the weight operand of each 16-neuron row
-// block (read straight in the operand layout).  The partial tiles of the 16
+// block.  The weights of two consecutive k-steps (64 columns, one 128-byte
+// line per row) of a row block come in two loads of 8 rows each, and two
+// lane rotations inside each 16-lane row turn them into the two steps'
+// operands.  The partial tiles of the 16
 // waves are summed in LDS in wave order, and each lane stores 4 consecutive
 // neurons of one token (8 bytes).
 #include <hip/hip_runtime.h>
@@ -41,6 +45,43 @@ using namespace dev;
 // are the same
 constexpr int kDecWaves = 16;
 constexpr int kDecSteps = 4;  // k-steps per wave whose weight loads are in flight together
+static_assert(kDecSteps % 2 == 0, "k-steps come in pairs of one 128-byte line");
+
+// Lane l of a 16-lane row takes the value of lane (l + 8) % 16 (DPP
+// row_ror:8, a VALU operand modifier; no LDS traffic).  Every lane is a
+// valid source, so no old value is kept.
+__device__ __forceinline__ uint32_t rot8(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true));
+}
+
+// (p & m) | (q & ~m) in one v_bitop3_b32 (truth table 0xCA over the operands
+// m, p, q: bit m ? p : q).  The operand choices below are bit selects on a
+// lane mask, not conditionals: a conditional may become a branch, and a
+// rotation issued under it would read lanes that the branch switched off.
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t p, uint32_t q) {
+    return __builtin_amdgcn_bitop3_b32(m, p, q, 0xCA);
+}
+
+// The two MFMA weight operands of a pair of k-steps from the pair's two loads
+// a (rows 0..7 of the row block) and b (rows 8..15); lane l of a load holds
+// row l%8 at the 16-byte piece (l/16) + 4*((l/8)%2) of the pair's 128 bytes.
+// Operand lane l wants row l%16 at piece l/16 (first step) or 4 + l/16
+// (second).  With lo8 all ones in lanes l%16 < 8: the first step's operand
+// is a in those lanes and b rotated by 8 in the others; the second step's is
+// a rotated by 8 in those lanes and b in the others.  One rotation of b
+// merged with a serves both.
+__device__ __forceinline__ void pair_operands(const uint4& a, const uint4& b, uint32_t lo8, uint4& t0, uint4& t1) {
+    const uint4 e = {rot8(bit_select(lo8, b.x, a.x)), rot8(bit_select(lo8, b.y, a.y)),
+                     rot8(bit_select(lo8, b.z, a.z)), rot8(bit_select(lo8, b.w, a.w))};
+    t0.x = bit_select(lo8, a.x, e.x);
+    t0.y = bit_select(lo8, a.y, e.y);
+    t0.z = bit_select(lo8, a.z, e.z);
+    t0.w = bit_select(lo8, a.w, e.w);
+    t1.x = bit_select(lo8, e.x, b.x);
+    t1.y = bit_select(lo8, e.y, b.y);
+    t1.z = bit_select(lo8, e.z, b.z);
+    t1.w = bit_select(lo8, e.w, b.w);
+}
 
 // LDS of a decode launch: the x tile (or the wave partials, which reuse it)
 // and the group's plan (J entries plus Jc counters).
@@ -93,26 +134,31 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
         lds_dma16(xrs, xlds + static_cast<uint32_t>(i * 1024), voff, 0u);
     }
 
-    // (3) this wave's weight loads: k-steps [sb, se) of the group's Kc/32.
-    // Lane l reads row l%16 of a 16-row block at columns 8*(l/16) of the step,
-    // the MFMA operand layout itself (16 rows x 64 bytes per load; measured
-    // slightly ahead of reading 64 contiguous bytes per lane quad and
-    // permuting across lanes); a step past se reads zeros.
+    // (3) this wave's weight loads: k-steps [sb, se) of the group's Kc/32,
+    // in pairs (sb even).  Each load covers 8 rows x 128 bytes, whole lines
+    // (on the Llama-3-8B gate/up decode shape the whole layer took 19.3 us
+    // with loads of 16 rows x 64 bytes in the operand layout itself, 15.9
+    // with these and no rotations); lane l reads row l%8 (plus 8 for the
+    // pair's second load) at piece (l/16) + 4*((l/8)%2).  A pair that starts
+    // before se is loaded whole (a second step at or past se is never
+    // multiplied); columns past Kc fall in the next row, or past the extent
+    // on the last row, which reads zeros.
     const int S = Kc / 32;
-    const int sb = (S * wave) / NW;
-    const int se = (S * (wave + 1)) / NW;
+    const int SP = (S + 1) / 2;
+    const int sb = 2 * ((SP * wave) / NW);
+    const int se = min(S, 2 * ((SP * (wave + 1)) / NW));
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(w + static_cast<size_t>(g) * BN * Kc, static_cast<uint32_t>(BN * Kc * 2));
-    const uint32_t wl = static_cast<uint32_t>(((lane & 15) * Kc + (lane >> 4) * 8) * 2);
-    uint4 wv[kDecSteps][RB];
+    const uint32_t wl = static_cast<uint32_t>(((lane & 7) * Kc + ((lane >> 4) + 4 * ((lane >> 3) & 1)) * 8) * 2);
+    uint4 wv[kDecSteps][RB];  // [2v][rb]: rows 0..7 of pair v, [2v+1][rb]: rows 8..15
     auto load_w = [&](int s0) {
 #pragma unroll
         for (int u = 0; u < kDecSteps; ++u)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                const uint32_t off = (s0 + u < se)
-                                         ? wl + static_cast<uint32_t>((rb * 16 * Kc + (s0 + u) * 32) * 2)
-                                         : kOutOfRange;
+                const int p0 = s0 + (u & ~1);  // first step of the pair
+                const uint32_t off =
+                    (p0 < se) ? wl + static_cast<uint32_t>(((rb * 16 + 8 * (u & 1)) * Kc + p0 * 32) * 2) : kOutOfRange;
                 wv[u][rb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, kNonTemporal));
             }
     };
@@ -126,6 +172,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
     // (5) sketch and MFMA per k-step
     const int tok = lane & 15;
     const int kq = (lane >> 4) * 8;
+    const uint32_t lo8 = (lane & 8) ? 0u : 0xFFFFFFFFu;
     const uint16_t* xrow = sx + tok * K;
     f32x4 acc[RB];
 #pragma unroll
@@ -150,13 +197,20 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
             z[u] = pack_bf16x8(a);
         }
 #pragma unroll
-        for (int u = 0; u < kDecSteps; ++u) {
+        for (int u = 0; u < kDecSteps; u += 2) {
             if (s0 + u < se) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[u][rb]),
+                for (int rb = 0; rb < RB; ++rb) {
+                    uint4 t0, t1;
+                    pair_operands(wv[u][rb], wv[u + 1][rb], lo8, t0, t1);
+                    acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t0),
                                                                        __builtin_bit_cast(bf16x8, z[u]), acc[rb],
                                                                        0, 0, 0);
+                    if (s0 + u + 1 < se)
+                        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t1),
+                                                                           __builtin_bit_cast(bf16x8, z[u + 1]),
+                                                                           acc[rb], 0, 0, 0);
+                }
             }
         }
     }
