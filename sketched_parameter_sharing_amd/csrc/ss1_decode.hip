@@ -47,42 +47,6 @@ constexpr int kDecWaves = 16;
 constexpr int kDecSteps = 4;  // k-steps per wave whose weight loads are in flight together
 static_assert(kDecSteps % 2 == 0, "k-steps come in pairs of one 128-byte line");
 
-// Lane l of a 16-lane row takes the value of lane (l + 8) % 16 (DPP
-// row_ror:8, a VALU operand modifier; no LDS traffic).  Every lane is a
-// valid source, so no old value is kept.
-__device__ __forceinline__ uint32_t rot8(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true));
-}
-
-// (p & m) | (q & ~m) in one v_bitop3_b32 (truth table 0xCA over the operands
-// m, p, q: bit m ? p : q).  The operand choices below are bit selects on a
-// lane mask, not conditionals: a conditional may become a branch, and a
-// rotation issued under it would read lanes that the branch switched off.
-__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t p, uint32_t q) {
-    return __builtin_amdgcn_bitop3_b32(m, p, q, 0xCA);
-}
-
-// The two MFMA weight operands of a pair of k-steps from the pair's two loads
-// a (rows 0..7 of the row block) and b (rows 8..15); lane l of a load holds
-// row l%8 at the 16-byte piece (l/16) + 4*((l/8)%2) of the pair's 128 bytes.
-// Operand lane l wants row l%16 at piece l/16 (first step) or 4 + l/16
-// (second).  With lo8 all ones in lanes l%16 < 8: the first step's operand
-// is a in those lanes and b rotated by 8 in the others; the second step's is
-// a rotated by 8 in those lanes and b in the others.  One rotation of b
-// merged with a serves both.
-__device__ __forceinline__ void pair_operands(const uint4& a, const uint4& b, uint32_t lo8, uint4& t0, uint4& t1) {
-    const uint4 e = {rot8(bit_select(lo8, b.x, a.x)), rot8(bit_select(lo8, b.y, a.y)),
-                     rot8(bit_select(lo8, b.z, a.z)), rot8(bit_select(lo8, b.w, a.w))};
-    t0.x = bit_select(lo8, a.x, e.x);
-    t0.y = bit_select(lo8, a.y, e.y);
-    t0.z = bit_select(lo8, a.z, e.z);
-    t0.w = bit_select(lo8, a.w, e.w);
-    t1.x = bit_select(lo8, e.x, b.x);
-    t1.y = bit_select(lo8, e.y, b.y);
-    t1.z = bit_select(lo8, e.z, b.z);
-    t1.w = bit_select(lo8, e.w, b.w);
-}
-
 // LDS of a decode launch: the x tile (or the wave partials, which reuse it)
 // and the group's plan (J entries plus Jc counters).
 size_t decode_lds(int64_t K, const Dims& d) {
@@ -149,7 +113,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
     const int se = min(S, 2 * ((SP * (wave + 1)) / NW));
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(w + static_cast<size_t>(g) * BN * Kc, static_cast<uint32_t>(BN * Kc * 2));
-    const uint32_t wl = static_cast<uint32_t>(((lane & 7) * Kc + ((lane >> 4) + 4 * ((lane >> 3) & 1)) * 8) * 2);
+    const uint32_t wl = pair_load_offset(lane, Kc);
     uint4 wv[kDecSteps][RB];  // [2v][rb]: rows 0..7 of pair v, [2v+1][rb]: rows 8..15
     auto load_w = [&](int s0) {
 #pragma unroll
@@ -172,7 +136,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
     // (5) sketch and MFMA per k-step
     const int tok = lane & 15;
     const int kq = (lane >> 4) * 8;
-    const uint32_t lo8 = (lane & 8) ? 0u : 0xFFFFFFFFu;
+    const uint32_t lo8 = pair_lane_mask(lane);
     const uint16_t* xrow = sx + tok * K;
     f32x4 acc[RB];
 #pragma unroll

@@ -321,6 +321,60 @@ __device__ __forceinline__ uint4 to_operand_layout(const uint4& v, int src_bytes
     return r;
 }
 
+// --------------------------------- weight operands from whole-line loads
+// The 16x16x32 MFMA operand of a 16-row weight block wants, in lane l, row
+// l%16 at 8 consecutive columns 8*(l/16) of a 32-wide k-step: 16 rows x 64
+// bytes per load, half of every 128-byte line.  Two consecutive k-steps (64
+// bf16 columns, one line per row) are loaded instead as two loads of 8 rows x
+// 128 bytes (whole lines): lane l reads row l%8 (plus 8 for the second load)
+// at the 16-byte piece (l/16) + 4*((l/8)%2) of the pair's 128 bytes, and
+// pair_operands turns the two loads into the two steps' operands.
+
+// Byte offset of lane l's piece in the first load of a pair, rows Kc
+// elements apart (add 8 rows for the second load, and the pair's columns).
+__device__ __forceinline__ uint32_t pair_load_offset(int lane, int Kc) {
+    return static_cast<uint32_t>(((lane & 7) * Kc + ((lane >> 4) + 4 * ((lane >> 3) & 1)) * 8) * 2);
+}
+
+// All ones in lanes with l%16 < 8.
+__device__ __forceinline__ uint32_t pair_lane_mask(int lane) { return (lane & 8) ? 0u : 0xFFFFFFFFu; }
+
+// Lane l of a 16-lane row takes the value of lane (l + 8) % 16 (DPP
+// row_ror:8, a VALU operand modifier; no LDS traffic).  Every lane is a
+// valid source, so no old value is kept.
+__device__ __forceinline__ uint32_t rot8(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x128, 0xF, 0xF, true));
+}
+
+// (p & m) | (q & ~m) in one v_bitop3_b32 (truth table 0xCA over the operands
+// m, p, q: bit m ? p : q).  The operand choices below are bit selects on a
+// lane mask, not conditionals: a conditional may become a branch, and a
+// rotation issued under it would read lanes that the branch switched off.
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t p, uint32_t q) {
+    return __builtin_amdgcn_bitop3_b32(m, p, q, 0xCA);
+}
+
+// The two MFMA weight operands of a pair of k-steps from the pair's two loads
+// a (rows 0..7 of the row block) and b (rows 8..15); lane l of a load holds
+// row l%8 at the 16-byte piece (l/16) + 4*((l/8)%2) of the pair's 128 bytes.
+// Operand lane l wants row l%16 at piece l/16 (first step) or 4 + l/16
+// (second).  With lo8 all ones in lanes l%16 < 8: the first step's operand
+// is a in those lanes and b rotated by 8 in the others; the second step's is
+// a rotated by 8 in those lanes and b in the others.  One rotation of b
+// merged with a serves both.
+__device__ __forceinline__ void pair_operands(const uint4& a, const uint4& b, uint32_t lo8, uint4& t0, uint4& t1) {
+    const uint4 e = {rot8(bit_select(lo8, b.x, a.x)), rot8(bit_select(lo8, b.y, a.y)),
+                     rot8(bit_select(lo8, b.z, a.z)), rot8(bit_select(lo8, b.w, a.w))};
+    t0.x = bit_select(lo8, a.x, e.x);
+    t0.y = bit_select(lo8, a.y, e.y);
+    t0.z = bit_select(lo8, a.z, e.z);
+    t0.w = bit_select(lo8, a.w, e.w);
+    t1.x = bit_select(lo8, e.x, b.x);
+    t1.y = bit_select(lo8, e.y, b.y);
+    t1.z = bit_select(lo8, e.z, b.z);
+    t1.w = bit_select(lo8, e.w, b.w);
+}
+
 // Blocks are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
 // Renumber so that each XCD works through one contiguous range of tiles and
 // tiles sharing an input row band stay in one L2.  A bijection on [0, n).
