@@ -167,6 +167,7 @@ KERNEL_SOURCES = {
     "smallm": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "gemv": ("ss1_gemv.hip", "ss1_device.h", "ss1_internal.h"),
     "decode": ("ss1_decode.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
+    "split": ("ss1_decode.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "generic": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "fold8": ("ss1_fold.hip", "ss1_quant.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
@@ -350,10 +351,23 @@ def time_gpu(wl, steps, warmup, algo, use_index, warm, graph=False):
     xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
     ws = [w0] + [w0.clone() for _ in range(nsets - 1)]
     ys = [torch.empty((wl.M, wl.N), dtype=x0.dtype, device="cuda") for _ in range(nsets)]
+    # the auto path goes through ss1_forward_ws: a workspace (allocated here,
+    # outside the timed region) lets decode shapes whose input rows are too
+    # long for the decode kernel split each group's columns over blocks; for
+    # every other shape it runs as ss1_forward and the workspace is unused
+    work = None
+    if algo == "auto" and not use_index:
+        _, nbytes = ss1.forward_ws_query(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN,
+                                         ss1.BF16 if wl.dtype == "bf16" else ss1.F32)
+        if nbytes:
+            work = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
     def step(i):
         k = i % nsets
-        plan.forward(xs[k], ws[k], y=ys[k], algo=algo, use_index=use_index)
+        if work is not None:
+            ss1.forward_ws(xs[k], ws[k], plan.hash, plan.sign, wl.c, wl.BK, wl.BN, workspace=work, y=ys[k])
+        else:
+            plan.forward(xs[k], ws[k], y=ys[k], algo=algo, use_index=use_index)
 
     if graph:
         t = time_graph(step, steps, warmup)
@@ -753,11 +767,14 @@ def fp8_kernel_name(wl):
 
 
 def kernel_name(wl, algo):
-    """The kernel a call runs: the requested one, or what the library picks."""
+    """The kernel a call runs: the requested one, or what the library picks
+    for ss1_forward_ws (the auto path; it equals ss1_forward's choice except
+    where the column-split decode with a workspace applies)."""
     if algo != "auto":
         return algo
     import sketched_parameter_sharing_amd as ss1
-    return ss1.select_algo(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype)
+    return ss1.forward_ws_query(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN,
+                                ss1.BF16 if wl.dtype == "bf16" else ss1.F32)[0]
 
 
 def cpu_baseline(wl, budget_s=10.0):

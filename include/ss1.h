@@ -76,8 +76,11 @@ typedef enum {
     SS1_ALGO_BAND = 4,     /* bf16, short rows: a band of input rows held in LDS        */
     SS1_ALGO_FOLD = 5,     /* bf16: W_c expanded on chip, one dense-shaped MFMA GEMM    */
     SS1_ALGO_GEMV = 6,     /* bf16: M <= 4, matrix-vector kernel, W_c streamed once     */
-    SS1_ALGO_DECODE = 7    /* bf16: M <= 16 with 16 input rows in LDS, one group per
+    SS1_ALGO_DECODE = 7,   /* bf16: M <= 16 with 16 input rows in LDS, one group per
                               block, every weight load in flight, MFMA               */
+    SS1_ALGO_SPLIT = 8     /* bf16: M <= 16, each group's compressed columns split over
+                              blocks, partial sums in a caller workspace (ss1_forward_ws
+                              only)                                                  */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */
@@ -232,6 +235,45 @@ ss1_status ss1_forward_idx_algo(const ss1_tensor* x, const ss1_tensor* W_c,
  */
 ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
                            int32_t BN, int32_t* algo);
+
+/*
+ * ss1_forward_ws_query -- HOST.  For a layer with these descriptors (only
+ * dtypes and sizes are read; data may be NULL): *algo = the kernel
+ * ss1_forward_ws runs and *bytes = the device workspace it needs (0 when it
+ * needs none).  SS1_ALGO_SPLIT needs Q * M * N * 4 bytes, Q the number of
+ * column slices per neuron group; every other choice is ss1_forward's and
+ * needs none.  May query the current HIP device's properties.  Errors: as
+ * the shape and dtype checks of ss1_forward, SS1_ERR_NULL.
+ *
+ * ss1_forward_ws -- DEVICE, asynchronous on `stream`.  ss1_forward with a
+ * caller-owned device workspace, which lets decode shapes (5 <= M <= 16,
+ * BF16, BN of 32 or 64, BK % 64 == 0) whose input rows are too long for the
+ * DECODE kernel (16 rows of K bf16 over one block's LDS) split each neuron
+ * group's compressed columns over several blocks (SS1_ALGO_SPLIT): the fewest
+ * slices Q (a power of two, K % (512 Q) == 0, Kc % (BK Q) == 0) that give a
+ * block per compute unit and fit in LDS.  One block per (group, slice)
+ * stages only the input chunks its slice's compressed chunks sum (SS1
+ * summary page, "Approach": the sketch is a signed sum of input chunks, so a
+ * slice of the sketch needs only those chunks), multiplies the sketch rounded
+ * to bf16 by its slice of W_c on the matrix cores, and writes a float32
+ * partial tile; a second kernel sums the slices in a fixed order into y.
+ * Where the split does not apply the call runs exactly as ss1_forward and
+ * the workspace is not touched.
+ *   x, W_c, hash, sign, c, BK, BN, y : as ss1_forward
+ *   workspace       : DEVICE, at least the bytes ss1_forward_ws_query reports,
+ *                     16-byte aligned; its contents on entry are ignored and
+ *                     unspecified afterwards (may be NULL when it needs none)
+ *   workspace_bytes : its size
+ * Calls that share a workspace must be ordered (one stream).  The result
+ * equals ss1_forward's up to float32 summation order.  Errors: as
+ * ss1_forward; SS1_ERR_NULL (workspace needed and NULL), SS1_ERR_ALIGN,
+ * SS1_ERR_SHAPE (workspace_bytes too small) before any HIP call.
+ */
+ss1_status ss1_forward_ws_query(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK, int32_t BN,
+                                size_t* bytes, int32_t* algo);
+ss1_status ss1_forward_ws(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash, const int8_t* sign,
+                          int32_t c, int32_t BK, int32_t BN, ss1_tensor* y, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * ss1_sketch -- DEVICE, asynchronous.  The standalone input sketch (the first

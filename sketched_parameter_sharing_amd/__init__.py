@@ -9,6 +9,8 @@ from dataclasses import dataclass
 
 from ._lib import (  # noqa: F401
     ALGOS,
+    BF16,
+    F32,
     EXPORTS,
     SS1Error,
     backward,
@@ -17,6 +19,8 @@ from ._lib import (  # noqa: F401
     forward_fp8,
     forward_fp8w,
     forward_idx,
+    forward_ws,
+    forward_ws_query,
     load,
     mlp_forward,
     mlp_forward_static,

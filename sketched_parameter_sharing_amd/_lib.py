@@ -22,14 +22,15 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = ran
 # dtypes (ss1_dtype)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 # kernel choice (ss1_algo)
-ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD, ALGO_GEMV, ALGO_DECODE = range(8)
+ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD, ALGO_GEMV, ALGO_DECODE, ALGO_SPLIT = range(9)
 ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC,
-         "band": ALGO_BAND, "fold": ALGO_FOLD, "gemv": ALGO_GEMV, "decode": ALGO_DECODE}
+         "band": ALGO_BAND, "fold": ALGO_FOLD, "gemv": ALGO_GEMV, "decode": ALGO_DECODE, "split": ALGO_SPLIT}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",
            "ss1_project", "ss1_mlp_forward", "ss1_quantize_fp8", "ss1_forward_fp8w",
-           "ss1_backward", "ss1_backward_select_algo", "ss1_mlp_forward_static", "ss1_forward_fp8")
+           "ss1_backward", "ss1_backward_select_algo", "ss1_mlp_forward_static", "ss1_forward_fp8",
+           "ss1_forward_ws_query", "ss1_forward_ws")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 
@@ -97,6 +98,10 @@ def load():
     lib.ss1_forward_fp8w.argtypes = [tp, tp, vp, vp, vp, i32, i32, i32, tp, vp]
     lib.ss1_backward.restype = i32
     lib.ss1_backward.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, tp, tp, vp]
+    lib.ss1_forward_ws_query.restype = i32
+    lib.ss1_forward_ws_query.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(i32)]
+    lib.ss1_forward_ws.restype = i32
+    lib.ss1_forward_ws.argtypes = [tp, tp, vp, vp, i32, i32, i32, tp, vp, ctypes.c_size_t, vp]
     lib.ss1_select_algo.restype = i32
     lib.ss1_select_algo.argtypes = [tp, tp, i32, i32, i32, ctypes.POINTER(i32)]
     lib.ss1_backward_select_algo.restype = i32
@@ -231,6 +236,41 @@ def forward(x, W_c, hash_, sign, c: int, BK: int, BN: int, y=None, algo: str = "
         st = lib.ss1_forward_algo(ctypes.byref(dx), ctypes.byref(dw), hash_.data_ptr(), sign.data_ptr(),
                                   c, BK, BN, ctypes.byref(dy), ALGOS[algo], _stream(stream))
     _check(st, "ss1_forward")
+    return y
+
+
+def forward_ws_query(M: int, K: int, N: int, c: int, BK: int, BN: int, dtype: int = BF16):
+    """(kernel name, workspace bytes) of ss1_forward_ws for a layer of these
+    sizes (ss1_forward_ws_query; no data is read)."""
+    dx = Tensor(None, dtype, 0, M, K)
+    dw = Tensor(None, dtype, 0, N, K // c if c > 0 else 0)
+    nbytes, algo = ctypes.c_size_t(0), ctypes.c_int32(0)
+    _check(load().ss1_forward_ws_query(ctypes.byref(dx), ctypes.byref(dw), c, BK, BN, ctypes.byref(nbytes),
+                                       ctypes.byref(algo)), "ss1_forward_ws_query")
+    return ALGO_NAMES[algo.value], nbytes.value
+
+
+def forward_ws(x, W_c, hash_, sign, c: int, BK: int, BN: int, workspace=None, y=None, stream=None):
+    """y = SS1(x) on the GPU with a caller-owned workspace (ss1_forward_ws).
+    ``workspace`` is a device tensor of at least the bytes forward_ws_query
+    reports (allocated here when None and needed)."""
+    import torch
+    _check_device(x, W_c, hash_, sign)
+    _check_plan(hash_, sign, x.shape[-1], W_c.shape[0], c, BK, BN)
+    if y is None:
+        y = torch.empty((x.shape[0], W_c.shape[0]), dtype=x.dtype, device=x.device)
+    dx, dw, dy = _desc(x), _desc(W_c), _desc(y)
+    lib = load()
+    if workspace is None:
+        nbytes, algo = ctypes.c_size_t(0), ctypes.c_int32(0)
+        _check(lib.ss1_forward_ws_query(ctypes.byref(dx), ctypes.byref(dw), c, BK, BN, ctypes.byref(nbytes),
+                                        ctypes.byref(algo)), "ss1_forward_ws_query")
+        if nbytes.value:
+            workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=x.device)
+    wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None else (None, 0)
+    st = lib.ss1_forward_ws(ctypes.byref(dx), ctypes.byref(dw), hash_.data_ptr(), sign.data_ptr(), c, BK, BN,
+                            ctypes.byref(dy), wp, wb, _stream(stream))
+    _check(st, "ss1_forward_ws")
     return y
 
 

@@ -103,6 +103,21 @@ int32_t fp8_algo(const ForwardArgs& a) {
     return SS1_ALGO_FUSED;
 }
 
+// What ss1_forward_ws runs: the column-split decode (with its workspace)
+// for 5 <= M <= 16 where the decode kernel cannot hold the 16 input rows in
+// LDS, else ss1_forward's choice.  Measured with cold weights on the
+// Llama-3-8B decode shapes at M = 16: down (K = 14336) 23.8-24.2 us on the
+// small-M kernel, 19.2-19.4 split; gate/up (K = 4096) 16.6-17.3 on the decode
+// kernel, 25.6 split.
+int32_t ws_algo(const ForwardArgs& a, size_t* bytes) {
+    *bytes = 0;
+    if (a.M >= 5 && !ss1::decode_supported(a) && ss1::split_slices(a) > 0) {
+        *bytes = ss1::split_workspace_bytes(a);
+        return SS1_ALGO_SPLIT;
+    }
+    return auto_algo(a);
+}
+
 ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
     switch (algo) {
         case SS1_ALGO_SMALLM: return ss1::launch_smallm(a);
@@ -225,6 +240,42 @@ extern "C" ss1_status ss1_select_algo(const ss1_tensor* x, const ss1_tensor* W_c
     }
     *algo = auto_algo(a);
     return SS1_OK;
+}
+
+extern "C" ss1_status ss1_forward_ws_query(const ss1_tensor* x, const ss1_tensor* W_c, int32_t c, int32_t BK,
+                                           int32_t BN, size_t* bytes, int32_t* algo) {
+    if (!x || !W_c || !bytes || !algo) return SS1_ERR_NULL;
+    ss1_tensor y{x->data, x->dtype, 0, x->rows, W_c->rows};
+    static const int32_t plan_i = 0;
+    static const int8_t plan_s = 0;
+    static char dummy[16] __attribute__((aligned(16)));
+    ss1_tensor xs = *x, ws = *W_c;
+    if (!xs.data) xs.data = dummy;
+    if (!ws.data) ws.data = dummy;
+    y.data = xs.data;
+    ForwardArgs a;
+    ss1_status st = check_forward(&xs, &ws, &plan_i, &plan_s, c, BK, BN, &y, PlanForm::Index, nullptr, &a);
+    if (st != SS1_OK) return st;
+    *algo = ws_algo(a, bytes);
+    return SS1_OK;
+}
+
+extern "C" ss1_status ss1_forward_ws(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t* hash,
+                                     const int8_t* sign, int32_t c, int32_t BK, int32_t BN, ss1_tensor* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    ForwardArgs a;
+    ss1_status st = check_forward(x, W_c, hash, sign, c, BK, BN, y, PlanForm::Hash, stream, &a);
+    if (st != SS1_OK) return st;
+    size_t need = 0;
+    const int32_t algo = ws_algo(a, &need);
+    if (need > 0) {
+        if (!workspace) return SS1_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return SS1_ERR_ALIGN;
+        if (workspace_bytes < need) return SS1_ERR_SHAPE;
+    }
+    if (a.M == 0) return SS1_OK;
+    if (algo == SS1_ALGO_SPLIT) return ss1::launch_split(a, workspace);
+    return launch_algo(a, algo);
 }
 
 extern "C" ss1_status ss1_sketch(const ss1_tensor* x, const int32_t* hash, const int8_t* sign,

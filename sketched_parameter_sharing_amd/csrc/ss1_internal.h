@@ -50,6 +50,12 @@ bool gemv_supported(const ForwardArgs& a);
 // Decode kernel (ss1_decode.hip): bf16, M <= 16, K % 512 == 0 with 16 input
 // rows of K bf16 in LDS, BN of 32 or 64, BK % 32 == 0, J <= 2048.
 bool decode_supported(const ForwardArgs& a);
+// Column-split decode (ss1_decode.hip): slices per group (0 when it does not
+// apply), the float32 workspace it needs (Q * M * N floats), and the launch
+// (split kernel, then the in-order sum of the slices into y).
+int split_slices(const ForwardArgs& a);
+size_t split_workspace_bytes(const ForwardArgs& a);
+ss1_status launch_split(const ForwardArgs& a, void* workspace);
 // Band kernel: the layer's rows are short enough for a band of at least
 // min_rows input rows to sit in LDS.
 bool band_supported(const ForwardArgs& a, int min_rows);

@@ -490,3 +490,95 @@ def test_auto_runs_the_selected_kernel(name):
     inp = make_inputs(wl)
     p = device_plan(wl)
     assert torch.equal(run(wl, inp, p), run(wl, inp, p, algo=algo))
+
+
+# ------------------------------------------------- column-split decode (workspace)
+def run_ws(wl, inp, plan, workspace=None):
+    x = dev(inp.x_bits, "bf16")
+    w = dev(inp.w_bits, "bf16")
+    y = ss1.forward_ws(x, w, plan.hash, plan.sign, wl.c, wl.BK, wl.BN, workspace=workspace)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("M", [5, 9, 16])
+def test_split_llama_decode(M):
+    # Llama down: each group's compressed columns split over 4 blocks; float32
+    # partial tiles in the workspace, summed in order
+    name = "llama_down_m16"
+    wl = WORKLOADS[name].with_m(M)
+    kernel, nbytes = ss1.forward_ws_query(M, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert kernel == "split" and nbytes == 4 * M * wl.N * 4
+    inp = make_inputs(wl)
+    p = device_plan(wl)
+    y = run_ws(wl, inp, p)
+    err = check_bf16(wl, inp, y, kernel="split")
+    print(f"{name} M={M} split err={err:.3e} workspace={nbytes}", flush=True)
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [
+    (7, 8192, 512, 4, 64, 32),      # 16 groups -> 16 slices of 128 compressed columns
+    (16, 8192, 2048, 2, 64, 64),    # 32 groups -> 8 slices
+    (5, 16384, 8192, 2, 128, 64),   # BK = 128: four k-steps per compressed chunk; 4 slices
+    (9, 8192, 4096, 1, 64, 64),     # c = 1, 64 groups -> 4 slices
+    (6, 6144, 2048, 3, 64, 32),     # c at run time
+])
+def test_split_shapes(M, K, N, c, BK, BN):
+    # input rows too long for the decode kernel (16 rows of K bf16 exceed one
+    # block's LDS), so the workspace entry point splits: 16, 8 and 4 slices,
+    # c from 1 to 4, BK = 128; against the oracle and bit-exact on integers
+    wl = Workload("split_dec", 9, 8, M, K, N, c, BK, BN, "bf16")
+    kernel, nbytes = ss1.forward_ws_query(M, K, N, c, BK, BN)
+    assert kernel == "split" and nbytes > 0
+    p = device_plan(wl)
+    inp = make_inputs(wl)
+    y = run_ws(wl, inp, p)
+    check_bf16(wl, inp, y, kernel="split")
+    inp = make_inputs(wl, integer=True)
+    y = run_ws(wl, inp, p)
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
+
+
+def test_split_workspace_reused_with_fewer_rows():
+    # the workspace's contents on entry are ignored: a second call with fewer
+    # rows over the first call's partial sums gives its own result
+    wl = WORKLOADS["llama_down_m16"]
+    p = device_plan(wl)
+    _, nbytes = ss1.forward_ws_query(16, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    for M in (16, 6):
+        w = wl.with_m(M)
+        inp = make_inputs(w)
+        y = run_ws(w, inp, p, workspace=ws)
+        check_bf16(w, inp, y, kernel="split")
+
+
+def test_split_workspace_checks():
+    wl = WORKLOADS["llama_down_m16"]
+    p = device_plan(wl)
+    inp = make_inputs(wl)
+    x = dev(inp.x_bits, "bf16")
+    w = dev(inp.w_bits, "bf16")
+    _, nbytes = ss1.forward_ws_query(wl.M, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    small = torch.empty(nbytes - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ss1.SS1Error) as e:
+        ss1.forward_ws(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, workspace=small)
+    assert e.value.status == 2  # SS1_ERR_SHAPE
+    big = torch.empty(nbytes + 64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ss1.SS1Error) as e:
+        ss1.forward_ws(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, workspace=big[4:])
+    assert e.value.status == 5  # SS1_ERR_ALIGN
+
+
+def test_split_not_applicable_runs_forward():
+    # M <= 4 (the matrix-vector kernel) and large M need no workspace and give
+    # ss1_forward's bits
+    for name, M in (("llama_gateup_m1", 2), ("gpt2s_up", 300)):
+        wl = WORKLOADS[name].with_m(M)
+        kernel, nbytes = ss1.forward_ws_query(M, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+        assert nbytes == 0 and kernel == ss1.select_algo(M, wl.K, wl.N, wl.c, wl.BK, wl.BN, wl.dtype)
+        inp = make_inputs(wl)
+        p = device_plan(wl)
+        assert torch.equal(run_ws(wl, inp, p), run(wl, inp, p))
