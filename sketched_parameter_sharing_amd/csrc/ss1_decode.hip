@@ -129,7 +129,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(const uint16_t* 
     load_w(sb);
 
     // (4) the plan into LDS from the registers of (1); then every wave's part
-    // of the x tile must have landed (the weight loads may stay in flight)
+    // of the x tile must have landed (the weight loads may stay in flight).
+    // The count in the wait assumes the RB * kDecSteps weight loads above are
+    // issued before it: the compiler may move buffer loads below an inline-asm
+    // wait (it did so for loads placed right before one), but not below the
+    // LDS barriers of stage_plan_regs, which sit between them here; the
+    // parity tests read all 16 rows at M = 16, where a short wait would show.
     stage_plan_regs<FROM_HASH, kPlanPerThread>(iv, sv, J, Jc, c, BK, s_src, s_cnt);
     dma_stage_barrier<RB * kDecSteps>();
 
