@@ -55,8 +55,8 @@ def replay_matches_eager(call, x, y, replays=3):
 
 
 @pytest.mark.parametrize("name,M,algo", [("llama_gateup_m1", 1, "gemv"), ("llama_down_m1", 2, "gemv"),
-                                         ("llama_gateup_m16", 16, "smallm"), ("gpt2s_up", 300, "auto"),
-                                         ("llama_down_m4096", 300, "fold")])
+                                         ("llama_gateup_m16", 16, "smallm"), ("llama_gateup_m16", 16, "decode"),
+                                         ("gpt2s_up", 300, "auto"), ("llama_down_m4096", 300, "fold")])
 def test_forward_replays(name, M, algo):
     wl = WORKLOADS[name].with_m(M)
     inp = make_inputs(wl)
@@ -76,3 +76,18 @@ def test_forward_fp8w_replays(name, M):
     y = torch.empty((M, wl.N), dtype=torch.bfloat16, device="cuda")
     replay_matches_eager(
         lambda: ss1.forward_fp8w(x, Q, scale, p.hash, p.sign, wl.c, wl.BK, wl.BN, y=y), x, y)
+
+
+@pytest.mark.parametrize("M", [16, 7])
+def test_forward_ws_split_replays(M):
+    # the column-split decode: two launches (partial tiles into the workspace,
+    # then their in-order sum), captured together
+    wl = WORKLOADS["llama_down_m16"].with_m(M)
+    kernel, nbytes = ss1.forward_ws_query(M, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert kernel == "split"
+    inp = make_inputs(wl)
+    p = ss1.DevicePlan.make(wl.plan_seed, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    x, w = bf16_dev(inp.x_bits), bf16_dev(inp.w_bits)
+    y = torch.empty((M, wl.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    replay_matches_eager(lambda: ss1.forward_ws(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, workspace=ws, y=y), x, y)
