@@ -690,6 +690,12 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
     const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(w);
     const int perm_src = coalesced_src_lane_bytes(lane);
     const uint16_t* lrow = band + (rb0 * 16 + li) * LDK + q * 8;  // this lane's band row (first block), k offset
+    // c = 2: the sketch runs on the matrix cores (see compute); each lane
+    // reads 16 inputs of one source, at 16*(q%2) of a 32-wide half-step
+    constexpr bool MSK = C_T == 2;
+    const uint16_t* lrow_ms = band + (rb0 * 16 + li) * LDK + 16 * (q & 1);
+    uint4 sel_one, sel_neg;
+    sketch_selector_base(li, q, sel_one, sel_neg);
 
     // lane holds y[m0 + (rb0+rb)*16 + li][g*BN + q*4*NB + nb*4 + i] of acc[rb][nb][i]
     auto store_tile = [&](int g, f32x4 (&acc)[RBW][NB]) {
@@ -749,14 +755,27 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
             uint4 raw[RAW_PF ? KH : 1][RAW_PF ? RBW : 1][RAW_PF ? CR : 1];
         };
         auto read_band = [&](const Stage& st, uint4 (&raw)[KH][RBW][CR]) {
-#pragma unroll
-            for (int r = 0; r < C_T; ++r) {
-                const uint16_t* src = lrow + st.off[r];
+            if constexpr (MSK) {
+                // lanes 0-31 read source 0, lanes 32-63 source 1: 16
+                // consecutive inputs at 16*(q%2) of each 32-wide half
+                const uint16_t* src = lrow_ms + (q < 2 ? st.off[0] : st.off[1]);
 #pragma unroll
                 for (int h = 0; h < KH; ++h)
 #pragma unroll
                     for (int rb = 0; rb < RBW; ++rb)
-                        raw[h][rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK + 32 * h);
+#pragma unroll
+                        for (int e = 0; e < 2; ++e)
+                            raw[h][rb][e] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK + 32 * h + 8 * e);
+            } else {
+#pragma unroll
+                for (int r = 0; r < C_T; ++r) {
+                    const uint16_t* src = lrow + st.off[r];
+#pragma unroll
+                    for (int h = 0; h < KH; ++h)
+#pragma unroll
+                        for (int rb = 0; rb < RBW; ++rb)
+                            raw[h][rb][r] = *reinterpret_cast<const uint4*>(src + rb * 16 * LDK + 32 * h);
+                }
             }
         };
         auto load = [&](int gi, int s, Stage& st) {
@@ -809,6 +828,47 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
                     } else {
                         wop[nb] = to_operand_layout(st.wf[h][nb], perm_src);
                     }
+                }
+                if constexpr (MSK) {
+                    // Sketch on the matrix cores: D[i][token] = sum_k A[i][k] X[k][token]
+                    // with X this lane's 16 inputs of its source (k = 8q + e) and
+                    // A the signed one-hot selection (sketch_selector).  Two
+                    // MFMAs give the sketch columns 8q..8q+3 and 8q+4..8q+7 of
+                    // the half-step for this lane's token, which is the
+                    // contraction's operand layout.  Each output sums exactly
+                    // two signed bf16 values (the other products are zeros), so
+                    // the float32 result is the one rounding of the exact sum,
+                    // as in the ascending float32 sketch.
+                    const uint4 sel = sketch_selector(sel_one, sel_neg, q < 2 ? st.sx[0] : st.sx[1],
+                                                      q < 2 ? st.sg[0] : st.sg[1]);
+                    f32x4 d0[RBW], d1[RBW];
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb) {
+                        const uint4 ra = raw[h][rb][0], rbv = raw[h][rb][1];
+                        const uint4 x0 = make_uint4(ra.x, ra.y, rbv.x, rbv.y);
+                        const uint4 x1 = make_uint4(ra.z, ra.w, rbv.z, rbv.w);
+                        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                        d0[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sel),
+                                                                         __builtin_bit_cast(bf16x8, x0), zero, 0, 0, 0);
+                        d1[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sel),
+                                                                         __builtin_bit_cast(bf16x8, x1), zero, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb) {
+                        uint4 zp;
+                        zp.x = pack_bf16(d0[rb][0], d0[rb][1]);
+                        zp.y = pack_bf16(d0[rb][2], d0[rb][3]);
+                        zp.z = pack_bf16(d1[rb][0], d1[rb][1]);
+                        zp.w = pack_bf16(d1[rb][2], d1[rb][3]);
+                        const bf16x8 zf = __builtin_bit_cast(bf16x8, zp);
+                        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, wop[nb]), zf, acc[rb][nb], 0, 0, 0);
+                        __builtin_amdgcn_s_setprio(0);
+                    }
+                    continue;
                 }
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb) {
