@@ -835,7 +835,7 @@ def main():
     ap.add_argument("--row-chunk", type=int, default=8192, help="rows per chunk of the MLP pair (op mlp)")
     ap.add_argument("--mlp-only", action="store_true",
                     help="op mlp: time only the pair at --mlp-c and --row-chunk and the dense pair (for profiling)")
-    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "decode", "generic", "band", "fold"])
+    ap.add_argument("--algo", default="auto", choices=["auto", "fused", "smallm", "gemv", "decode", "generic", "band", "fold", "group"])
     ap.add_argument("--index", action="store_true", help="time ss1_forward_idx (inverse index plan)")
     ap.add_argument("--warm", action="store_true", help="reuse one buffer set (cache-warm)")
     ap.add_argument("--graph", action="store_true",

@@ -78,9 +78,12 @@ typedef enum {
     SS1_ALGO_GEMV = 6,     /* bf16: M <= 4, matrix-vector kernel, W_c streamed once     */
     SS1_ALGO_DECODE = 7,   /* bf16: M <= 16 with 16 input rows in LDS, one group per
                               block, every weight load in flight, MFMA               */
-    SS1_ALGO_SPLIT = 8     /* bf16: M <= 16, each group's compressed columns split over
+    SS1_ALGO_SPLIT = 8,    /* bf16: M <= 16, each group's compressed columns split over
                               blocks, partial sums in a caller workspace (ss1_forward_ws
                               only)                                                  */
+    SS1_ALGO_GROUP = 9     /* bf16, c in {2, 4, 8}, BK % 64 == 0, BN 64 or 128: one
+                              neuron group per block, the sketch formed on the matrix
+                              cores, only the compressed contraction                 */
 } ss1_algo;
 
 /* A dense row-major matrix in device memory (rows packed). */

@@ -22,9 +22,11 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_PLAN, ERR_ALIGN, ERR_HIP, ERR_ALGO = ran
 # dtypes (ss1_dtype)
 F32, BF16, FP8_E4M3 = 0, 1, 2
 # kernel choice (ss1_algo)
-ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD, ALGO_GEMV, ALGO_DECODE, ALGO_SPLIT = range(9)
+(ALGO_AUTO, ALGO_FUSED, ALGO_SMALLM, ALGO_GENERIC, ALGO_BAND, ALGO_FOLD, ALGO_GEMV, ALGO_DECODE, ALGO_SPLIT,
+ ALGO_GROUP) = range(10)
 ALGOS = {"auto": ALGO_AUTO, "fused": ALGO_FUSED, "smallm": ALGO_SMALLM, "generic": ALGO_GENERIC,
-         "band": ALGO_BAND, "fold": ALGO_FOLD, "gemv": ALGO_GEMV, "decode": ALGO_DECODE, "split": ALGO_SPLIT}
+         "band": ALGO_BAND, "fold": ALGO_FOLD, "gemv": ALGO_GEMV, "decode": ALGO_DECODE, "split": ALGO_SPLIT,
+         "group": ALGO_GROUP}
 
 EXPORTS = ("ss1_version", "ss1_status_string", "ss1_plan", "ss1_plan_index", "ss1_forward",
            "ss1_forward_idx", "ss1_forward_algo", "ss1_forward_idx_algo", "ss1_select_algo", "ss1_sketch",

@@ -31,6 +31,7 @@ COMMON = [
 # copies about a hundred registers back and forth on every k-stage.
 EXTRA = {
     "ss1_fold.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "ss1_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

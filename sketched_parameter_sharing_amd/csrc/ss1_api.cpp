@@ -126,6 +126,7 @@ ss1_status launch_algo(const ForwardArgs& a, int32_t algo) {
         case SS1_ALGO_BAND: return ss1::launch_band(a);
         case SS1_ALGO_FUSED: return ss1::launch_fused(a);
         case SS1_ALGO_FOLD: return ss1::launch_fold(a);
+        case SS1_ALGO_GROUP: return ss1::launch_group(a);
         default: return ss1::launch_generic(a);
     }
 }
@@ -158,6 +159,9 @@ ss1_status run_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32_t
         case SS1_ALGO_FOLD:
             if (!ss1::fold_supported(a)) return SS1_ERR_ALGO;
             return a.M == 0 ? SS1_OK : ss1::launch_fold(a);
+        case SS1_ALGO_GROUP:
+            if (!ss1::group_supported(a)) return SS1_ERR_ALGO;
+            return a.M == 0 ? SS1_OK : ss1::launch_group(a);
         case SS1_ALGO_GENERIC:
             return a.M == 0 ? SS1_OK : ss1::launch_generic(a);
         default:

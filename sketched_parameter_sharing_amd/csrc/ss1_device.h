@@ -262,9 +262,15 @@ __device__ __forceinline__ void acc_sign8(float (&acc)[8], const uint4& raw, flo
 // l (row li = l%16, quarter q = l/16) the selection row has one non-zero, at
 // element li%8, when li/8 == q%2.  `one` holds bf16 1.0 there, `neg` its sign
 // bit.
-__device__ __forceinline__ void sketch_selector_base(int li, int q, uint4& one, uint4& neg) {
+//
+// With `swapped`, lanes of the second source take the other offset half
+// (16*((q%2) ^ (q/2))), so that quarter-waves 0 and 2 (and 1 and 3), which may
+// be served in the same LDS cycle, read different 16-byte pieces when the two
+// sources' rows sit on the same banks; the non-zero then sits where
+// li/8 == (q%2) ^ (q/2).
+__device__ __forceinline__ void sketch_selector_base(int li, int q, uint4& one, uint4& neg, bool swapped = false) {
     uint32_t o[4] = {0u, 0u, 0u, 0u}, n[4] = {0u, 0u, 0u, 0u};
-    if ((li >> 3) == (q & 1)) {
+    if ((li >> 3) == ((q & 1) ^ (swapped ? (q >> 1) : 0))) {
         const int e = li & 7;
         o[e >> 1] = 0x3F80u << (16 * (e & 1));
         n[e >> 1] = 0x8000u << (16 * (e & 1));

@@ -149,7 +149,12 @@ FORWARD_ERRORS = [
     ("algo fold f32", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32),
      {"algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
     ("algo fold BK", T(8, 256), T(64, 128), T(8, 64), {"BK": 32, "algo": _lib.ALGO_FOLD}, _lib.ERR_ALGO),
-    ("algo unknown", T(8, 256), T(64, 128), T(8, 64), {"algo": 9}, _lib.ERR_ALGO),
+    ("algo group f32", T(8, 256, _lib.F32), T(64, 128, _lib.F32), T(8, 64, _lib.F32),
+     {"algo": _lib.ALGO_GROUP}, _lib.ERR_ALGO),
+    ("algo group BK", T(8, 256), T(64, 128), T(8, 64), {"BK": 32, "algo": _lib.ALGO_GROUP}, _lib.ERR_ALGO),
+    ("algo group c", T(8, 256), T(64, 256), T(8, 64), {"c": 1, "algo": _lib.ALGO_GROUP}, _lib.ERR_ALGO),
+    ("algo group BN", T(8, 256), T(32, 128), T(8, 32), {"BN": 32, "algo": _lib.ALGO_GROUP}, _lib.ERR_ALGO),
+    ("algo unknown", T(8, 256), T(64, 128), T(8, 64), {"algo": 10}, _lib.ERR_ALGO),
 ]
 
 

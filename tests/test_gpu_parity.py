@@ -148,7 +148,7 @@ BF16_NAMES = ["gpt2s_up", "gpt2l_up", "gpt2l_down", "llama_gateup_m4096", "llama
 
 
 @pytest.mark.parametrize("name", BF16_NAMES)
-@pytest.mark.parametrize("algo", ["auto", "fused", "band", "generic", "fold"])
+@pytest.mark.parametrize("algo", ["auto", "fused", "band", "generic", "fold", "group"])
 def test_bf16_reduced_m(name, algo):
     # M = 300: two full 128-row tiles and a ragged tail (and a ragged band;
     # for the fold kernel one 256-row tile and a ragged one)
@@ -159,8 +159,9 @@ def test_bf16_reduced_m(name, algo):
     try:
         y = run(wl, inp, device_plan(wl), algo=algo)
     except ss1.SS1Error as e:
-        assert e.status == 7 and algo == "band"
-        pytest.skip("input rows too long for the band kernel")
+        assert e.status == 7 and algo in ("band", "group")
+        pytest.skip("input rows too long for the band kernel" if algo == "band"
+                    else "the group kernel takes c in {2, 4, 8}, BK % 64 == 0, BN of 64 or 128")
     err = check_bf16(wl, inp, y, kernel=kernel_of(wl, algo))
     print(f"{name} algo={algo} err={err:.3e}", flush=True)
 
@@ -189,7 +190,9 @@ def test_bf16_full_size_sampled_rows(name):
                                        ("gpt2l_up", "generic"), ("gpt2s_up", "band"),
                                        ("gpt2l_up", "band"), ("gpt2s_up", "fold"),
                                        ("llama_down_m4096", "fold"), ("square_c1_bn128", "fold"),
-                                       ("square_c8_bn32", "fold")])
+                                       ("square_c8_bn32", "fold"), ("llama_gateup_m4096", "group"),
+                                       ("gpt2l_down", "group"), ("square_c4_bn64", "group"),
+                                       ("square_c8_bn128", "group")])
 def test_bf16_integer_bit_exact(name, algo):
     wl = WORKLOADS[name]
     wl = wl.with_m(min(wl.M, {"smallm": 16, "decode": 16, "gemv": 4}.get(algo, 300)))
