@@ -149,7 +149,8 @@ def roofline(wl, t, kernel=None, peaks=None):
                                    "peak_tbs": peaks["l2_dma_tbs"], "frac": ob / t / 1e12 / peaks["l2_dma_tbs"],
                                    "note": "x and expanded-weight tiles moved L2 -> LDS per call (tile model) "
                                            "against the measured buffer-to-LDS read rate"}
-    traffic = recorded_traffic(wl.name, kernel)
+    # a record per workload for the kernel auto picks, "<family>:<workload>" for the others
+    traffic = recorded_traffic(wl.name, kernel) or recorded_traffic(f"{kernel}:{wl.name}", kernel)
     r["traffic"] = traffic
     r["traffic_unit"] = "HBM bytes per step (TCC_EA0_RDREQ* read bytes + WRITE_SIZE; all launches of one call)"
     r["traffic_vs_algorithmic"] = (traffic / wk["bytes"]) if traffic else None
@@ -162,7 +163,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 # Device sources of each kernel family (its kernels and the headers they include).
 KERNEL_SOURCES = {
-    "band": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
+    "band": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h", "ss1_msketch.h"),
     "fused": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "smallm": ("ss1_kernels.hip", "ss1_device.h", "ss1_internal.h"),
     "gemv": ("ss1_gemv.hip", "ss1_device.h", "ss1_internal.h"),
@@ -172,6 +173,7 @@ KERNEL_SOURCES = {
     "fold": ("ss1_fold.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "fold8": ("ss1_fold.hip", "ss1_quant.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h"),
     "project": ("ss1_project.hip", "ss1_device.h", "ss1_internal.h"),
+    "group": ("ss1_group.hip", "ss1_device.h", "ss1_dma.h", "ss1_internal.h", "ss1_msketch.h"),
 }
 
 

@@ -3,6 +3,7 @@
 // that fails a check has enqueued nothing.
 #include <stdint.h>
 
+#include "ss1_group.h"
 #include "ss1_internal.h"
 
 using ss1::Dims;

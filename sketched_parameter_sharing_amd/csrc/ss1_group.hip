@@ -10,7 +10,7 @@
 // 128 bytes each, ascending source order) and the group's W_c columns of the
 // stage (BN rows x 128 bytes).  The sketch is formed on the matrix cores: a
 // 16x16x32 bf16 MFMA against a signed one-hot selection adds two signed
-// sources exactly (sketch_selector in ss1_device.h), pairs of sources
+// sources exactly (sketch_selector in ss1_msketch.h), pairs of sources
 // accumulate in float32, and the sum is rounded to bf16 (RNE) as it becomes the
 // contraction's operand.  The contraction is y^T = W_c z^T with the weight
 // rows placed in a permuted order, so each lane ends with 4*BN/16 consecutive
@@ -36,7 +36,9 @@
 
 #include "ss1_device.h"
 #include "ss1_dma.h"
+#include "ss1_group.h"
 #include "ss1_internal.h"
+#include "ss1_msketch.h"
 
 namespace ss1 {
 

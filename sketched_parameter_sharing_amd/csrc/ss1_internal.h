@@ -100,11 +100,6 @@ ss1_status launch_decode(const ForwardArgs& a);
 ss1_status launch_band(const ForwardArgs& a);
 ss1_status launch_generic(const ForwardArgs& a);
 ss1_status launch_fold(const ForwardArgs& a);
-// Group kernel (ss1_group.hip): bf16 weights, c in {2, 4, 8}, BK % 64 == 0,
-// BN of 64 or 128; one neuron group per block, only the compressed
-// contraction, the sketch on the matrix cores.
-bool group_supported(const ForwardArgs& a);
-ss1_status launch_group(const ForwardArgs& a);
 ss1_status launch_sketch(const void* x, int32_t x_dtype, const int32_t* plan_i, const int8_t* plan_s,
                          int64_t M, const Dims& d, void* z, int32_t z_dtype, void* stream);
 // Backward: dW_c (when dW is not null) and dx (when dx is not null), bf16,

@@ -36,6 +36,7 @@
 
 #include "ss1_device.h"
 #include "ss1_internal.h"
+#include "ss1_msketch.h"
 
 namespace ss1 {
 
