@@ -691,11 +691,10 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
     const uint8_t* wbytes = reinterpret_cast<const uint8_t*>(w);
     const int perm_src = coalesced_src_lane_bytes(lane);
     const uint16_t* lrow = band + (rb0 * 16 + li) * LDK + q * 8;  // this lane's band row (first block), k offset
-    // c = 2: the sketch runs on the matrix cores (see compute); each lane
-    // reads 16 inputs of one source per pair, at 16*(q%2) of a 32-wide
-    // half-step.  (The same form at c = 4, two pairs accumulated, measured
-    // 567 us on the GPT-2 L up-projection; the float32 sketch is kept there.)
-    constexpr bool MSK = C_T == 2;
+    // c = 2, 4, 8: the sketch runs on the matrix cores (see compute); each
+    // lane reads 16 inputs of one source per pair, at 16*(q%2) of a 32-wide
+    // half-step.  Other c keep the float32 sketch on the vector ALUs.
+    constexpr bool MSK = C_T == 2 || C_T == 4 || C_T == 8;
     const uint16_t* lrow_ms = band + (rb0 * 16 + li) * LDK + 16 * (q & 1);
     uint4 sel_one, sel_neg;
     sketch_selector_base(li, q, sel_one, sel_neg);
@@ -763,7 +762,11 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
                 // 2p+1, 16 consecutive inputs at 16*(q%2) of each 32-wide half
 #pragma unroll
                 for (int p = 0; p < C_T / 2; ++p) {
-                    const uint16_t* src = lrow_ms + (q < 2 ? st.off[2 * p] : st.off[2 * p + 1]);
+                    // select between the two values, not the two array elements: a
+                    // lane-dependent index puts the whole stage in scratch memory
+                    const uint32_t o0 = __builtin_amdgcn_readfirstlane(st.off[2 * p]);
+                    const uint32_t o1 = __builtin_amdgcn_readfirstlane(st.off[2 * p + 1]);
+                    const uint16_t* src = lrow_ms + (q < 2 ? o0 : o1);
 #pragma unroll
                     for (int h = 0; h < KH; ++h)
 #pragma unroll
@@ -850,9 +853,15 @@ __global__ __launch_bounds__(NW * 64) void band_kernel(const uint16_t* __restric
                     // are added in pair order.
                     uint4 sel[C_T / 2];
 #pragma unroll
-                    for (int p = 0; p < C_T / 2; ++p)
-                        sel[p] = sketch_selector(sel_one, sel_neg, q < 2 ? st.sx[2 * p] : st.sx[2 * p + 1],
-                                                 q < 2 ? st.sg[2 * p] : st.sg[2 * p + 1]);
+                    for (int p = 0; p < C_T / 2; ++p) {
+                        const uint32_t x0 = __builtin_amdgcn_readfirstlane(st.sx[2 * p]);
+                        const uint32_t x1 = __builtin_amdgcn_readfirstlane(st.sx[2 * p + 1]);
+                        const float g0 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                                       __builtin_bit_cast(int, st.sg[2 * p])));
+                        const float g1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                                       __builtin_bit_cast(int, st.sg[2 * p + 1])));
+                        sel[p] = sketch_selector(sel_one, sel_neg, q < 2 ? x0 : x1, q < 2 ? g0 : g1);
+                    }
                     f32x4 d0[RBW], d1[RBW];
 #pragma unroll
                     for (int rb = 0; rb < RBW; ++rb) {
@@ -1168,7 +1177,9 @@ ss1_status launch_band_cfg(const ForwardArgs& a, const BandCfg& cfg) {
     constexpr int NW = (BN == 128 || C_T >= 8 || (C_T == 4 && MT == 64)) ? 4 : 8;
     constexpr int RS = 1;
     constexpr int KH = SH == BandShape::WIDE ? 2 : 1;
-    constexpr bool RAW_PF = KH == 1 && C_T <= 4 && BN < 128;
+    // (not with the matrix-core sketch of c = 2 and 4: its lane-dependent
+    // source choice then kept the prefetched stage in scratch memory)
+    constexpr bool RAW_PF = KH == 1 && C_T <= 4 && BN < 128 && C_T != 2 && C_T != 4;
     constexpr int PD = 2;
     const long long nbands = (a.M + MT - 1) / MT;
     auto kern = &band_kernel<MT, BN, C_T, NW, RS, KH, RAW_PF, PD, FROM_HASH, W8>;

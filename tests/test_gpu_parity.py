@@ -326,6 +326,9 @@ def test_gemv_shapes(M, K, N, c, BK, BN):
     (65, 160, 30, 5, 8, 3),
     (1, 64, 8, 8, 8, 8),
     (129, 512, 64, 1, 32, 64),
+    (300, 1024, 256, 8, 32, 64),    # band: the sketch on the matrix cores, four source pairs
+    (150, 512, 128, 4, 32, 32),     # band: two source pairs, BN = 32
+    (100, 768, 256, 2, 32, 128),    # band: 32-wide steps, BN = 128
 ])
 def test_bf16_odd_shapes(M, K, N, c, BK, BN):
     wl = Workload("odd", 9, 0, M, K, N, c, BK, BN, "bf16")
@@ -340,6 +343,22 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
             continue
         check_bf16(wl, inp, ys[algo], kernel=kernel_of(wl, algo))
     assert "auto" in ys and "generic" in ys
+
+
+@pytest.mark.parametrize("M,K,N,c,BK,BN", [(300, 1024, 256, 8, 32, 64), (150, 512, 128, 4, 32, 32),
+                                           (77, 1280, 320, 4, 64, 64), (100, 768, 256, 2, 32, 128),
+                                           (64, 768, 192, 2, 64, 64)])
+def test_band_matrix_core_sketch_integer_bit_exact(M, K, N, c, BK, BN):
+    # c = 2, 4, 8 on the band kernel form the sketch by MFMA against a signed
+    # selection: with integer inputs every sum is exact, so y is the oracle
+    # rounded to bf16 bit for bit
+    wl = Workload("band_int", 11, 0, M, K, N, c, BK, BN, "bf16")
+    inp = make_inputs(wl, integer=True)
+    y = run(wl, inp, device_plan(wl), algo="band")
+    h, s = oracle_plan(wl)
+    ref = oracle.forward(inp.x, inp.w, h, s, wl.K, wl.N, wl.c, wl.BK, wl.BN)
+    assert np.max(np.abs(ref)) < 2 ** 24
+    assert np.array_equal(bits(y), f32_to_bf16_bits(ref.astype(np.float32)))
 
 
 @pytest.mark.parametrize("name,algo", [("gpt2s_up", "fused"), ("llama_down_m16", "smallm"),
