@@ -207,6 +207,15 @@ ss1_status ss1_forward_idx(const ss1_tensor* x, const ss1_tensor* W_c,
  *            Multiplies x by the expanded weight W_c S_g (built in LDS from
  *            W_c, never stored): the same y as the sketch kernels up to
  *            rounding (no bf16 rounding of a sketch), dense MFMA work.
+ *   GROUP  : BF16 weights, c in {2, 4, 8}, BK % 64 == 0, BN in {64, 128}, and
+ *            the block's stages fit in LDS (true for every such layer on
+ *            gfx950).  One neuron group and 64-256 tokens per block: only the
+ *            compressed contraction (2 M N K / c) plus the sketch, which is
+ *            formed on the matrix cores (two signed sources per bf16 MFMA) and
+ *            rounded to bf16 as in the sketch kernels.  Never picked by
+ *            ss1_forward: its per-group gather of x makes it slower than FOLD
+ *            on the large-M layers measured.  (SS1 summary page, "Approach":
+ *            the sketch cuts the multiplies by c.)
  * ss1_forward picks GEMV for M <= 4 where it applies, else DECODE, else
  * SMALLM for M <= 16, and FOLD for large M where its modelled time is below the sketch
  * kernels' (ss1_select_algo reports the choice).
