@@ -25,9 +25,13 @@
 // compressed multiply-add through its load path, against 2/256 per dense
 // multiply-add for the fold's 256x256 tiles.
 //
-// LDS: 3 stages of (c*BM + BN) rows of 128 bytes, c*BM = 256 (about 40-48 KB
-// each), two stages in flight while one is read.  Rows are XOR-swizzled in
-// 16-byte pieces as in the fold kernels (conflict-free 16-byte operand reads).
+// LDS: 2 or 3 stages of (c*BM + BN) rows of 128 bytes (c*BM = 256 or 512;
+// the launch shapes are listed at group_shape_dims), the next stages loading
+// while one is read.  Rows are XOR-swizzled in 16-byte pieces as in the fold
+// kernels; lanes of the second source read the other 16-input half of a
+// half-step, so that quarter-waves that may share an LDS cycle read different
+// pieces.  (The counters still show about a third of the LDS-active cycles as
+// bank conflicts; the kernel is bound by its loads, not by the LDS.)
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(NW * 64) void group_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ pi,
                                                         const int8_t* __restrict__ ps, uint16_t* __restrict__ y,
                                                         int M, int K, int N, int J, int Jc, int BK, int n_mt,
-                                                        int gm_strip, int act) {
+                                                        int tpb, int act) {
     constexpr int RB = kGroupRowBytes;
     constexpr int NB = BN / 16;          // 16-neuron blocks of the group
     constexpr int TB = BM / 16 / NW;     // 16-token blocks per wave
@@ -87,32 +91,29 @@ __global__ __launch_bounds__(NW * 64) void group_kernel(const uint16_t* __restri
     uint32_t* s_src = reinterpret_cast<uint32_t*>(group_smem + NSTG * SB);
     int* s_cnt = reinterpret_cast<int*>(s_src + J);
 
-    // Tile order: each XCD takes a contiguous range of tiles; inside it the
-    // tiles go group by group over strips of gm_strip token tiles, so the
-    // blocks that run together on an XCD share a few x bands and stream each
-    // group's W_c once per strip.
+    // A block is one group and tpb consecutive token tiles, which it runs as
+    // one pipeline of stages (the plan staged once, no drain between tiles).
+    // Each XCD takes a contiguous range of blocks, groups fastest, so the
+    // blocks that run together on an XCD read the same token tiles of x.
     const int G = N / BN;
-    const int tile = xcd_tile(blockIdx.x, n_mt * G);
-    const int strip = tile / (gm_strip * G);
-    const int gm = min(gm_strip, n_mt - strip * gm_strip);
-    const int rem = tile - strip * gm_strip * G;
-    const int mt = strip * gm_strip + rem % gm;
-    const int g = rem / gm;
-    const int m0 = mt * BM;
+    const int n_chunks = (n_mt + tpb - 1) / tpb;
+    const int bid = xcd_tile(blockIdx.x, n_chunks * G);
+    const int g = bid % G;
+    const int mt0 = (bid / G) * tpb;
+    const int ntile = min(tpb, n_mt - mt0);
     stage_plans<FROM_HASH>(pi, ps, g, 1, J, Jc, C, BK, s_src, s_cnt);  // ends with a barrier
 
     const int Kc = Jc * BK;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nstage = Kc / 64;
+    const int nstage = Kc / 64;   // stages per token tile
+    const int ntot = ntile * nstage;
 
     // ---- direct-to-LDS loads: wave-wide load L fills LDS rows [8L, 8L+8);
     // lane l writes 16 bytes at row 8L + l/8, slot l%8, and so reads piece
     // (l%8) ^ key(row) of that row.  This wave does loads wave, wave+NW, ...;
     // the key repeats every 16 rows, so one lane offset serves all of them.
-    const i32x4 xr = dma_rsrc(x + static_cast<size_t>(m0) * K,
-                               static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K * 2));
     const i32x4 wr = dma_rsrc(w + static_cast<size_t>(g) * BN * Kc, static_cast<uint32_t>(static_cast<size_t>(BN) * Kc * 2));
     const int lrow = lane >> 3;
     const int piece = (lane & 7) ^ swz_key<RB>(wave * 8 + lrow);
@@ -131,7 +132,12 @@ __global__ __launch_bounds__(NW * 64) void group_kernel(const uint16_t* __restri
         w_voff[ii] = static_cast<uint32_t>(group_neuron<NB>(p) * Kc + piece * 8) * 2u;
     }
     const uint32_t lds0 = lds_address(group_smem);
-    auto dma = [&](int s, int buf) {
+    auto dma = [&](int S, int buf) {
+        const int i = S / nstage;  // token tile of the block
+        const int s = S - i * nstage;
+        const int m0 = (mt0 + i) * BM;
+        const i32x4 xr = dma_rsrc(x + static_cast<size_t>(m0) * K,
+                                   static_cast<uint32_t>(static_cast<size_t>(min(BM, M - m0)) * K * 2));
         const int k0 = s * 64;
         const int t = k0 / BK;
         const int ub = k0 - t * BK;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void group_kernel(const uint16_t* __restri
 #pragma unroll
         for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto compute = [&](int s, int buf) {
+    auto compute = [&](int s, int buf) {  // s: stage inside the token tile
         const int t = (s * 64) / BK;
         uint4 sel[NP];
 #pragma unroll
@@ -251,46 +257,81 @@ __global__ __launch_bounds__(NW * 64) void group_kernel(const uint16_t* __restri
         else dma_stage_barrier<0>();
     };
 
-    // ---- pipeline.  Stage s lives in buffer s % NSTG, loaded NSTG-1 stages
-    // ahead.  At the top of stage s a barrier finds stage s loaded (all waves)
-    // and every wave done with stage s-1, whose buffer the loads of stage
-    // s+NSTG-1 then refill.
+    // epilogue of token tile m0: lane holds neurons q*4*NB + nb*4 + i of token
+    // m0 + tok0 + tb*16 + li; the accumulators start again from zero
+    const int nbase = g * BN + q * 4 * NB;
+    auto store_tile = [&](int m0) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int m = m0 + tok0 + tb * 16 + li;
+            if (m < M) {
+                uint16_t* yr = y + static_cast<size_t>(m) * N + nbase;
+#pragma unroll
+                for (int hh = 0; hh < NB / 2; ++hh) {
+                    uint4 o;
+                    o.x = pack_bf16(apply_act(acc[2 * hh][tb][0], act), apply_act(acc[2 * hh][tb][1], act));
+                    o.y = pack_bf16(apply_act(acc[2 * hh][tb][2], act), apply_act(acc[2 * hh][tb][3], act));
+                    o.z = pack_bf16(apply_act(acc[2 * hh + 1][tb][0], act), apply_act(acc[2 * hh + 1][tb][1], act));
+                    o.w = pack_bf16(apply_act(acc[2 * hh + 1][tb][2], act), apply_act(acc[2 * hh + 1][tb][3], act));
+                    *reinterpret_cast<uint4*>(yr + 8 * hh) = o;
+                }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb][tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+
+    // ---- pipeline over the block's ntot stages (tile-major).  Stage S lives
+    // in buffer S % NSTG, loaded NSTG-1 stages ahead.  At the top of stage S a
+    // barrier finds stage S loaded (all waves) and every wave done with stage
+    // S-1, whose buffer the loads of stage S+NSTG-1 then refill.  A tile's
+    // output stores go out after its last stage; they count among the vector
+    // memory operations the next barrier's wait covers, which only makes that
+    // wait longer.
 #pragma unroll
     for (int p = 0; p < NSTG - 1; ++p)
-        if (p < nstage) dma(p, p);
-    auto step = [&](int s, int buf) {
-        wait_stage(min(NSTG - 2, nstage - 1 - s));
-        if (s + NSTG - 1 < nstage) dma(s + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        if (p < ntot) dma(p, p);
+    auto step = [&](int S, int buf) {
+        wait_stage(min(NSTG - 2, ntot - 1 - S));
+        if (S + NSTG - 1 < ntot) dma(S + NSTG - 1, (buf + NSTG - 1) % NSTG);
+        const int i = S / nstage;
+        const int s = S - i * nstage;
         compute(s, buf);
+        if (s == nstage - 1) store_tile((mt0 + i) * BM);
     };
-    for (int s0 = 0; s0 < nstage; s0 += NSTG) {
+    for (int s0 = 0; s0 < ntot; s0 += NSTG) {
 #pragma unroll
         for (int b = 0; b < NSTG; ++b)
-            if (s0 + b < nstage) step(s0 + b, b);
-    }
-
-    // epilogue: lane holds neurons q*4*NB + nb*4 + i of token tok0 + tb*16 + li
-    const int nbase = g * BN + q * 4 * NB;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const int m = m0 + tok0 + tb * 16 + li;
-        if (m >= M) continue;
-        uint16_t* yr = y + static_cast<size_t>(m) * N + nbase;
-#pragma unroll
-        for (int hh = 0; hh < NB / 2; ++hh) {
-            uint4 o;
-            o.x = pack_bf16(apply_act(acc[2 * hh][tb][0], act), apply_act(acc[2 * hh][tb][1], act));
-            o.y = pack_bf16(apply_act(acc[2 * hh][tb][2], act), apply_act(acc[2 * hh][tb][3], act));
-            o.z = pack_bf16(apply_act(acc[2 * hh + 1][tb][0], act), apply_act(acc[2 * hh + 1][tb][1], act));
-            o.w = pack_bf16(apply_act(acc[2 * hh + 1][tb][2], act), apply_act(acc[2 * hh + 1][tb][3], act));
-            *reinterpret_cast<uint4*>(yr + 8 * hh) = o;
-        }
+            if (s0 + b < ntot) step(s0 + b, b);
     }
 }
 
 inline size_t group_lds(int C, int BM, int BN, int NSTG, const Dims& d) {
     const size_t stage = static_cast<size_t>(C * BM + BN) * kGroupRowBytes;
     return NSTG * stage + static_cast<size_t>(d.J) * 4 + static_cast<size_t>(d.Jc) * 4;
+}
+
+// Token tiles per block: the count that minimises rounds of blocks times tiles
+// per block (the launch's length in tile times), the most tiles per block
+// among equals (the fewest plan stagings and pipeline fills).
+inline int group_tiles_per_block(long long n_mt, long long G) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    long long best_cost = -1;
+    int best = 1;
+    for (long long nc = 1; nc <= n_mt; ++nc) {
+        const long long tpb = (n_mt + nc - 1) / nc;
+        const long long chunks = (n_mt + tpb - 1) / tpb;
+        const long long cost = (chunks * G + cus - 1) / cus * tpb;
+        if (best_cost < 0 || cost < best_cost || (cost == best_cost && tpb > best)) {
+            best_cost = cost;
+            best = static_cast<int>(tpb);
+        }
+    }
+    return best;
 }
 
 template <int C, int BN, int BM, int NW, int NSTG, bool FROM_HASH>
@@ -302,12 +343,12 @@ ss1_status launch_group_shape(const ForwardArgs& a) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds)) != hipSuccess)
         return SS1_ERR_HIP;
-    // strips of two token tiles (four measured the same on Llama-3-8B gate/up)
-    const int strip = static_cast<int>(std::min<long long>(2, n_mt));
-    hipLaunchKernelGGL((group_kernel<C, BN, BM, NW, NSTG, FROM_HASH>), dim3(static_cast<unsigned>(n_mt * d.G)),
+    const int tpb = group_tiles_per_block(n_mt, d.G);
+    const long long blocks = (n_mt + tpb - 1) / tpb * d.G;
+    hipLaunchKernelGGL((group_kernel<C, BN, BM, NW, NSTG, FROM_HASH>), dim3(static_cast<unsigned>(blocks)),
                        dim3(NW * 64), lds, static_cast<hipStream_t>(a.stream), static_cast<const uint16_t*>(a.x),
                        static_cast<const uint16_t*>(a.w), a.plan_i, a.plan_s, static_cast<uint16_t*>(a.y), (int)a.M,
-                       (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.BK, (int)n_mt, strip, a.act);
+                       (int)d.K, (int)d.N, (int)d.J, (int)d.Jc, d.BK, (int)n_mt, tpb, a.act);
     return hipGetLastError() == hipSuccess ? SS1_OK : SS1_ERR_HIP;
 }
 

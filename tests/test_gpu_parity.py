@@ -345,6 +345,22 @@ def test_bf16_odd_shapes(M, K, N, c, BK, BN):
     assert "auto" in ys and "generic" in ys
 
 
+@pytest.mark.parametrize("name", ["llama_gateup_m4096", "square_c4_bn128", "square_c8_bn64", "gpt2l_down"])
+def test_group_full_size_sampled_rows(name):
+    # full size: blocks that run several token tiles through one pipeline
+    # (the last one ragged where M is not a multiple of the tile)
+    wl = WORKLOADS[name]
+    if name == "gpt2l_down":
+        wl = wl.with_m(wl.M - 77)
+    inp = make_inputs(wl)
+    y = run(wl, inp, device_plan(wl), algo="group")
+    rng = np.random.Generator(np.random.PCG64(7))
+    rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, 62, replace=False)]))
+    assert np.isfinite(host(y)).all()
+    err = check_bf16(wl, inp, y, rows, kernel="group")
+    print(f"{name} group full M={wl.M} err={err:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("M,K,N,c,BK,BN", [(300, 1024, 256, 8, 32, 64), (150, 512, 128, 4, 32, 32),
                                            (77, 1280, 320, 4, 64, 64), (100, 768, 256, 2, 32, 128),
                                            (64, 768, 192, 2, 64, 64)])
