@@ -381,7 +381,9 @@ def test_band_matrix_core_sketch_integer_bit_exact(M, K, N, c, BK, BN):
                                        ("llama_gateup_m16", "decode"),
                                        ("gpt2l_up", "generic"), ("tiny", "generic"),
                                        ("gpt2s_up", "band"), ("gpt2l_up", "band"),
-                                       ("gpt2s_up", "fold"), ("llama_gateup_m4096", "fold")])
+                                       ("gpt2s_up", "fold"), ("llama_gateup_m4096", "fold"),
+                                       ("llama_gateup_m4096", "group"), ("square_c8_bn128", "group"),
+                                       ("gpt2l_down", "group")])
 def test_hash_and_index_forms_agree(name, algo):
     wl = WORKLOADS[name]
     wl = wl.with_m(min(wl.M, 256))
@@ -400,12 +402,12 @@ def test_m0_is_noop_and_y_fully_written():
     w = torch.zeros((wl.N, wl.Kc), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((0, wl.N), dtype=torch.bfloat16, device="cuda")
     ss1.forward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, y)
-    for algo in ("fold", "band", "fused"):
+    for algo in ("fold", "band", "fused", "group"):
         ss1.forward(x, w, p.hash, p.sign, wl.c, wl.BK, wl.BN, y, algo=algo)
     # every output is written: start from NaN
     wl2 = wl.with_m(131)
     inp = make_inputs(wl2)
-    for algo in ("fused", "band", "generic", "fold"):
+    for algo in ("fused", "band", "generic", "fold", "group"):
         y = torch.full((131, wl.N), float("nan"), dtype=torch.bfloat16, device="cuda")
         p.forward(dev(inp.x_bits, "bf16"), dev(inp.w_bits, "bf16"), y=y, algo=algo)
         torch.cuda.synchronize()
