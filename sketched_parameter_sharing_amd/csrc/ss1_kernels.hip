@@ -1163,7 +1163,7 @@ inline BandCfg band_config(const Dims& d, int64_t M, const DeviceInfo& di) {
 }
 
 // Launch shapes of the band kernel:
-//   WIDE (c <= 2, BK % 64 == 0): 64-wide steps, so each pair of W_c requests
+//   WIDE (c <= 2, or c = 4 with BN <= 64; BK % 64 == 0): 64-wide steps, so each pair of W_c requests
 //        covers whole 128-byte lines; band reads issued at the start of a step
 //   BASE: 32-wide steps, band reads a step ahead where registers allow
 // Both run 8 waves (4 when the tile needs more than 256 registers) with W_c
@@ -1202,7 +1202,10 @@ ss1_status launch_band_c(const ForwardArgs& a, const BandCfg& cfg) {
                             : launch_band_cfg<MT, BN, 1, BandShape::BASE, FROM_HASH, W8>(a, cfg);
         case 2: return wide ? launch_band_cfg<MT, BN, 2, BandShape::WIDE, FROM_HASH, W8>(a, cfg)
                             : launch_band_cfg<MT, BN, 2, BandShape::BASE, FROM_HASH, W8>(a, cfg);
-        case 4: return launch_band_cfg<MT, BN, 4, BandShape::BASE, FROM_HASH, W8>(a, cfg);
+        case 4:
+            if constexpr (BN <= 64)
+                if (wide) return launch_band_cfg<MT, BN, 4, BandShape::WIDE, FROM_HASH, W8>(a, cfg);
+            return launch_band_cfg<MT, BN, 4, BandShape::BASE, FROM_HASH, W8>(a, cfg);
         case 8: return launch_band_cfg<MT, BN, 8, BandShape::BASE, FROM_HASH, W8>(a, cfg);
         default:
             if constexpr (W8) return SS1_ERR_ALGO;  // E4M3 weights need a fixed c
