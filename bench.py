@@ -646,6 +646,34 @@ def mlp_bk(c, m=MLP_SHAPE):
     return m["BK"] if (m["K"] // m["BK"]) % c == 0 else m["BK"] // 2
 
 
+def mlp_kernel_families(c, row_chunk, m=MLP_SHAPE):
+    """The kernels ss1_mlp_forward runs for the pair's up and down layers at
+    chunks of row_chunk rows (ss1_select_algo)."""
+    import sketched_parameter_sharing_amd as ss1
+    R, BK, BN = min(row_chunk, m["M"]), mlp_bk(c, m), m["BN"]
+    return (ss1.select_algo(R, m["K"], m["N1"], c, BK, BN, "bf16"),
+            ss1.select_algo(R, m["N1"], m["N2"], c, BK, BN, "bf16"))
+
+
+def mlp_recorded_traffic(c, row_chunk):
+    """The pair's recorded HBM bytes per call, or None when the record's kernels
+    are not the ones the pair runs now or their sources changed since."""
+    name = f"mlp:gpt2l_mlp_pair_c{c}_r{row_chunk}"
+    try:
+        with open(TRAFFIC_FILE) as f:
+            w = json.load(f).get("records", {}).get(name)
+    except (OSError, ValueError):
+        return None
+    if not w or "sources" not in w:
+        return None
+    fams = set(mlp_kernel_families(c, row_chunk))
+    if {kernel_family(k["kernel"]) for k in w.get("kernels", [])} != fams:
+        return None
+    if not all(set(KERNEL_SOURCES[f]) <= set(w["sources"]) for f in fams):
+        return None
+    return recorded_traffic(name)
+
+
 def make_mlp(c, m=MLP_SHAPE, seed=0x5f00):
     """Device tensors of an SS1 MLP pair at compression c (seeded inputs)."""
     import torch
@@ -995,7 +1023,7 @@ def main():
             r["frac"] = r["achieved"] / r["peak"]
         roof = dict(mf if t_f >= t_b else hb)
         roof["other"] = hb if t_f >= t_b else mf
-        roof.update({"traffic": recorded_traffic(f"mlp:gpt2l_mlp_pair_c{c}_r{args.row_chunk}", "fold"),
+        roof.update({"traffic": mlp_recorded_traffic(c, args.row_chunk),
                      "t_lower_us": max(t_f, t_b) * 1e6,
                      "note": "whole pair (both projections and the GELU epilogue) per call"})
         roof["traffic_vs_algorithmic"] = roof["traffic"] / wk["bytes"] if roof["traffic"] else None

@@ -60,10 +60,9 @@ ss1_status check_forward(const ss1_tensor* x, const ss1_tensor* W_c, const int32
 }
 
 // Estimated time in microseconds of the sketch kernels (band or fused) on a
-// large-M bf16 call, fitted to MI355X measurements (inputs not in cache): the
-// sketch VALU work, about 0.17 ps per (group, token, input element) and 2x
-// that with 128-neuron groups, or the compressed MFMA work at 0.6 PFLOP/s if
-// larger.
+// large-M bf16 call, fitted to MI355X measurements (inputs not in cache): about
+// 0.17 ps per (group, token, input element) and 2x that with 128-neuron
+// groups, or the compressed MFMA work at 0.6 PFLOP/s if larger.
 double sketch_estimate_us(const ForwardArgs& a) {
     const double M = static_cast<double>(a.M), K = static_cast<double>(a.d.K);
     const double G = static_cast<double>(a.d.G), N = static_cast<double>(a.d.N);
