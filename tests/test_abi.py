@@ -426,3 +426,13 @@ def test_mlp_forward_static_argument_checks():
     assert f(ctypes.byref(T(0, 768, data=None)), ctypes.byref(up), ctypes.byref(down),
              ctypes.byref(T(0, 700, data=None)), None) == _lib.ERR_SHAPE
     assert _lib.static_rows(5120, 2) == 3072 and _lib.static_rows(N1 - 64, 2) == 1
+
+
+def test_binding_constants_match_the_header():
+    # the binding's kernel, status and dtype codes are the header's enum values
+    text = open(os.path.join(ROOT, "include", "ss1.h")).read()
+    enum = {m.group(1): int(m.group(2)) for m in re.finditer(r"\b(SS1_[A-Z0-9_]+)\s*=\s*(-?\d+)", text)}
+    for name, code in _lib.ALGOS.items():
+        assert enum[f"SS1_ALGO_{name.upper()}"] == code, name
+    assert enum["SS1_OK"] == _lib.OK and enum["SS1_ERR_ALGO"] == _lib.ERR_ALGO
+    assert (enum["SS1_F32"], enum["SS1_BF16"], enum["SS1_FP8_E4M3"]) == (_lib.F32, _lib.BF16, _lib.FP8_E4M3)
